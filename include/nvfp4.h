@@ -1,0 +1,149 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled GEMM library.
+ *
+ * The operation is the FP4 GEMM debugged and benchmarked on the pages
+ * "The Art of Reading the Manual: Debugging FP4 GEMM Kernels on Blackwell
+ * SM120" (section "The Message": mm_fp4(a, b, a_descale, b_descale, alpha,
+ * out_dtype=bfloat16, out, block_size=16, ...)), "The Moment the Zeros
+ * Disappeared: A Pivotal FP4 Kernel Test on Blackwell SM120" (section "The
+ * Subject Message: A Corrected Test": scalar alpha, caller-allocated out, b as
+ * the column-major K x N operand, scales as uint8 bytes viewed as
+ * float8_e4m3fn) and "When a Benchmark Crashes: The Elusive FP4 GEMM
+ * Comparison on Blackwell SM120" (section "Input Knowledge Required", items 3
+ * and 4: two 4-bit floats per uint8, float8_e4m3fn block scales, dequantise on
+ * the fly and accumulate in higher precision):
+ *
+ *   D[m][n] = bf16_rne( alpha * sum_k xA[m][k] * xB[n][k] )
+ *   xA[m][k] = E2M1(code of element k of row m of A) * E4M3(a_sf[m][k/16])
+ *   xB[n][k] = E2M1(code of element k of row n of B) * E4M3(b_sf[n][k/16])
+ *
+ * Layouts (all row-major, no padding between rows):
+ *   A     uint8 [M][K/2]   two e2m1 codes per byte, element 2j in bits 0-3
+ *                          and element 2j+1 in bits 4-7 of byte j
+ *   a_sf  uint8 [M][K/16]  raw e4m3fn bytes, one per 16-element K block
+ *   B     uint8 [N][K/2]   the K x N operand stored column-major, i.e. each
+ *                          of the N columns is K-contiguous
+ *   b_sf  uint8 [N][K/16]
+ *   D     uint16 [M][N]    bf16 bit patterns
+ *
+ * Ownership and execution: every pointer argument except `workspace`-free
+ * host scalars is device memory owned by the caller.  The library never
+ * allocates device memory and keeps no device state between calls.  All work
+ * is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ * stream) with no internal synchronisation, so calls can be captured in a HIP
+ * graph.  Argument errors are detected on the host before anything is
+ * enqueued; faults inside kernels surface at the caller's next
+ * synchronisation, as with any HIP launch.
+ *
+ * Errors: every entry point returns an nvfp4_status; a non-zero status leaves
+ * all outputs untouched and nvfp4_last_error() returns a message for the
+ * calling thread (compare the K-mismatch error of the pages, "The Art of
+ * Reading the Manual", section "Why This Message Was Written").  There is no
+ * backend choice and no fallback chain: one code path for gfx950.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* negative size, K % 16 != 0, offsets/E invalid */
+  NVFP4_ERR_ALIGN = 3,       /* a base pointer is not aligned as documented */
+  NVFP4_ERR_UNSUPPORTED = 4, /* valid NVFP4 call outside this build's shapes (K % 256 != 0) */
+  NVFP4_ERR_WORKSPACE = 5,   /* workspace missing or smaller than *_workspace_size() */
+  NVFP4_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+} nvfp4_status;
+
+/*
+ * Single GEMM (mm_fp4).  a, b, a_sf, b_sf: 16-byte aligned;
+ * d: 4-byte aligned.  K must be a multiple of 256 (ERR_UNSUPPORTED otherwise;
+ * ERR_SHAPE if not a multiple of 16).  alpha: device fp32 scalar, NULL means
+ * 1.0f.  M == 0 or N == 0 is a successful no-op.  workspace: device memory of
+ * at least nvfp4_gemm_workspace_size(M, N, K) bytes (may be NULL when that
+ * size is 0), 256-byte aligned; its contents need no initialisation and are
+ * clobbered.
+ */
+nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf,
+                        const uint8_t* b, const uint8_t* b_sf,
+                        const float* alpha, uint16_t* d,
+                        int64_t M, int64_t N, int64_t K,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes nvfp4_gemm needs for this shape (0 for most large shapes). */
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Grouped-by-expert GEMM (the per-expert FP4 GEMMs of an MoE layer: pages
+ * "When a Benchmark Crashes", section "Why This Message Was Written": 256
+ * experts, 8 active per token, tokens scattered thinly over experts).
+ * Rows offsets[e] .. offsets[e+1]-1 of A are multiplied by expert e's weights:
+ *   D[r][n] = bf16_rne( alpha[e] * sum_k xA[r][k] * xB_e[n][k] ).
+ *   a      uint8 [rows][K/2],  a_sf uint8 [rows][K/16]
+ *   b      uint8 [E][N][K/2],  b_sf uint8 [E][N][K/16]
+ *   offsets int32 [E+1], device memory, offsets[0] = 0, non-decreasing,
+ *          offsets[E] <= rows.  Rows at or beyond offsets[E] are not written.
+ *   alpha  fp32 [E], device memory; NULL means all 1.0f.
+ *   d      uint16 [rows][N] bf16.
+ *   status optional device int32: if non-NULL it is set to 0 when offsets are
+ *          valid, or to 1 + (first bad expert) when offsets decrease or exceed
+ *          rows; bad experts are skipped (their rows are not written).
+ * Empty experts cost no weight traffic.  workspace: at least
+ * nvfp4_grouped_workspace_size(rows, N, K, E) bytes, 256-byte aligned.
+ */
+nvfp4_status nvfp4_grouped_gemm(const uint8_t* a, const uint8_t* a_sf,
+                                const uint8_t* b, const uint8_t* b_sf,
+                                const int32_t* offsets, const float* alpha,
+                                uint16_t* d, int64_t rows, int64_t N, int64_t K,
+                                int32_t E, void* workspace, size_t workspace_bytes,
+                                int32_t* status, void* stream);
+
+size_t nvfp4_grouped_workspace_size(int64_t rows, int64_t N, int64_t K, int32_t E);
+
+/*
+ * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
+ * The pages never quantise (their test used random bytes); this follows the
+ * block_size 16 and e4m3fn scale format of the pages above with these steps,
+ * all fp32 round-to-nearest-even, per 16-element block of one row:
+ *   t  = (amax_block / 6) * gs;         sf = e4m3fn_rne_saturating(t)
+ *   r  = gs / E4M3(sf)  (0 if E4M3(sf) == 0, correctly rounded division)
+ *   code = e2m1_rne_saturating(x * r)   (sign bit kept, so -0 -> 0x8)
+ * global_scale: device fp32 encode scale gs; NULL means 1.0f.  K % 16 == 0;
+ * x 16-byte aligned; non-finite inputs are outside the contract.
+ */
+nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K,
+                            const float* global_scale, uint8_t* q, uint8_t* sf,
+                            void* stream);
+
+/*
+ * Per-tensor encode scale: gs = (6 * 448) / max|x| in fp32 (1.0f if all x
+ * are zero), written to the device fp32 *gs.  n >= 0.  The caller's *gs is
+ * also used as the reduction cell, so it must not alias x.
+ */
+nvfp4_status nvfp4_global_scale(const float* x, int64_t n, float* gs, void* stream);
+
+/*
+ * alpha[i] = 1.0f / (gs_a[0] * gs_b[i]) in fp32 for i < count: the product of
+ * the two decode factors, for one activation tensor and `count` weight
+ * tensors (count = E for the grouped GEMM, 1 for a single GEMM).
+ */
+nvfp4_status nvfp4_alpha_from_scales(const float* gs_a, const float* gs_b,
+                                     float* alpha, int32_t count, void* stream);
+
+/* Name of the kernel plan nvfp4_gemm picks for a shape (static string). */
+const char* nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K);
+
+/* Message describing the calling thread's last error ("" if none). */
+const char* nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

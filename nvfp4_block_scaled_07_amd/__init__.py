@@ -1,0 +1,131 @@
+"""Python binding of the gfx950 NVFP4 library (``include/nvfp4.h``).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI of ``libnvfp4_gfx950.so`` (built in-tree by
+``nvfp4_block_scaled_07_amd.build``).  All arithmetic runs in the library's
+HIP kernels; there is no CPU or PyTorch fallback, and a missing library is an
+error.
+
+The C entry points are exposed with their own names (``nvfp4_gemm``,
+``nvfp4_grouped_gemm``, ...) taking torch tensors in place of pointers.
+Tensors are used only as device memory; the stream is
+``torch.cuda.current_stream()``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libnvfp4_gfx950.so")
+
+STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
+          4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_WORKSPACE", 6: "NVFP4_ERR_HIP"}
+
+# exported symbol -> (restype, argtypes)
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SIGNATURES = {
+    "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "nvfp4_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
+                                          _vp, _vp]),
+    "nvfp4_grouped_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_global_scale": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
+    "nvfp4_alpha_from_scales": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
+    "nvfp4_gemm_plan": (ctypes.c_char_p, [_i64, _i64, _i64]),
+    "nvfp4_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load the in-tree library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m nvfp4_block_scaled_07_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype, f.argtypes = res, args
+        _lib = l
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise Nvfp4Error(status, fn, lib().nvfp4_last_error().decode())
+
+
+def nvfp4_last_error() -> str:
+    return lib().nvfp4_last_error().decode()
+
+
+def nvfp4_gemm_plan(M: int, N: int, K: int) -> str:
+    return lib().nvfp4_gemm_plan(M, N, K).decode()
+
+
+def nvfp4_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_gemm_workspace_size(M, N, K))
+
+
+def nvfp4_grouped_workspace_size(rows: int, N: int, K: int, E: int) -> int:
+    return int(lib().nvfp4_grouped_workspace_size(rows, N, K, E))
+
+
+def nvfp4_gemm(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, workspace=None, stream=None):
+    """D = bf16(alpha * dequant(A) @ dequant(B)^T); see include/nvfp4.h.
+    a: uint8 [M][K/2], a_sf: uint8 [M][K/16], b: uint8 [N][K/2],
+    b_sf: uint8 [N][K/16], alpha: fp32 device scalar tensor or None,
+    d: caller-allocated [M][N] bf16 (or int16/uint16) tensor, returned."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_gemm(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(d), M, N, K,
+                          _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_gemm")
+    return d
+
+
+def nvfp4_grouped_gemm(a, a_sf, b, b_sf, offsets, alpha, d, rows: int, N: int, K: int, E: int,
+                       workspace=None, status=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_grouped_gemm(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(offsets), _ptr(alpha), _ptr(d),
+                                  rows, N, K, E, _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
+    _check(st, "nvfp4_grouped_gemm")
+    return d
+
+
+def nvfp4_quantize(x, R: int, K: int, global_scale, q, sf, stream=None):
+    st = lib().nvfp4_quantize(_ptr(x), R, K, _ptr(global_scale), _ptr(q), _ptr(sf), _stream(stream))
+    _check(st, "nvfp4_quantize")
+    return q, sf
+
+
+def nvfp4_global_scale(x, n: int, gs, stream=None):
+    st = lib().nvfp4_global_scale(_ptr(x), n, _ptr(gs), _stream(stream))
+    _check(st, "nvfp4_global_scale")
+    return gs
+
+
+def nvfp4_alpha_from_scales(gs_a, gs_b, alpha, count: int, stream=None):
+    st = lib().nvfp4_alpha_from_scales(_ptr(gs_a), _ptr(gs_b), _ptr(alpha), count, _stream(stream))
+    _check(st, "nvfp4_alpha_from_scales")
+    return alpha

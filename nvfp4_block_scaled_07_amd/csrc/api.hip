@@ -1,0 +1,148 @@
+// C ABI of the NVFP4 library: host-side validation, plan choice and launch.
+// Every check runs on the host before anything is enqueued, so a rejected
+// call touches no device memory.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/nvfp4.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+nvfp4_status fail(nvfp4_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+nvfp4_status ok() {
+  g_err[0] = '\0';
+  return NVFP4_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+nvfp4_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape rules shared by the GEMM entry points.
+nvfp4_status check_k(int64_t K) {
+  if (K < 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is negative", (long long)K);
+  if (K % 16 != 0)
+    return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of the block size 16", (long long)K);
+  if (K % 256 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: this build needs K %% 256 == 0", (long long)K);
+  if (K == 0) return fail(NVFP4_ERR_UNSUPPORTED, "K = 0 is not supported");
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_err; }
+
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256) return 0;
+  return nvfp4::choose_plan(M, N, K).workspace;
+}
+
+const char* nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256) return "none";
+  return nvfp4::choose_plan(M, N, K).name;
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                        const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0) return fail(NVFP4_ERR_SHAPE, "M = %lld, N = %lld must be >= 0", (long long)M, (long long)N);
+  nvfp4_status s = check_k(K);
+  if (s != NVFP4_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  if (!a || !a_sf || !b || !b_sf || !d)
+    return fail(NVFP4_ERR_NULL, "a, a_sf, b, b_sf and d must be non-NULL (alpha may be NULL)");
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_sf, 16) || !aligned(b_sf, 16))
+    return fail(NVFP4_ERR_ALIGN, "a, b, a_sf and b_sf must be 16-byte aligned");
+  if (!aligned(d, 4) || !aligned(alpha, 4)) return fail(NVFP4_ERR_ALIGN, "d and alpha must be 4-byte aligned");
+  if (M > (1ll << 30) || N > (1ll << 30) || K > (1ll << 30))
+    return fail(NVFP4_ERR_UNSUPPORTED, "dimensions above 2^30 are not supported");
+  const nvfp4::GemmPlan plan = nvfp4::choose_plan(M, N, K);
+  if (plan.workspace > 0) {
+    if (!workspace || workspace_bytes < plan.workspace)
+      return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu workspace bytes, got %zu", plan.name, plan.workspace,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 1};
+  return hip_status(nvfp4::launch_gemm(plan, p, (hipStream_t)stream), "nvfp4_gemm launch");
+}
+
+size_t nvfp4_grouped_workspace_size(int64_t rows, int64_t N, int64_t K, int32_t E) {
+  return nvfp4::grouped_workspace(rows, N, K, E);
+}
+
+nvfp4_status nvfp4_grouped_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                                const int32_t* offsets, const float* alpha, uint16_t* d, int64_t rows, int64_t N,
+                                int64_t K, int32_t E, void* workspace, size_t workspace_bytes, int32_t* status,
+                                void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (rows < 0 || N < 0 || E < 0)
+    return fail(NVFP4_ERR_SHAPE, "rows = %lld, N = %lld, E = %d must be >= 0", (long long)rows, (long long)N, E);
+  nvfp4_status s = check_k(K);
+  if (s != NVFP4_OK) return s;
+  if (!offsets && E > 0) return fail(NVFP4_ERR_NULL, "offsets must be non-NULL");
+  if (!aligned(offsets, 4) || !aligned(status, 4))
+    return fail(NVFP4_ERR_ALIGN, "offsets and status must be 4-byte aligned");
+  if (E == 0 || N == 0 || rows == 0) {
+    // nothing to multiply; the offsets are still checked when status is asked for
+    nvfp4::GroupedLaunch p{a, a_sf, b, b_sf, offsets, alpha, d, rows, N, K, E};
+    return hip_status(nvfp4::launch_grouped(p, status, (hipStream_t)stream, false), "nvfp4_grouped_gemm status");
+  }
+  if (!a || !a_sf || !b || !b_sf || !d)
+    return fail(NVFP4_ERR_NULL, "a, a_sf, b, b_sf and d must be non-NULL (alpha and status may be NULL)");
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_sf, 16) || !aligned(b_sf, 16))
+    return fail(NVFP4_ERR_ALIGN, "a, b, a_sf and b_sf must be 16-byte aligned");
+  if (!aligned(d, 4) || !aligned(alpha, 4)) return fail(NVFP4_ERR_ALIGN, "d and alpha must be 4-byte aligned");
+  if (rows > (1ll << 30) || N > (1ll << 30) || K > (1ll << 30) || E > 65535)
+    return fail(NVFP4_ERR_UNSUPPORTED, "dimensions above 2^30 (or E > 65535) are not supported");
+  nvfp4::GroupedLaunch p{a, a_sf, b, b_sf, offsets, alpha, d, rows, N, K, E};
+  return hip_status(nvfp4::launch_grouped(p, status, (hipStream_t)stream, true), "nvfp4_grouped_gemm launch");
+}
+
+nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K, const float* global_scale, uint8_t* q,
+                            uint8_t* sf, void* stream) {
+  if (R < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "R = %lld, K = %lld must be >= 0", (long long)R, (long long)K);
+  if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
+  if (R == 0 || K == 0) return ok();
+  if (!x || !q || !sf) return fail(NVFP4_ERR_NULL, "x, q and sf must be non-NULL");
+  if (!aligned(x, 16) || !aligned(q, 2) || !aligned(global_scale, 4))
+    return fail(NVFP4_ERR_ALIGN, "x must be 16-byte aligned, q 2-byte aligned, global_scale 4-byte aligned");
+  return hip_status(nvfp4::launch_quantize(x, R, K, global_scale, q, sf, (hipStream_t)stream),
+                    "nvfp4_quantize launch");
+}
+
+nvfp4_status nvfp4_global_scale(const float* x, int64_t n, float* gs, void* stream) {
+  if (n < 0) return fail(NVFP4_ERR_SHAPE, "n = %lld must be >= 0", (long long)n);
+  if (!gs || (!x && n > 0)) return fail(NVFP4_ERR_NULL, "x and gs must be non-NULL");
+  if (!aligned(x, 16) || !aligned(gs, 4)) return fail(NVFP4_ERR_ALIGN, "x must be 16-byte aligned, gs 4-byte");
+  return hip_status(nvfp4::launch_global_scale(x, n, gs, (hipStream_t)stream), "nvfp4_global_scale launch");
+}
+
+nvfp4_status nvfp4_alpha_from_scales(const float* gs_a, const float* gs_b, float* alpha, int32_t count,
+                                     void* stream) {
+  if (count < 0) return fail(NVFP4_ERR_SHAPE, "count = %d must be >= 0", count);
+  if (count == 0) return ok();
+  if (!gs_a || !gs_b || !alpha) return fail(NVFP4_ERR_NULL, "gs_a, gs_b and alpha must be non-NULL");
+  if (!aligned(gs_a, 4) || !aligned(gs_b, 4) || !aligned(alpha, 4))
+    return fail(NVFP4_ERR_ALIGN, "gs_a, gs_b and alpha must be 4-byte aligned");
+  return hip_status(nvfp4::launch_alpha(gs_a, gs_b, alpha, count, (hipStream_t)stream), "nvfp4_alpha launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal interfaces between the host API (api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct GemmLaunch {
+  const uint8_t* a;
+  const uint8_t* a_sf;
+  const uint8_t* b;
+  const uint8_t* b_sf;
+  const float* alpha;
+  uint16_t* d;
+  float* ws;
+  int64_t M, N, K;
+  int tiles_n;
+  int splits;
+};
+
+struct GroupedLaunch {
+  const uint8_t* a;
+  const uint8_t* a_sf;
+  const uint8_t* b;
+  const uint8_t* b_sf;
+  const int32_t* offsets;
+  const float* alpha;
+  uint16_t* d;
+  int64_t rows, N, K;
+  int E;
+};
+
+struct PlanInfo {
+  const char* name;
+  int bm, bn;
+};
+
+struct GemmPlan {
+  const char* name;
+  int kind;
+  int64_t tiles_m, tiles_n;
+  int splits;
+  size_t workspace;
+};
+
+GemmPlan choose_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
+hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
+size_t grouped_workspace(int64_t rows, int64_t N, int64_t K, int32_t E);
+
+hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs, uint8_t* q, uint8_t* sf,
+                           hipStream_t stream);
+hipError_t launch_global_scale(const float* x, int64_t n, float* gs, hipStream_t stream);
+hipError_t launch_alpha(const float* gs_a, const float* gs_b, float* alpha, int32_t count, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,98 @@
+"""The C ABI loads and exports every declared symbol; host-side validation
+returns the documented status codes.  CPU only: every call below is rejected
+(or answered) on the host before any HIP call, so no GPU is needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_07_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "nvfp4_gemm" in names and "nvfp4_grouped_gemm" in names
+    lib = nv.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(nv.SIGNATURES), "binding and header disagree"
+
+
+def test_binding_loads_in_tree_library():
+    assert os.path.dirname(nv.LIB_PATH) == os.path.join(ROOT, "nvfp4_block_scaled_07_amd")
+    maps = open("/proc/self/maps").read()
+    nv.lib()
+    assert nv.LIB_PATH in open("/proc/self/maps").read() or nv.LIB_PATH in maps
+
+
+FAKE = 0x10000  # an aligned non-NULL address; never dereferenced (calls are rejected on the host)
+
+
+def _gemm(a=FAKE, asf=FAKE, b=FAKE, bsf=FAKE, alpha=None, d=FAKE, M=16, N=16, K=256, ws=None, wsb=0):
+    return nv.lib().nvfp4_gemm(a, asf, b, bsf, alpha, d, M, N, K, ws, wsb, None)
+
+
+def test_gemm_error_paths():
+    assert _gemm(K=40) == 2 and "block size 16" in nv.nvfp4_last_error()
+    assert _gemm(K=-16) == 2
+    assert _gemm(M=-1) == 2
+    assert _gemm(K=128) == 4 and "256" in nv.nvfp4_last_error()
+    assert _gemm(K=0) == 4
+    assert _gemm(a=None) == 1
+    assert _gemm(d=None) == 1
+    assert _gemm(a=FAKE + 8) == 3
+    assert _gemm(bsf=FAKE + 4) == 3
+    assert _gemm(d=FAKE + 2) == 3
+    # small M needs a split-K workspace
+    need = nv.nvfp4_gemm_workspace_size(16, 768, 6144)
+    assert need > 0
+    assert _gemm(N=768, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
+    assert _gemm(N=768, K=6144, ws=FAKE, wsb=need - 1) == 5
+    assert _gemm(N=768, K=6144, ws=FAKE + 16, wsb=need) == 3
+    # empty problems succeed without touching anything
+    assert _gemm(M=0, a=None, d=None) == 0
+    assert _gemm(N=0) == 0
+
+
+def test_grouped_error_paths():
+    L = nv.lib()
+    call = lambda **k: L.nvfp4_grouped_gemm(k.get("a", FAKE), FAKE, FAKE, FAKE, k.get("off", FAKE), None,
+                                            k.get("d", FAKE), k.get("rows", 64), k.get("N", 64),
+                                            k.get("K", 256), k.get("E", 4), None, 0, k.get("st", None), None)
+    assert call(K=24) == 2
+    assert call(E=-1) == 2
+    assert call(off=None) == 1
+    assert call(a=None) == 1
+    assert call(off=FAKE + 2) == 3
+    assert call(st=FAKE + 1) == 3
+    assert call(K=384) == 4
+
+
+def test_quantize_and_scale_error_paths():
+    L = nv.lib()
+    assert L.nvfp4_quantize(FAKE, 4, 24, None, FAKE, FAKE, None) == 2
+    assert L.nvfp4_quantize(None, 4, 32, None, FAKE, FAKE, None) == 1
+    assert L.nvfp4_quantize(FAKE + 4, 4, 32, None, FAKE, FAKE, None) == 3
+    assert L.nvfp4_quantize(None, 0, 32, None, None, None, None) == 0
+    assert L.nvfp4_global_scale(FAKE, -1, FAKE, None) == 2
+    assert L.nvfp4_global_scale(FAKE, 10, None, None) == 1
+    assert L.nvfp4_alpha_from_scales(FAKE, FAKE, None, 3, None) == 1
+    assert L.nvfp4_alpha_from_scales(None, None, None, 0, None) == 0
+
+
+def test_plan_and_workspace_queries():
+    assert nv.nvfp4_gemm_plan(16384, 6144, 6144).startswith("tile")
+    assert nv.nvfp4_gemm_plan(16, 768, 6144).startswith("skinny")
+    assert nv.nvfp4_gemm_plan(16, 768, 100) == "none"
+    assert nv.nvfp4_gemm_workspace_size(16384, 6144, 6144) == 0
+    assert nv.nvfp4_gemm_workspace_size(16, 768, 6144) % (16 * 768 * 4) == 0

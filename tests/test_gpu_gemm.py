@@ -1,0 +1,166 @@
+"""GPU GEMM parity with the oracle through the C ABI, at every plan the
+library picks for the page workloads, plus ragged, degenerate and invariant
+cases."""
+import functools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_07_amd as nv
+import synth
+from oracle import nvfp4_ref as o
+from tests.gpu_util import bits, check_gemm, dev, gpu_gemm, gpu_global_scale, gpu_quantize, host, say, scalar
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _quantized_workload(name, m=None):
+    """oracle-side and GPU-side quantisation of the same seeded fp32 inputs;
+    the bytes must agree before the GEMM is compared."""
+    a, b = synth.single_operands(name, m)
+    w = synth.WORKLOADS[name]
+    at, bt = dev(a), dev(b)
+    if w["unit_global_scale"]:
+        gsa = gsb = np.float32(1)
+        gsa_t = gsb_t = None
+        alpha = np.float32(1)
+        alpha_t = scalar(1.0)
+    else:
+        gsa, gsb = o.global_encode_scale(a), o.global_encode_scale(b)
+        gsa_t, gsb_t = gpu_global_scale(at), gpu_global_scale(bt)
+        alpha = o.alpha_from_scales(gsa, gsb)
+        alpha_t = torch.empty(1, dtype=torch.float32, device="cuda")
+        nv.nvfp4_alpha_from_scales(gsa_t, gsb_t, alpha_t, 1)
+        assert host(alpha_t)[0] == alpha
+    qa, sfa = o.quantize(a, gsa)
+    qb, sfb = o.quantize(b, gsb)
+    qa_t, sfa_t = gpu_quantize(at, gsa_t)
+    qb_t, sfb_t = gpu_quantize(bt, gsb_t)
+    np.testing.assert_array_equal(host(qa_t), qa)
+    np.testing.assert_array_equal(host(sfa_t), sfa)
+    np.testing.assert_array_equal(host(qb_t), qb)
+    np.testing.assert_array_equal(host(sfb_t), sfb)
+    return (qa, sfa, qb, sfb, alpha), (qa_t, sfa_t, qb_t, sfb_t, alpha_t)
+
+
+def test_worked_fixture_padded_to_k256():
+    with open(os.path.join(GOLD, "worked_gemm_2x3x32.json")) as f:
+        g = json.load(f)
+    rows = lambda hexes, per: np.frombuffer(b"".join(bytes.fromhex(h) for h in hexes), np.uint8).reshape(-1, per)
+    pad = lambda x, w: np.concatenate([x, np.zeros((x.shape[0], w - x.shape[1]), np.uint8)], axis=1)
+    a = pad(rows(g["a_hex"], 16), 128)
+    asf = pad(rows(g["a_sf_hex"], 2), 16)
+    b = pad(rows(g["b_hex"], 16), 128)
+    bsf = pad(rows(g["b_sf_hex"], 2), 16)
+    say("worked fixture")
+    d = gpu_gemm(dev(a), dev(asf), dev(b), dev(bsf), scalar(1.0), 2, 3, 256)
+    np.testing.assert_array_equal(o.bf16_to_f64(bits(d)), np.array(g["expected"]))
+    d = gpu_gemm(dev(a), dev(asf), dev(b), dev(bsf), scalar(0.5), 2, 3, 256)
+    np.testing.assert_array_equal(o.bf16_to_f64(bits(d)), np.array(g["alpha_half_expected"]))
+    d = gpu_gemm(dev(a), dev(asf), dev(b), dev(bsf), None, 2, 3, 256)   # NULL alpha = 1
+    np.testing.assert_array_equal(o.bf16_to_f64(bits(d)), np.array(g["expected"]))
+
+
+def test_smoke_workload_not_all_zeros_and_matches():
+    ref, gpu = _quantized_workload("smoke_128x256x256")
+    say("smoke gemm 128x256x256")
+    d = gpu_gemm(*gpu, 128, 256, 256)
+    db = bits(d)
+    v = o.bf16_to_f64(db)
+    assert not (v == 0).all() and np.isfinite(v).all()
+    check_gemm(db, *ref, label="smoke")
+
+
+def test_random_bytes_like_the_page_smoke_test():
+    # the pages' kernel test fed random code bytes and random scale bytes
+    M, N, K = 128, 256, 256
+    a, b = synth.random_codes(11, M, K), synth.random_codes(12, N, K)
+    asf, bsf = synth.random_scale_bytes(13, M, K), synth.random_scale_bytes(14, N, K)
+    say("random bytes 128x256x256")
+    d = gpu_gemm(dev(a), dev(asf), dev(b), dev(bsf), scalar(1.0), M, N, K)
+    st = check_gemm(bits(d), a, asf, b, bsf, np.float32(1), "random bytes")
+    assert st["n"] == M * N
+
+
+@pytest.mark.parametrize("name", ["attn_proj_n768_k6144", "moe_expert_n2048_k6144"])
+def test_decode_and_prefill_sweeps(name):
+    w = synth.WORKLOADS[name]
+    ref, gpu = _quantized_workload(name)
+    qa, sfa, qb, sfb, alpha = ref
+    for m in w["ms"]:
+        say(name, "M =", m, "plan", nv.nvfp4_gemm_plan(m, w["n"], w["k"]))
+        d = gpu_gemm(gpu[0][:m], gpu[1][:m], gpu[2], gpu[3], gpu[4], m, w["n"], w["k"])
+        st = check_gemm(bits(d), qa[:m], sfa[:m], qb, sfb, alpha, f"{name} M={m}")
+        assert st["strict_2ulp_frac"] > 0.999
+
+
+@functools.lru_cache(maxsize=1)
+def _oracle_quantized_large_b(gsb):
+    _, b = synth.single_operands("large_n6144_k6144", 4096)
+    return o.quantize(b, gsb)
+
+
+@pytest.mark.parametrize("m", [4096, 8192, 16384])
+def test_large_sampled_rows(m):
+    name = "large_n6144_k6144"
+    a, b = synth.single_operands(name, m)
+    gsb = o.global_encode_scale(b)
+    qb, sfb = _oracle_quantized_large_b(gsb)
+    gsa = o.global_encode_scale(a)
+    at, bt = dev(a), dev(b)
+    gsa_t, gsb_t = gpu_global_scale(at), gpu_global_scale(bt)
+    alpha_t = torch.empty(1, dtype=torch.float32, device="cuda")
+    nv.nvfp4_alpha_from_scales(gsa_t, gsb_t, alpha_t, 1)
+    alpha = o.alpha_from_scales(gsa, gsb)
+    assert host(alpha_t)[0] == alpha
+    qa_t, sfa_t = gpu_quantize(at, gsa_t)
+    qb_t, sfb_t = gpu_quantize(bt, gsb_t)
+    del at, bt
+    say(name, "M =", m, "plan", nv.nvfp4_gemm_plan(m, 6144, 6144))
+    d = gpu_gemm(qa_t, sfa_t, qb_t, sfb_t, alpha_t, m, 6144, 6144)
+    rows = np.unique(np.concatenate([np.random.default_rng(m).choice(m, 48, replace=False),
+                                     [0, 127, 128, m - 1]]))
+    np.testing.assert_array_equal(host(qb_t), qb)
+    qa_r, sfa_r = o.quantize(a[rows], gsa)
+    ridx = torch.from_numpy(rows).cuda()
+    np.testing.assert_array_equal(host(qa_t[ridx]), qa_r)
+    check_gemm(bits(d[ridx]), qa_r, sfa_r, qb, sfb, alpha, f"large M={m} sampled rows")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 129, 512), (100, 200, 768), (65, 96, 256),
+                                   (129, 130, 1024), (33, 5, 2048), (300, 1000, 256)])
+def test_ragged_shapes(M, N, K):
+    a, b = synth.random_codes(M * 7 + 1, M, K), synth.random_codes(N * 7 + 2, N, K)
+    asf = synth.random_scale_bytes(M + 3, M, K, lo=0x28, hi=0x48, signed=True)
+    bsf = synth.random_scale_bytes(N + 4, N, K, lo=0x28, hi=0x48)
+    say("ragged", M, N, K, nv.nvfp4_gemm_plan(M, N, K))
+    d = gpu_gemm(dev(a), dev(asf), dev(b), dev(bsf), scalar(0.75), M, N, K, d_fill=0x7FC1)
+    check_gemm(bits(d), a, asf, b, bsf, np.float32(0.75), f"ragged {M}x{N}x{K}")
+
+
+def test_deterministic_and_sign_flip():
+    for (M, N, K) in [(16, 768, 6144), (300, 384, 1024), (512, 512, 2048), (2048, 2048, 256)]:
+        a, b = synth.random_codes(1, M, K), synth.random_codes(2, N, K)
+        asf = synth.random_scale_bytes(3, M, K, lo=0x30, hi=0x40)
+        bsf = synth.random_scale_bytes(4, N, K, lo=0x30, hi=0x40)
+        at, asft, bt, bsft = dev(a), dev(asf), dev(b), dev(bsf)
+        say("determinism", M, N, K, nv.nvfp4_gemm_plan(M, N, K))
+        d1 = bits(gpu_gemm(at, asft, bt, bsft, scalar(1.0), M, N, K))
+        d2 = bits(gpu_gemm(at, asft, bt, bsft, scalar(1.0), M, N, K))
+        np.testing.assert_array_equal(d1, d2)
+        dn = bits(gpu_gemm(dev(a ^ np.uint8(0x88)), asft, bt, bsft, scalar(1.0), M, N, K))
+        np.testing.assert_array_equal(o.bf16_to_f64(dn), -o.bf16_to_f64(d1))
+
+
+def test_zero_sized_calls_are_noops():
+    d = torch.full((4, 4), 7, dtype=torch.int16, device="cuda")
+    x = torch.zeros((4, 128), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    say("zero sized")
+    nv.nvfp4_gemm(x, s, x, s, None, d, 0, 4, 256)
+    nv.nvfp4_gemm(x, s, x, s, None, d, 4, 0, 256)
+    assert (host(d) == 7).all()

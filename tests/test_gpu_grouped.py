@@ -1,0 +1,119 @@
+"""GPU grouped-by-expert GEMM parity with the oracle: the 512-token, 256-expert,
+top-8 MoE workload (sampled experts) and adversarial row distributions."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_07_amd as nv
+import synth
+from oracle import nvfp4_ref as o
+from tests.gpu_util import bits, check_gemm, dev, gpu_global_scale, gpu_quantize, host, say
+
+pytestmark = pytest.mark.gpu
+SENTINEL = 0x7FC1
+
+
+def _grouped(a_t, asf_t, b_t, bsf_t, off_t, alpha_t, rows, N, K, E, status=True):
+    d = torch.full((max(rows, 1), max(N, 1)), SENTINEL, dtype=torch.int16, device="cuda")
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda") if status else None
+    need = nv.nvfp4_grouped_workspace_size(rows, N, K, E)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    nv.nvfp4_grouped_gemm(a_t, asf_t, b_t, bsf_t, off_t, alpha_t, d, rows, N, K, E, ws, st)
+    return d, st
+
+
+def test_moe_workload_512_tokens_256_experts():
+    g = synth.GROUPED
+    T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
+    tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
+    rows = int(off[-1])
+    assert rows == T * g["top_k"]
+    say("moe: quantise token activations")
+    x = synth.token_activations(T, K)
+    gsa = o.global_encode_scale(x)
+    qa_tok, sfa_tok = o.quantize(x, gsa)
+    xt = dev(x)
+    gsa_t = gpu_global_scale(xt)
+    assert host(gsa_t)[0] == gsa
+    qa_t_tok, sfa_t_tok = gpu_quantize(xt, gsa_t)
+    np.testing.assert_array_equal(host(qa_t_tok), qa_tok)
+    np.testing.assert_array_equal(host(sfa_t_tok), sfa_tok)
+    # rows ordered by expert then token (a gather of the quantised tokens)
+    qa, sfa = qa_tok[tok], sfa_tok[tok]
+    tok_t = torch.from_numpy(tok).cuda()
+    qa_t, sfa_t = qa_t_tok[tok_t].contiguous(), sfa_t_tok[tok_t].contiguous()
+    # expert weights: seeded random code and scale bytes (1.6 GB of codes)
+    say("moe: expert weights")
+    b = synth.random_codes(g["seed_expert_base"], E * N, K).reshape(E, N, K // 2)
+    bsf = synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, lo=0x20, hi=0x38).reshape(E, N, K // 16)
+    alpha = np.random.default_rng(77).uniform(0.5, 2.0, E).astype(np.float32) / np.float32(gsa)
+    b_t, bsf_t = dev(b), dev(bsf)
+    say("moe: grouped gemm rows", rows)
+    d, st = _grouped(qa_t, sfa_t, b_t, bsf_t, dev(off), dev(alpha), rows, N, K, E)
+    assert int(host(st)[0]) == 0
+    db = bits(d)
+    experts = np.unique(np.concatenate([np.random.default_rng(5).choice(E, 20, replace=False),
+                                        [0, E - 1, int(np.argmax(np.diff(off)))]]))
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(db[lo:hi], qa[lo:hi], sfa[lo:hi], b[e], bsf[e], alpha[e], f"expert {e}")
+    assert not (db == SENTINEL).any()
+
+
+def _small_problem(kind, rows=300, E=8, N=192, K=512, seed=0):
+    off = synth.adversarial_offsets(kind, rows, E) if isinstance(kind, str) else np.asarray(kind, np.int32)
+    a = synth.random_codes(seed + 1, rows, K)
+    asf = synth.random_scale_bytes(seed + 2, rows, K, lo=0x30, hi=0x40)
+    b = synth.random_codes(seed + 3, E * N, K).reshape(E, N, K // 2)
+    bsf = synth.random_scale_bytes(seed + 4, E * N, K, lo=0x30, hi=0x40).reshape(E, N, K // 16)
+    alpha = np.linspace(0.5, 2.0, E).astype(np.float32)
+    return off, a, asf, b, bsf, alpha
+
+
+@pytest.mark.parametrize("kind", ["one", "alternate", "ones", "empty",
+                                  [0, 0, 5, 5, 70, 70, 71, 200, 250], [0, 16, 32, 48, 64, 80, 96, 112, 128]])
+def test_adversarial_row_distributions(kind):
+    rows, E, N, K = 300, 8, 192, 512
+    off, a, asf, b, bsf, alpha = _small_problem(kind, rows, E, N, K)
+    say("grouped adversarial", kind)
+    d, st = _grouped(dev(a), dev(asf), dev(b), dev(bsf), dev(off), dev(alpha), rows, N, K, E)
+    assert int(host(st)[0]) == 0
+    want = o.grouped_gemm(a, asf, b, bsf, off, alpha, np.full((rows, N), SENTINEL, np.uint16))
+    db = bits(d)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], alpha[e], f"{kind} expert {e}")
+    # rows beyond offsets[E] are untouched
+    np.testing.assert_array_equal(db[int(off[-1]):], want[int(off[-1]):])
+
+
+def test_null_alpha_and_no_status():
+    off, a, asf, b, bsf, _ = _small_problem([0, 40, 41, 100, 100, 160, 161, 162, 300])
+    say("grouped null alpha")
+    d, _ = _grouped(dev(a), dev(asf), dev(b), dev(bsf), dev(off), None, 300, 192, 512, 8, status=False)
+    db = bits(d)
+    for e in range(8):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], np.float32(1), f"expert {e}")
+
+
+def test_invalid_offsets_reported_and_skipped():
+    # expert 3's range decreases: status = 1 + 3; other experts still computed
+    off = np.array([0, 10, 20, 60, 50, 70, 80, 90, 100], np.int32)
+    _, a, asf, b, bsf, alpha = _small_problem("empty")
+    say("grouped invalid offsets")
+    d, st = _grouped(dev(a), dev(asf), dev(b), dev(bsf), dev(off), dev(alpha), 300, 192, 512, 8)
+    assert int(host(st)[0]) == 4
+    db = bits(d)
+    # expert 4's range [50, 70) overlaps expert 2's [20, 60): check the rows
+    # that only one valid expert writes
+    for e, lo, hi in ((0, 0, 10), (1, 10, 20), (2, 20, 50), (4, 60, 70), (5, 70, 80), (6, 80, 90), (7, 90, 100)):
+        check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], alpha[e], f"expert {e}")
+    # offsets beyond rows: status names the first such expert
+    off2 = np.array([0, 10, 20, 30, 40, 50, 60, 70, 400], np.int32)
+    d2, st2 = _grouped(dev(a), dev(asf), dev(b), dev(bsf), dev(off2), dev(alpha), 300, 192, 512, 8)
+    assert int(host(st2)[0]) == 8
+    assert (bits(d2)[70:] == SENTINEL).all()
