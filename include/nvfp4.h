@@ -67,8 +67,13 @@ typedef enum {
  * ERR_SHAPE if not a multiple of 16).  alpha: device fp32 scalar, NULL means
  * 1.0f.  M == 0 or N == 0 is a successful no-op.  workspace: device memory of
  * at least nvfp4_gemm_workspace_size(M, N, K) bytes (may be NULL when that
- * size is 0), 256-byte aligned; its contents need no initialisation and are
- * clobbered.
+ * size is 0), 256-byte aligned.  Split-K plans keep per-tile arrival
+ * counters (first 4096 bytes) and fp32 partial tiles (after them) in it: the
+ * buffer must be zero-filled once before its first use (nvfp4_workspace_init,
+ * or any zero fill), and every completed call leaves the counters at zero
+ * again, so one workspace serves any number of calls and shapes.  Calls that
+ * share a workspace must be ordered on one stream (concurrent calls on one
+ * workspace race).
  */
 nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf,
                         const uint8_t* b, const uint8_t* b_sf,
@@ -78,6 +83,9 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf,
 
 /* Workspace bytes nvfp4_gemm needs for this shape (0 for most large shapes). */
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Zero-fill a workspace on `stream` with a kernel (safe inside graph capture). */
+nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Grouped-by-expert GEMM (the per-expert FP4 GEMMs of an MoE layer: pages

@@ -27,6 +27,7 @@ _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c
 SIGNATURES = {
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "nvfp4_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "nvfp4_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
                                           _vp, _vp]),
     "nvfp4_grouped_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
@@ -86,6 +87,25 @@ def nvfp4_gemm_plan(M: int, N: int, K: int) -> str:
 
 def nvfp4_gemm_workspace_size(M: int, N: int, K: int) -> int:
     return int(lib().nvfp4_gemm_workspace_size(M, N, K))
+
+
+def nvfp4_workspace_init(workspace, stream=None):
+    """Zero-fill a workspace tensor (needed once before its first use)."""
+    if workspace is None:
+        return None
+    st = lib().nvfp4_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "nvfp4_workspace_init")
+    return workspace
+
+
+def gemm_workspace(M: int, N: int, K: int, device="cuda"):
+    """Allocate and zero-fill the workspace nvfp4_gemm needs (None if none)."""
+    import torch
+    need = nvfp4_gemm_workspace_size(M, N, K)
+    if need == 0:
+        return None
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return nvfp4_workspace_init(ws)
 
 
 def nvfp4_grouped_workspace_size(rows: int, N: int, K: int, E: int) -> int:

@@ -79,8 +79,16 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
-  nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 1};
+  nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 0, 1, 1};
   return hip_status(nvfp4::launch_gemm(plan, p, (hipStream_t)stream), "nvfp4_gemm launch");
+}
+
+nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return ok();
+  if (!workspace) return fail(NVFP4_ERR_NULL, "workspace must be non-NULL");
+  if (!aligned(workspace, 4)) return fail(NVFP4_ERR_ALIGN, "workspace must be 4-byte aligned");
+  return hip_status(nvfp4::launch_workspace_init(workspace, workspace_bytes, (hipStream_t)stream),
+                    "nvfp4_workspace_init launch");
 }
 
 size_t nvfp4_grouped_workspace_size(int64_t rows, int64_t N, int64_t K, int32_t E) {

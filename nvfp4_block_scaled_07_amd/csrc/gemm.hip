@@ -8,31 +8,40 @@
 // precision).
 //
 // Design (gfx950):
-//  * Packed codes and scale bytes are staged HBM -> VGPR -> LDS with 16-byte
-//    loads, double buffered: a stage covers 256 K elements, i.e. 128 code
-//    bytes and 16 scale bytes per row.  LDS keeps the packed form (a quarter
-//    of the bytes of f16), laid out [chunk][row][16 B] so that the 64 lanes
-//    of a wave read contiguous 16-byte entries.
-//  * Each lane turns one 16-byte chunk (32 consecutive K elements of one row)
-//    into the f16 operands of 4 MFMA K-steps: hardware e2m1->f16 conversion
-//    plus one packed f16 multiply by the e4m3 block scale (exact in f16).
-//    A and B use the same lane->K map, so the order of K inside a chunk does
-//    not change the sum's terms.
-//  * The contraction runs on v_mfma_f32_32x32x16_f16 (large tiles) or
+//  * HBM -> LDS: packed codes and scale bytes go straight into LDS with
+//    global_load_lds (16 or 4 bytes per lane, no VGPR staging), STAGES-deep
+//    ring of buffers, one barrier per stage.  Code rows are stored row-major
+//    with the 16-byte chunks XOR-swizzled per row, which keeps both the
+//    coalesced global loads and the MFMA-side ds_read_b128 free of bank
+//    conflicts.
+//  * LDS -> VGPR -> MFMA: each lane reads one 16-byte chunk (32 consecutive K
+//    elements of one row) and turns it into the f16 operands of 4 MFMA
+//    K-steps: hardware e2m1->f16 conversion plus one packed f16 multiply by
+//    the e4m3 block scale (exact in f16).  A and B use the same lane->K map,
+//    so the order of K inside a chunk does not change the sum's terms.
+//  * The contraction is v_mfma_f32_32x32x16_f16 (large tiles) or
 //    v_mfma_f32_16x16x32_f16 (skinny and grouped tiles) with fp32
-//    accumulators; the e4m3 scales are not powers of two and come per 16
+//    accumulators.  The e4m3 scales are not powers of two and come per 16
 //    elements, so they cannot ride the E8M0-per-32 scaled FP4 MFMA exactly.
-//  * Split-K writes fp32 partials to the caller's workspace and a second
-//    kernel sums them in a fixed order (bitwise deterministic).
+//  * Split-K: each split writes its fp32 partial tile to the workspace; the
+//    last split of a tile to arrive (device-scope counter) sums the partials
+//    in split order, applies alpha and stores bf16, then resets the counter.
+//    One launch, bitwise deterministic.
+//  * Work-group order is remapped so that work-groups sharing operand rows
+//    run on the same XCD (its own 4 MB L2).
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "device.h"
 #include "internal.h"
 
 namespace nvfp4 {
 
-constexpr int kBK = 256;             // K elements per LDS stage
-constexpr int kChunks = kBK / 32;    // 16-byte chunks of codes per row per stage
-constexpr int kBKBytes = kBK / 2;    // code bytes per row per stage
-constexpr int kBKScales = kBK / 16;  // scale bytes per row per stage
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Split-K workspace: int32 arrival counters for up to 1024 tiles, then the
+// fp32 partial tiles.
+constexpr int64_t kCounterBytes = 4096;
 
 template <int MF>
 struct Mfma;
@@ -56,117 +65,192 @@ struct Mfma<16> {
   __device__ __forceinline__ static int row(int j, int g) { return 4 * g + j; }
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int MF_>
+template <int BM_, int BN_, int WM_, int WN_, int MF_, int BK_, int STAGES_, int IL_ = 0>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_;
-  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, BK = BK_, STAGES = STAGES_;
+  // IL > 0: ask the scheduler to interleave IL VALU instructions after each
+  // MFMA of a sub-step (dequantisation of the next K-step under the MFMAs)
+  static constexpr int IL = IL_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * 64;
   static constexpr int kWM = BM / WM;        // rows per wave
   static constexpr int kWN = BN / WN;        // cols per wave
   static constexpr int TM = kWM / MF;        // MFMA tiles per wave along M
   static constexpr int TN = kWN / MF;
   static constexpr int KG = 64 / MF;         // lane groups along K in one MFMA
-  static constexpr int kSub = kChunks / KG;  // MFMA sub-steps per stage (4 K-steps each)
+  static constexpr int CH = BK / 32;         // 16-byte code chunks per row per stage
+  static constexpr int RB = BK / 2;          // code bytes per row per stage
+  static constexpr int SB = BK / 16;         // scale bytes per row per stage
+  static constexpr int kSub = CH / KG;       // MFMA sub-steps per stage (4 K-steps each)
   static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "tile shape");
+  static_assert(BK == 128 || BK == 256, "stage depth");
+  static_assert(STAGES >= 2 && STAGES <= 8, "pipeline");
   typedef typename Mfma<MF>::Acc Acc;
 };
 
-template <int BM, int BN>
+template <class C>
 struct Smem {
-  u4_t a[2][kChunks][BM];
-  u4_t b[2][kChunks][BN];
-  u4_t asf[2][BM];
-  u4_t bsf[2][BN];
+  uint8_t a[C::STAGES][C::BM * C::RB];
+  uint8_t b[C::STAGES][C::BN * C::RB];
+  uint8_t asf[C::STAGES][C::BM * C::SB];
+  uint8_t bsf[C::STAGES][C::BN * C::SB];
 };
 
-// One operand tile: rows [0, rows) of `data` are valid; rows beyond are
-// clamped to the last valid row on load (their results are never stored).
+// XOR swizzle of the 16-byte chunk index of row r (CH chunks per row), chosen
+// per MFMA shape by measuring ds_read_b128 throughput of the MFMA-side read
+// pattern on gfx950 (rows r_in of one chunk per lane group): 32-row reads
+// prefer pairs of rows sharing a slot, 16-row reads a plain rotation.
+template <int CH, int MF>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 8) return MF == 32 ? ((r >> 1) & 7) : (r & 7);
+  else return MF == 32 ? ((r >> 1) & 3) : (r & 3);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over `bytes` bytes at `base`: loads at or beyond `bytes` return
+// zero, which is how rows past the end of an operand are filled.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Copy the [ROWS][BYTES] slice at column offset col of a row-major operand
+// (row r at base + r * ld, rows >= rows_valid read as zero) into contiguous
+// LDS with buffer_load ... lds, VEC bytes per lane.  SWZ stores 16-byte chunk
+// c of row r at slot c ^ swz(r).  Wave-instruction j of this tile is issued by
+// wave (BASE + j) % NWAVES, so the instructions of all tiles of a stage spread
+// evenly over the waves; instructions whose rows are all >= rows_dma are
+// skipped (uniform).
+template <int ROWS, int BYTES, int VEC>
+struct DmaShape {
+  static constexpr int kPerRow = BYTES / VEC;
+  static constexpr int kRowsPerInst = 64 / kPerRow;
+  static constexpr int kInst = (ROWS + kRowsPerInst - 1) / kRowsPerInst;
+  static_assert(64 % kPerRow == 0, "row split");
+  static_assert(VEC == 16 || VEC == 4, "dma width");
+};
+
+template <int ROWS, int BYTES, int VEC, int SWZ_MF, int NWAVES, int BASE>
+__device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int64_t ld, int rows_valid, int col,
+                                         int wave, int lane, int rows_dma = ROWS) {
+  typedef DmaShape<ROWS, BYTES, VEC> D;
+  const rsrc_t rs = make_rsrc(base + col, (uint32_t)((int64_t)rows_valid * ld - col));
+  const int lr = lane / D::kPerRow, p = lane % D::kPerRow;
+#pragma unroll
+  for (int j = 0; j < D::kInst; ++j) {
+    if ((BASE + j) % NWAVES == wave && j * D::kRowsPerInst < rows_dma) {
+      const int r = j * D::kRowsPerInst + lr;
+      if (D::kInst * D::kRowsPerInst == ROWS || r < ROWS) {
+        int c = p;
+        if constexpr (SWZ_MF != 0) c = p ^ swz<D::kPerRow, SWZ_MF>(r);
+        const uint32_t off = (uint32_t)(r * ld + c * VEC);
+        if constexpr (VEC == 16)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 4, off, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Wave index as a scalar: the compiler then emits uniform branches (not
+// exec-masked ones) for per-wave work such as the DMA assignment.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// One operand tile: rows [0, rows) of `data` are valid (rows >= 1).
 struct Operand {
   const uint8_t* data;
   const uint8_t* sf;
   int64_t ld;    // code bytes per row (K/2)
   int64_t lds;   // scale bytes per row (K/16)
-  int rows;      // >= 1
+  int rows;
 };
 
 template <class C>
-struct Stage {
-  static constexpr int NT = C::kThreads;
-  static constexpr int kA = C::BM * kChunks;
-  static constexpr int kB = C::BN * kChunks;
-  static constexpr int kS = C::BM + C::BN;
-  static constexpr int nA = (kA + NT - 1) / NT;
-  static constexpr int nB = (kB + NT - 1) / NT;
-  static constexpr int nS = (kS + NT - 1) / NT;
-  u4_t ra[nA], rb[nB], rs[nS];
-
-  __device__ __forceinline__ void load(const Operand& A, const Operand& B, int kt, int tid) {
-#pragma unroll
-    for (int i = 0; i < nA; ++i) {
-      const int idx = tid + i * NT;
-      if (kA % NT == 0 || idx < kA) {
-        const int row = min(idx / kChunks, A.rows - 1), ch = idx % kChunks;
-        ra[i] = *(const u4_t*)(A.data + row * A.ld + (int64_t)kt * kBKBytes + ch * 16);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < nB; ++i) {
-      const int idx = tid + i * NT;
-      if (kB % NT == 0 || idx < kB) {
-        const int row = min(idx / kChunks, B.rows - 1), ch = idx % kChunks;
-        rb[i] = *(const u4_t*)(B.data + row * B.ld + (int64_t)kt * kBKBytes + ch * 16);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < nS; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < C::BM) {
-        const int row = min(idx, A.rows - 1);
-        rs[i] = *(const u4_t*)(A.sf + row * A.lds + (int64_t)kt * kBKScales);
-      } else if (idx < kS) {
-        const int row = min(idx - C::BM, B.rows - 1);
-        rs[i] = *(const u4_t*)(B.sf + row * B.lds + (int64_t)kt * kBKScales);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(Smem<C::BM, C::BN>& sm, int st, int tid) {
-#pragma unroll
-    for (int i = 0; i < nA; ++i) {
-      const int idx = tid + i * NT;
-      if (kA % NT == 0 || idx < kA) sm.a[st][idx % kChunks][idx / kChunks] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < nB; ++i) {
-      const int idx = tid + i * NT;
-      if (kB % NT == 0 || idx < kB) sm.b[st][idx % kChunks][idx / kChunks] = rb[i];
-    }
-#pragma unroll
-    for (int i = 0; i < nS; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < C::BM) sm.asf[st][idx] = rs[i];
-      else if (idx < kS) sm.bsf[st][idx - C::BM] = rs[i];
-    }
-  }
+struct StageDma {
+  static constexpr int SV = C::SB == 16 ? 16 : 4;
+  typedef DmaShape<C::BM, C::RB, 16> A;
+  typedef DmaShape<C::BN, C::RB, 16> B;
+  typedef DmaShape<C::BM, C::SB, SV> AS;
+  typedef DmaShape<C::BN, C::SB, SV> BS;
+  static constexpr int kTotal = A::kInst + B::kInst + AS::kInst + BS::kInst;
+  // Every wave issues at least this many load instructions per stage.  A's
+  // code instructions come first and may be skipped (rows an expert does not
+  // have), so only the instructions after them are counted.
+  static constexpr int kMinPerWave = (kTotal - A::kInst) / C::kWaves;
+  static_assert(kMinPerWave * (C::STAGES - 2) <= 63, "vmcnt range");
 };
 
-// Scale pair (s, s) for half `hi` (0: first 16 elements of the chunk, 1:
-// second) from the two scale bytes in bits 0-15 of w.
-__device__ __forceinline__ h2_t scale_pair(uint32_t w, int hi) {
-  h2_t sp = e4m3x2_to_h2(w);
+template <class C>
+__device__ __forceinline__ void issue_stage(Smem<C>& sm, int buf, const Operand& A, const Operand& B, int kt,
+                                            int wave, int lane, int a_rows_dma) {
+  typedef StageDma<C> D;
+  constexpr int W = C::kWaves;
+  dma_tile<C::BM, C::RB, 16, C::MF, W, 0>(sm.a[buf], A.data, A.ld, A.rows, kt * C::RB, wave, lane, a_rows_dma);
+  dma_tile<C::BN, C::RB, 16, C::MF, W, D::A::kInst>(sm.b[buf], B.data, B.ld, B.rows, kt * C::RB, wave, lane);
+  dma_tile<C::BM, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst>(sm.asf[buf], A.sf, A.lds, A.rows,
+                                                                     kt * C::SB, wave, lane);
+  dma_tile<C::BN, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst>(sm.bsf[buf], B.sf, B.lds,
+                                                                                    B.rows, kt * C::SB, wave, lane);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then a work-group barrier.  The empty asm
+// keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until the stage whose loads were followed by `later` more issued
+// stages has landed in LDS (loads of one wave return in order), then barrier.
+template <class C, int L = C::STAGES - 2>
+__device__ __forceinline__ void stage_ready(int later) {
+  if constexpr (L <= 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (later >= L) {
+      wait_vm_barrier<L * StageDma<C>::kMinPerWave>();
+      return;
+    }
+    stage_ready<C, L - 1>(later);
+  }
+}
+
+__device__ __forceinline__ h2_t scale_pair(h2_t sp, int hi) {
   h2_t r;
   r[0] = sp[hi];
   r[1] = sp[hi];
   return r;
 }
 
+// LDS reads of the MFMA operands are issued as inline asm: the compiler then
+// does not treat them as aliasing the in-flight global_load_lds writes of later
+// stages (it would otherwise drain all loads before every read).  Completion
+// is awaited explicitly with lgkm_wait(), which re-defines every result so no
+// use can be scheduled before the wait.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
+__device__ __forceinline__ void ds_read128(u4_t& v, uint32_t a) { asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a)); }
+__device__ __forceinline__ void ds_read32(uint32_t& v, uint32_t a) { asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(a)); }
+__device__ __forceinline__ void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void pin(u4_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 // Multiply-accumulate one LDS stage into acc.  tm_active (uniform) limits the
-// row blocks that are computed (grouped experts with few rows).
+// row blocks that are computed (grouped experts with few rows).  Per K-step
+// only the A operands and one B operand are live, which keeps the 128x128
+// wave tile of the large plan inside the register file.
 template <class C>
-__device__ __forceinline__ void compute_stage(const Smem<C::BM, C::BN>& sm, int st, int tid, int tm_active,
+__device__ __forceinline__ void compute_stage(const Smem<C>& sm, int buf, int tm_active,
                                               typename C::Acc (&acc)[C::TM][C::TN]) {
-  const int lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = wave_id();
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r_in = lane % C::MF, g = lane / C::MF;
+  const uint32_t a_base = lds_addr(sm.a[buf]), b_base = lds_addr(sm.b[buf]);
+  const uint32_t as_base = lds_addr(sm.asf[buf]), bs_base = lds_addr(sm.bsf[buf]);
 #pragma unroll
   for (int s = 0; s < C::kSub; ++s) {
     const int c = C::KG * s + g;  // chunk of this lane: K offset 32c in the stage
@@ -176,121 +260,242 @@ __device__ __forceinline__ void compute_stage(const Smem<C::BM, C::BN>& sm, int 
     for (int tm = 0; tm < C::TM; ++tm) {
       if (tm < tm_active) {
         const int row = wm * C::kWM + tm * C::MF + r_in;
-        ac[tm] = sm.a[st][c][row];
-        asw[tm] = ((const uint32_t*)&sm.asf[st][row])[c >> 1] >> (16 * (c & 1));
+        ds_read128(ac[tm], a_base + row * C::RB + ((c ^ swz<C::CH, C::MF>(row)) << 4));
+        ds_read32(asw[tm], as_base + row * C::SB + 4 * (c >> 1));
       }
     }
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
       const int row = wn * C::kWN + tn * C::MF + r_in;
-      bc[tn] = sm.b[st][c][row];
-      bsw[tn] = ((const uint32_t*)&sm.bsf[st][row])[c >> 1] >> (16 * (c & 1));
+      ds_read128(bc[tn], b_base + row * C::RB + ((c ^ swz<C::CH, C::MF>(row)) << 4));
+      ds_read32(bsw[tn], bs_base + row * C::SB + 4 * (c >> 1));
+    }
+    lgkm_wait();
+    h2_t asp[C::TM], bsp[C::TN];
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      if (tm < tm_active) {
+        pin(ac[tm]);
+        pin(asw[tm]);
+        asp[tm] = e4m3x2_to_h2(asw[tm] >> (16 * (c & 1)));
+      }
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      pin(bc[tn]);
+      pin(bsw[tn]);
+      bsp[tn] = e4m3x2_to_h2(bsw[tn] >> (16 * (c & 1)));
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      h8_t af[C::TM], bf[C::TN];
+      h8_t af[C::TM];
 #pragma unroll
       for (int tm = 0; tm < C::TM; ++tm)
-        if (tm < tm_active) af[tm] = dequant8(ac[tm][t], scale_pair(asw[tm], t >> 1));
+        if (tm < tm_active) af[tm] = dequant8(ac[tm][t], scale_pair(asp[tm], t >> 1));
 #pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) bf[tn] = dequant8(bc[tn][t], scale_pair(bsw[tn], t >> 1));
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const h8_t bf = dequant8(bc[tn][t], scale_pair(bsp[tn], t >> 1));
 #pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm)
-        if (tm < tm_active) {
+        for (int tm = 0; tm < C::TM; ++tm)
+          if (tm < tm_active) acc[tm][tn] = Mfma<C::MF>::run(af[tm], bf, acc[tm][tn]);
+      }
+    }
+    if constexpr (C::IL > 0) {
 #pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<C::MF>::run(af[tm], bf[tn], acc[tm][tn]);
-        }
+      for (int i = 0; i < 4 * C::TM * C::TN; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, C::IL, 0);  // then IL VALU
+      }
     }
   }
 }
 
 template <class C>
-__device__ __forceinline__ void mainloop(Smem<C::BM, C::BN>& sm, const Operand& A, const Operand& B, int kt0,
-                                         int kt1, int tm_active, typename C::Acc (&acc)[C::TM][C::TN]) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void zero_acc(typename C::Acc (&acc)[C::TM][C::TN]) {
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
       for (int j = 0; j < Mfma<C::MF>::kAcc; ++j) acc[tm][tn][j] = 0.0f;
-  if (kt0 >= kt1) return;
-  Stage<C> stg;
-  stg.load(A, B, kt0, tid);
-  stg.store(sm, 0, tid);
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int st = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) stg.load(A, B, kt + 1, tid);
-    compute_stage<C>(sm, st, tid, tm_active, acc);
-    if (more) stg.store(sm, st ^ 1, tid);
-    __syncthreads();
+}
+
+// K-tiles [kt0, kt1) of the tile into acc (which is zeroed first).  Loads run
+// STAGES - 1 stages ahead of the MFMAs; each wait only drains the stage needed
+// next, so the later stages stay in flight across the barrier.
+template <class C>
+__device__ __forceinline__ void mainloop(Smem<C>& sm, const Operand& A, const Operand& B, int kt0, int kt1,
+                                         int tm_active, typename C::Acc (&acc)[C::TM][C::TN]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = wave_id();
+  zero_acc<C>(acc);
+  const int n = kt1 - kt0;
+  if (n <= 0) return;
+  // the previous user of these buffers (an earlier tile of this work-group)
+  // is done once every wave passes this barrier
+  wait_vm_barrier<0>();
+  // A rows whose products are used: fewer only when an expert has fewer rows
+  // than the tile (grouped plans have one wave row, WM == 1)
+  const int a_rows_dma = C::WM == 1 ? tm_active * C::MF : C::BM;
+#pragma unroll
+  for (int i = 0; i < C::STAGES - 1; ++i)
+    if (i < n) issue_stage<C>(sm, i, A, B, kt0 + i, wave, lane, a_rows_dma);
+  stage_ready<C>(min(C::STAGES - 2, n - 1));
+  for (int i = 0; i < n; ++i) {
+    const int pre = i + C::STAGES - 1;
+    if (pre < n) issue_stage<C>(sm, pre % C::STAGES, A, B, kt0 + pre, wave, lane, a_rows_dma);
+    compute_stage<C>(sm, i % C::STAGES, tm_active, acc);
+    if (i + 1 < n) stage_ready<C>(min(C::STAGES - 2, n - 2 - i));
   }
 }
 
-// Store alpha * acc as bf16 (F32OUT = false) or acc as fp32 partials.
-template <class C, bool F32OUT>
-__device__ __forceinline__ void epilogue(const typename C::Acc (&acc)[C::TM][C::TN], int tm_active, float alpha,
-                                         void* out, int64_t ldo, int rows_valid, int cols_valid) {
+// alpha * acc -> bf16 stores; bounds checks only for partial tiles.
+template <class C>
+__device__ __forceinline__ void store_bf16(const typename C::Acc (&acc)[C::TM][C::TN], int tm_active, float alpha,
+                                           uint16_t* out, int64_t ldo, int rows_valid, int cols_valid) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int n_in = lane % C::MF, g = lane / C::MF;
+  if (rows_valid >= C::BM && cols_valid >= C::BN) {  // full tile (uniform)
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      if (tm >= tm_active) continue;
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const int col = wn * C::kWN + tn * C::MF + n_in;
+#pragma unroll
+        for (int j = 0; j < Mfma<C::MF>::kAcc; ++j) {
+          const int row = wm * C::kWM + tm * C::MF + Mfma<C::MF>::row(j, g);
+          out[row * ldo + col] = f32_to_bf16_bits(alpha * acc[tm][tn][j]);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
     if (tm >= tm_active) continue;
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
       const int col = wn * C::kWN + tn * C::MF + n_in;
-      if (col >= cols_valid) continue;
 #pragma unroll
       for (int j = 0; j < Mfma<C::MF>::kAcc; ++j) {
         const int row = wm * C::kWM + tm * C::MF + Mfma<C::MF>::row(j, g);
-        if (row < rows_valid) {
-          if (F32OUT)
-            ((float*)out)[row * ldo + col] = acc[tm][tn][j];
-          else
-            ((uint16_t*)out)[row * ldo + col] = f32_to_bf16_bits(alpha * acc[tm][tn][j]);
-        }
+        if (row < rows_valid && col < cols_valid) out[row * ldo + col] = f32_to_bf16_bits(alpha * acc[tm][tn][j]);
       }
     }
   }
 }
 
+// Write acc as an fp32 [BM][BN] row-major tile (split-K partial).
 template <class C>
+__device__ __forceinline__ void store_partial(const typename C::Acc (&acc)[C::TM][C::TN], float* tile) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = wave_id();
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int n_in = lane % C::MF, g = lane / C::MF;
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int col = wn * C::kWN + tn * C::MF + n_in;
+#pragma unroll
+      for (int j = 0; j < Mfma<C::MF>::kAcc; ++j) {
+        const int row = wm * C::kWM + tm * C::MF + Mfma<C::MF>::row(j, g);
+        tile[row * C::BN + col] = acc[tm][tn][j];
+      }
+    }
+}
+
+// Sum the S (<= kMaxSplits) partial tiles in split order, scale by alpha,
+// store bf16 (bounds-checked).  All S loads of a 16-byte chunk are issued
+// before the first add (predicated), so one chunk costs one memory round trip.
+constexpr int kMaxSplits = 16;
+
+template <class C>
+__device__ __forceinline__ void reduce_partials(const float* part, int S, float alpha, uint16_t* out, int64_t ldo,
+                                                int rows_valid, int cols_valid) {
+  constexpr int kTile = C::BM * C::BN, kQ = kTile / 4, kQRow = C::BN / 4;
+  for (int q = threadIdx.x; q < kQ; q += C::kThreads) {
+    const f4_t* src = (const f4_t*)part + q;
+    f4_t v[kMaxSplits];
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z) {
+      if (z < S) v[z] = src[z * kQ];
+    }
+    f4_t s = v[0];
+#pragma unroll
+    for (int z = 1; z < kMaxSplits; ++z) {
+      if (z < S) s += v[z];
+    }
+    const int row = q / kQRow, col = (q % kQRow) * 4;
+    if (row < rows_valid) {
+      uint16_t* o = out + row * ldo + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (col + i < cols_valid) o[i] = f32_to_bf16_bits(alpha * s[i]);
+    }
+  }
+}
+
+// Map a linear work-group id to a logical id so that each XCD (work-groups
+// are dispatched round-robin over 8 XCDs) gets one contiguous logical range.
+__device__ __forceinline__ int xcd_remap(int b, int G) {
+  const int q = G / 8, r = G % 8, x = b % 8, i = b / 8;
+  return x * q + min(x, r) + i;
+}
+
+template <class C, bool SPLITK>
 __global__ __launch_bounds__(C::kThreads) void k_gemm(GemmLaunch p) {
-  __shared__ Smem<C::BM, C::BN> sm;
-  const int tile = blockIdx.x;
-  const int tmi = tile / p.tiles_n, tni = tile % p.tiles_n;
-  const int z = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) Smem<C> sm;
+  __shared__ int last_flag;
+  const int S = p.splits;
+  const int G = (int)(p.tiles_m * p.tiles_n) * S;
+  const int L = xcd_remap(blockIdx.x, G);
+  const int tile_l = L / S, z = L % S;
+  // grouped raster: bands of GROUP_M tile rows, column by column inside a band
+  const int tiles_m = (int)p.tiles_m, tiles_n = (int)p.tiles_n;
+  const int band = p.group_m * tiles_n;
+  const int first_m = (tile_l / band) * p.group_m;
+  const int gm = min(p.group_m, tiles_m - first_m);
+  const int tmi = first_m + (tile_l % band) % gm, tni = (tile_l % band) / gm;
+  const int tile = tmi * tiles_n + tni;
+
   const int64_t m0 = (int64_t)tmi * C::BM, n0 = (int64_t)tni * C::BN;
   const int64_t ld = p.K / 2, lds = p.K / 16;
   Operand A{p.a + m0 * ld, p.a_sf + m0 * lds, ld, lds, (int)min<int64_t>(C::BM, p.M - m0)};
   Operand B{p.b + n0 * ld, p.b_sf + n0 * lds, ld, lds, (int)min<int64_t>(C::BN, p.N - n0)};
-  const int nk = (int)(p.K / kBK);
-  const int kt0 = (int)((int64_t)z * nk / p.splits), kt1 = (int)((int64_t)(z + 1) * nk / p.splits);
+  const int nk = (int)(p.K / C::BK);
+  const int kt0 = (int)((int64_t)z * nk / S), kt1 = (int)((int64_t)(z + 1) * nk / S);
   typename C::Acc acc[C::TM][C::TN];
   mainloop<C>(sm, A, B, kt0, kt1, C::TM, acc);
-  if (p.splits == 1) {
-    const float alpha = p.alpha ? *p.alpha : 1.0f;
-    epilogue<C, false>(acc, C::TM, alpha, p.d + m0 * p.N + n0, p.N, A.rows, B.rows);
-  } else {
-    float* ws = p.ws + (int64_t)z * p.M * p.N;
-    epilogue<C, true>(acc, C::TM, 1.0f, ws + m0 * p.N + n0, p.N, A.rows, B.rows);
+  const float alpha = p.alpha ? *p.alpha : 1.0f;
+  uint16_t* out = p.d + m0 * p.N + n0;
+  if (!SPLITK || S == 1) {
+    store_bf16<C>(acc, C::TM, alpha, out, p.N, A.rows, B.rows);
+    return;
   }
-}
-
-// Sum split-K partials in split order, scale by alpha, round to bf16.
-__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int splits, int64_t mn,
-                                                       const float* __restrict__ alpha_p, uint16_t* __restrict__ d) {
-  const float alpha = alpha_p ? *alpha_p : 1.0f;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
-    float s = 0.0f;
-    for (int z = 0; z < splits; ++z) s += ws[(int64_t)z * mn + i];
-    d[i] = f32_to_bf16_bits(alpha * s);
+  // split-K: publish this split's partial, count arrivals, last one reduces
+  const int tid = threadIdx.x;
+  constexpr int kTileFloats = C::BM * C::BN;
+  int* counter = (int*)p.ws + tile;
+  float* part = p.ws + kCounterBytes / 4 + (int64_t)tile * S * kTileFloats;
+  store_partial<C>(acc, part + (int64_t)z * kTileFloats);
+  // every wave's partial stores reach L2, then one agent-scope release (L2
+  // write-back) publishes them before the arrival is counted
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = prev == S - 1;
+    if (prev == S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
+  __syncthreads();
+  if (!last_flag) return;
+  reduce_partials<C>(part, S, alpha, out, p.N, A.rows, B.rows);
+  if (tid == 0) *counter = 0;  // ready for the next call
 }
 
 // Offsets check for the grouped GEMM: status = 0, or 1 + first bad expert.
@@ -307,82 +512,155 @@ __global__ void k_check_offsets(const int32_t* __restrict__ offsets, int E, int6
   *status = bad;
 }
 
+// Grouped GEMM: one work-group per (expert, N tile); consecutive logical ids
+// (one XCD) walk the N tiles of one expert, so its A rows stay in that L2.
 template <class C>
-__global__ __launch_bounds__(C::kThreads) void k_grouped(GroupedLaunch p) {
-  __shared__ Smem<C::BM, C::BN> sm;
-  const int e = blockIdx.y;
-  const int64_t n0 = (int64_t)blockIdx.x * C::BN;
+__global__ __launch_bounds__(C::kThreads, 1) void k_grouped(GroupedLaunch p) {
+  __shared__ __attribute__((aligned(16))) Smem<C> sm;
+  const int tiles_n = (int)((p.N + C::BN - 1) / C::BN);
+  const int L = xcd_remap(blockIdx.x, tiles_n * p.E);
+  const int e = L / tiles_n;
+  const int64_t n0 = (int64_t)(L % tiles_n) * C::BN;
   const int64_t lo = p.offsets[e], hi = p.offsets[e + 1];
   if (lo < 0 || hi <= lo || hi > p.rows) return;  // empty or invalid expert
   const int64_t ld = p.K / 2, lds = p.K / 16;
   const float alpha = p.alpha ? p.alpha[e] : 1.0f;
   Operand B{p.b + ((int64_t)e * p.N + n0) * ld, p.b_sf + ((int64_t)e * p.N + n0) * lds, ld, lds,
             (int)min<int64_t>(C::BN, p.N - n0)};
-  const int nk = (int)(p.K / kBK);
+  const int nk = (int)(p.K / C::BK);
   for (int64_t mc = lo; mc < hi; mc += C::BM) {
     const int rows_c = (int)min<int64_t>(C::BM, hi - mc);
-    const int tm_active = (rows_c + C::MF - 1) / C::MF;  // row blocks of this wave layout (WM == 1)
+    const int tm_active = (rows_c + C::MF - 1) / C::MF;  // row blocks (one wave row: WM == 1)
     Operand A{p.a + mc * ld, p.a_sf + mc * lds, ld, lds, rows_c};
     typename C::Acc acc[C::TM][C::TN];
     mainloop<C>(sm, A, B, 0, nk, tm_active, acc);
-    epilogue<C, false>(acc, tm_active, alpha, p.d + mc * p.N + n0, p.N, rows_c, B.rows);
+    store_bf16<C>(acc, tm_active, alpha, p.d + mc * p.N + n0, p.N, rows_c, B.rows);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Plans and launchers.
 // ---------------------------------------------------------------------------
-typedef Cfg<128, 128, 2, 2, 32> CfgTile128;
-typedef Cfg<16, 128, 1, 4, 16> CfgSkinny16;
-typedef Cfg<32, 128, 1, 4, 16> CfgSkinny32;
-typedef Cfg<64, 128, 1, 4, 16> CfgSkinny64;
-typedef Cfg<64, 128, 1, 4, 16> CfgGrouped;
+typedef Cfg<256, 256, 2, 2, 32, 128, 4> CfgTile256;     // large M and N: 128x128 wave tiles
+typedef Cfg<128, 128, 2, 2, 32, 128, 4> CfgTile128;     // mid-large shapes (split-K)
+typedef Cfg<64, 64, 2, 2, 32, 128, 6> CfgTile64;        // mid shapes (split-K)
+typedef Cfg<16, 64, 1, 4, 16, 128, 8> CfgSkinny16;      // decode (split-K)
+typedef Cfg<32, 64, 1, 4, 16, 128, 6> CfgSkinny32;      // decode (split-K)
+typedef Cfg<64, 64, 1, 4, 16, 128, 6> CfgSkinny64;      // decode (split-K)
+typedef Cfg<256, 256, 2, 4, 32, 128, 4> CfgTile256w8;   // large: 8 waves of 128x64 (2 per SIMD)
+typedef Cfg<256, 256, 2, 2, 32, 128, 4, 4> CfgTile256il; // large, MFMA/VALU interleave hint
+typedef Cfg<128, 128, 2, 2, 32, 128, 4, 4> CfgTile128il; // mid-large, interleave hint
+typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 
-static const PlanInfo kPlans[] = {
-    {"tile128x128_mfma32", 128, 128},
-    {"skinny16x128_mfma16", 16, 128},
-    {"skinny32x128_mfma16", 32, 128},
-    {"skinny64x128_mfma16", 64, 128},
+struct PlanKind {
+  const char* name;
+  int bm, bn, bk;
+  bool splitk;
 };
+static const PlanKind kKinds[] = {
+    {"tile256x256_mfma32", 256, 256, 128, false},
+    {"tile128x128_mfma32", 128, 128, 128, true},
+    {"tile64x64_mfma32", 64, 64, 128, true},
+    {"skinny16x64_mfma16", 16, 64, 128, true},
+    {"skinny32x64_mfma16", 32, 64, 128, true},
+    {"skinny64x64_mfma16", 64, 64, 128, true},
+    {"tile256x256w8_mfma32", 256, 256, 128, false},
+    {"tile256x256il_mfma32", 256, 256, 128, false},
+    {"tile128x128il_mfma32", 128, 128, 128, true},
+};
+static constexpr int kNumKinds = (int)(sizeof(kKinds) / sizeof(kKinds[0]));
 
-static int target_blocks() { return 512; }  // two work-groups per CU on 256 CUs
+static const int kCUs = 256;
+static_assert(kCounterBytes / 4 >= kCUs, "split-K runs only below kCUs tiles");
+static const int64_t kMaxPartialBytesPerTile = 256 * 1024;  // one CU reduces a tile
 
+static const int64_t kTargetBlocks = 384;   // 1.5 work-groups per CU
+static const int64_t kMinStagesPerSplit = 6;
+
+static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) {
+  const int64_t tiles = pl.tiles_m * pl.tiles_n;
+  const int64_t nk = K / k.bk;
+  int64_t s = 1;
+  if (k.splitk && tiles < kCUs) {
+    if (forced > 0) {
+      s = forced;
+    } else {
+      s = (kTargetBlocks + tiles - 1) / tiles;
+      int64_t cap = kMaxPartialBytesPerTile / ((int64_t)k.bm * k.bn * 4);
+      if (cap > nk / kMinStagesPerSplit) cap = nk / kMinStagesPerSplit;
+      if (s > cap) s = cap;
+    }
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s > nk) s = nk;
+    if (s < 1) s = 1;
+  }
+  pl.splits = (int)s;
+  pl.workspace = 0;
+  if (s > 1) {
+    // fixed counter block first (same offsets for every shape, so counters a
+    // completed call leaves at zero stay valid for any later shape), partials after
+    const size_t part = (size_t)tiles * (size_t)s * (size_t)k.bm * (size_t)k.bn * sizeof(float);
+    pl.workspace = kCounterBytes + part;
+  }
+}
+
+// Plan choice, from measured sweeps on MI355X of the pages' shapes
+// (K = 6144): skinny 16-row tiles up to M = 32, 32-row tiles up to M = 64,
+// 64x64 tiles with split-K for the mid range, 128x128 and then 256x256 tiles
+// once there are enough of them to fill the CUs twice.
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
-  pl.kind = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 3 : 0;
-  const PlanInfo& info = kPlans[pl.kind];
-  pl.name = info.name;
-  pl.tiles_m = (M + info.bm - 1) / info.bm;
-  pl.tiles_n = (N + info.bn - 1) / info.bn;
-  const int64_t tiles = pl.tiles_m * pl.tiles_n;
-  const int64_t nk = K / kBK;
-  int64_t s = 1;
-  if (tiles > 0 && tiles < target_blocks()) s = (target_blocks() + tiles - 1) / tiles;
-  if (s > nk) s = nk;
-  if (s < 1) s = 1;
-  pl.splits = (int)s;
-  pl.workspace = s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+  int kind;
+  int forced_splits = 0;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (M <= 32) kind = 3;
+  else if (M <= 64) kind = 4;
+  else if (t256 >= 2 * kCUs) kind = 0;
+  else if (t128 >= 2 * kCUs) kind = 1;
+  else kind = 2;
+  // NVFP4_PLAN=<kind>[,<splits>] forces a plan (tuning sweeps only)
+  if (const char* env = getenv("NVFP4_PLAN")) {
+    int fk = -1, fs = 0;
+    if (sscanf(env, "%d,%d", &fk, &fs) >= 1 && fk >= 0 && fk < kNumKinds) {
+      kind = fk;
+      forced_splits = fs;
+    }
+  }
+  const PlanKind& k = kKinds[kind];
+  pl.kind = kind;
+  pl.name = k.name;
+  pl.tiles_m = (M + k.bm - 1) / k.bm;
+  pl.tiles_n = (N + k.bn - 1) / k.bn;
+  pl.group_m = 8;
+  if (!k.splitk || pl.tiles_m * pl.tiles_n >= kCUs) forced_splits = 1;
+  plan_splits(pl, k, K, forced_splits);
   return pl;
 }
 
+template <class C, bool SPLITK>
+static void launch_one(const GemmPlan& pl, const GemmLaunch& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)(pl.tiles_m * pl.tiles_n * pl.splits);
+  hipLaunchKernelGGL((k_gemm<C, SPLITK>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+}
+
 hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
-  p.tiles_n = (int)pl.tiles_n;
+  p.tiles_m = pl.tiles_m;
+  p.tiles_n = pl.tiles_n;
   p.splits = pl.splits;
-  dim3 grid((unsigned)(pl.tiles_m * pl.tiles_n), (unsigned)pl.splits);
+  p.group_m = pl.group_m;
   switch (pl.kind) {
-    case 0: hipLaunchKernelGGL(k_gemm<CfgTile128>, grid, dim3(CfgTile128::kThreads), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL(k_gemm<CfgSkinny16>, grid, dim3(CfgSkinny16::kThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(k_gemm<CfgSkinny32>, grid, dim3(CfgSkinny32::kThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL(k_gemm<CfgSkinny64>, grid, dim3(CfgSkinny64::kThreads), 0, stream, p); break;
+    case 0: launch_one<CfgTile256, false>(pl, p, stream); break;  // plan keeps splits == 1
+    case 1: launch_one<CfgTile128, true>(pl, p, stream); break;
+    case 2: launch_one<CfgTile64, true>(pl, p, stream); break;
+    case 3: launch_one<CfgSkinny16, true>(pl, p, stream); break;
+    case 4: launch_one<CfgSkinny32, true>(pl, p, stream); break;
+    case 5: launch_one<CfgSkinny64, true>(pl, p, stream); break;
+    case 6: launch_one<CfgTile256w8, false>(pl, p, stream); break;
+    case 7: launch_one<CfgTile256il, false>(pl, p, stream); break;
+    default: launch_one<CfgTile128il, true>(pl, p, stream); break;
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || pl.splits == 1) return err;
-  const int64_t mn = p.M * p.N;
-  int64_t blocks = (mn + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, p.ws, pl.splits, mn, p.alpha,
-                     p.d);
   return hipGetLastError();
 }
 
@@ -393,11 +671,26 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
     if (err != hipSuccess) return err;
   }
   if (!compute) return hipSuccess;
-  dim3 grid((unsigned)((p.N + CfgGrouped::BN - 1) / CfgGrouped::BN), (unsigned)p.E);
-  hipLaunchKernelGGL(k_grouped<CfgGrouped>, grid, dim3(CfgGrouped::kThreads), 0, stream, p);
+  const unsigned tiles_n = (unsigned)((p.N + CfgGrouped::BN - 1) / CfgGrouped::BN);
+  hipLaunchKernelGGL(k_grouped<CfgGrouped>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGrouped::kThreads), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
 size_t grouped_workspace(int64_t, int64_t, int64_t, int32_t) { return 0; }
+
+__global__ void k_fill_zero(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, (uint32_t*)ws, n);
+  return hipGetLastError();
+}
 
 }  // namespace nvfp4

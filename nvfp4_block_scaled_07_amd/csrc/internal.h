@@ -15,8 +15,9 @@ struct GemmLaunch {
   uint16_t* d;
   float* ws;
   int64_t M, N, K;
-  int tiles_n;
+  int64_t tiles_m, tiles_n;
   int splits;
+  int group_m;
 };
 
 struct GroupedLaunch {
@@ -31,16 +32,12 @@ struct GroupedLaunch {
   int E;
 };
 
-struct PlanInfo {
-  const char* name;
-  int bm, bn;
-};
-
 struct GemmPlan {
   const char* name;
   int kind;
   int64_t tiles_m, tiles_n;
   int splits;
+  int group_m;
   size_t workspace;
 };
 
@@ -48,6 +45,7 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
 hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
 size_t grouped_workspace(int64_t rows, int64_t N, int64_t K, int32_t E);
+hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);
 
 hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs, uint8_t* q, uint8_t* sf,
                            hipStream_t stream);

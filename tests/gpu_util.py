@@ -51,8 +51,7 @@ def gpu_gemm(a_t, asf_t, b_t, bsf_t, alpha_t, M, N, K, d_fill=None):
     d = torch.empty((M, N), dtype=torch.int16, device=DEV)
     if d_fill is not None:
         d.fill_(d_fill)
-    need = nv.nvfp4_gemm_workspace_size(M, N, K)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV) if need else None
+    ws = nv.gemm_workspace(M, N, K)
     nv.nvfp4_gemm(a_t, asf_t, b_t, bsf_t, alpha_t, d, M, N, K, ws)
     return d
 

@@ -92,7 +92,10 @@ def test_quantize_and_scale_error_paths():
 
 def test_plan_and_workspace_queries():
     assert nv.nvfp4_gemm_plan(16384, 6144, 6144).startswith("tile")
-    assert nv.nvfp4_gemm_plan(16, 768, 6144).startswith("skinny")
+    assert nv.nvfp4_gemm_plan(16, 768, 6144).startswith("skinny16x64")
     assert nv.nvfp4_gemm_plan(16, 768, 100) == "none"
     assert nv.nvfp4_gemm_workspace_size(16384, 6144, 6144) == 0
-    assert nv.nvfp4_gemm_workspace_size(16, 768, 6144) % (16 * 768 * 4) == 0
+    # split-K plans: a 4096-byte counter block, then fp32 partial tiles
+    ws = nv.nvfp4_gemm_workspace_size(16, 768, 6144)
+    tiles = 768 // 64
+    assert ws > 4096 and (ws - 4096) % (tiles * 16 * 64 * 4) == 0

@@ -164,3 +164,82 @@ def test_zero_sized_calls_are_noops():
     nv.nvfp4_gemm(x, s, x, s, None, d, 0, 4, 256)
     nv.nvfp4_gemm(x, s, x, s, None, d, 4, 0, 256)
     assert (host(d) == 7).all()
+
+
+def test_split_k_workspace_reuse_and_counters_return_to_zero():
+    # one workspace, zero-filled once, serves several split-K shapes in a row;
+    # afterwards every arrival counter is back at zero
+    shapes = [(16, 768, 6144), (64, 2048, 6144), (300, 384, 1024), (16, 768, 6144)]
+    need = max(nv.nvfp4_gemm_workspace_size(*s) for s in shapes)
+    assert need > 0
+    ws = nv.nvfp4_workspace_init(torch.empty(need, dtype=torch.uint8, device="cuda"))
+    for (M, N, K) in shapes:
+        a, b = synth.random_codes(M, M, K), synth.random_codes(N, N, K)
+        asf = synth.random_scale_bytes(M + 1, M, K, lo=0x30, hi=0x40)
+        bsf = synth.random_scale_bytes(N + 1, N, K, lo=0x30, hi=0x40)
+        d = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        say("workspace reuse", M, N, K, nv.nvfp4_gemm_plan(M, N, K))
+        nv.nvfp4_gemm(dev(a), dev(asf), dev(b), dev(bsf), None, d, M, N, K, ws)
+        check_gemm(bits(d), a, asf, b, bsf, np.float32(1), f"reuse {M}x{N}x{K}")
+        # the arrival counters occupy the first 4096 bytes of every split-K
+        # workspace; a completed call leaves all of them at zero
+        counters = host(ws)[:4096].view(np.int32)
+        assert (counters == 0).all(), counters
+
+
+def test_graph_capture_replays_match_eager():
+    # split-K and single-pass plans captured in one HIP graph; each replay,
+    # with eager work and synchronisation in between, must equal the eager run
+    cases = [(16, 768, 6144), (256, 768, 6144), (2048, 2048, 512)]
+    ins, outs, eager = [], [], []
+    for (M, N, K) in cases:
+        a, b = synth.random_codes(M + 5, M, K), synth.random_codes(N + 5, N, K)
+        asf = synth.random_scale_bytes(M + 6, M, K, lo=0x30, hi=0x40)
+        bsf = synth.random_scale_bytes(N + 6, N, K, lo=0x30, hi=0x40)
+        t = (dev(a), dev(asf), dev(b), dev(bsf), nv.gemm_workspace(M, N, K))
+        ins.append(t)
+        d = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+        outs.append(d)
+        say("graph eager", M, N, K, nv.nvfp4_gemm_plan(M, N, K))
+        nv.nvfp4_gemm(t[0], t[1], t[2], t[3], None, d, M, N, K, t[4])
+        eager.append(bits(d).copy())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    say("graph capture")
+    with torch.cuda.graph(g):
+        for (M, N, K), t, d in zip(cases, ins, outs):
+            nv.nvfp4_gemm(t[0], t[1], t[2], t[3], None, d, M, N, K, t[4])
+    for rep in range(3):
+        for d in outs:
+            d.fill_(0)
+        torch.cuda.synchronize()
+        say("graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for d, e in zip(outs, eager):
+            np.testing.assert_array_equal(bits(d), e)
+
+
+def test_every_plan_kind_forced(monkeypatch):
+    # each kernel instantiation (plan kind), with and without split-K, on a
+    # ragged shape; the plan is forced through NVFP4_PLAN=<kind>,<splits>
+    M, N, K = 200, 330, 1536
+    a, b = synth.random_codes(91, M, K), synth.random_codes(92, N, K)
+    asf = synth.random_scale_bytes(93, M, K, lo=0x28, hi=0x48)
+    bsf = synth.random_scale_bytes(94, N, K, lo=0x28, hi=0x48)
+    at, asft, bt, bsft = dev(a), dev(asf), dev(b), dev(bsf)
+    seen = set()
+    for kind in range(16):
+        for splits in (1, 3):
+            monkeypatch.setenv("NVFP4_PLAN", f"{kind},{splits}")
+            plan = nv.nvfp4_gemm_plan(M, N, K)
+            if plan in seen and splits == 1:
+                continue
+            seen.add(plan)
+            say("forced plan", kind, splits, plan, nv.nvfp4_gemm_workspace_size(M, N, K))
+            d = gpu_gemm(at, asft, bt, bsft, scalar(1.25), M, N, K, d_fill=0x7FC1)
+            check_gemm(bits(d), a, asf, b, bsf, np.float32(1.25), f"plan {plan} splits {splits}")
+    monkeypatch.delenv("NVFP4_PLAN")
+    assert len(seen) >= 6
