@@ -33,6 +33,7 @@ PEAK_F16_TFLOPS = 2500.0      # dense f16 MFMA, MI355X
 PEAK_FP4_TFLOPS = 10100.0     # dense fp4 MFMA, MI355X (context: not the issued instruction)
 PEAK_HBM_GBPS = 8000.0
 ROTATE_BYTES = 600 << 20      # > 2 x 256 MB Infinity Cache
+GRAPH_STEPS = 8               # steps captured per HIP graph
 
 
 def algo_bytes(M, N, K):
@@ -47,7 +48,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-call", type=int, default=0, metavar="M",
+                    help="for hardware-counter runs: one 256 MiB device copy (counter calibration), then 8 "
+                         "cold calls of the headline GEMM at this M; prints nothing else")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --profile-call: time the call as the headline does (graphs of 64 calls over "
+                         "the rotating sets, replayed 8 times) instead of 8 eager calls")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs of a --profile-call run (FETCH_SIZE, "
+                         "WRITE_SIZE) into the HBM traffic record read by the roofline (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic:
+        if not args.profile_call:
+            raise SystemExit("--traffic needs the --profile-call M the counters were taken with")
+        write_traffic_record(*args.traffic, m=args.profile_call)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not implemented", "n_gpus": args.gpus}), flush=True)
@@ -93,25 +108,41 @@ def main():
         qa, sfa, qb, sfb = s
         nv.nvfp4_gemm(qa[:m], sfa[:m], qb, sfb, alpha, outs[m], m, w["n"], w["k"], wss[m])
 
+    if args.profile_call:
+        profile_call(torch, nv, sweep_inputs, call, args.profile_call, args.graph)
+        return
+
     # ---------------- headline: attention-projection sweep -----------------
-    # Each step replays one captured HIP graph holding the seven GEMM calls on
-    # one buffer set; graphs rotate over the sets, so the host enqueues one
-    # replay per step and the GPU never waits on Python.
+    # Steps are captured into HIP graphs, GRAPH_STEPS consecutive steps (each
+    # on the next buffer set) per graph, as a serving loop would capture a
+    # whole pass; single-step graphs cover a remainder.  The host enqueues one
+    # replay per GRAPH_STEPS steps and the GPU never waits on Python.
     name = "attn_proj_n768_k6144"
     w, sets, alpha, outs, wss = sweep_inputs(name)
     ms = list(w["ms"])
     N, K = w["n"], w["k"]
-    graphs = [capture(torch, lambda s=s: [call(w, s, alpha, outs, wss, m) for m in ms]) for s in sets]
+    G = min(GRAPH_STEPS, len(sets))
+    multi = [capture(torch, lambda j=j: [call(w, sets[(j * G + t) % len(sets)], alpha, outs, wss, m)
+                                         for t in range(G) for m in ms])
+             for j in range((len(sets) + G - 1) // G)]
+    single = [capture(torch, lambda t=t: [call(w, sets[t], alpha, outs, wss, m) for m in ms]) for t in range(G)]
 
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
+    def run_steps(n, first):
+        i = 0
+        while n - i >= G:
+            multi[((first + i) // G) % len(multi)].replay()
+            i += G
+        while i < n:
+            single[(first + i) % G].replay()
+            i += 1
+
+    run_steps(args.warmup, 0)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % len(graphs)].replay()
+    run_steps(args.steps, args.warmup)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -139,15 +170,19 @@ def main():
     fl = 2.0 * dom["M"] * N * K
     by = algo_bytes(dom["M"], N, K)
     mfma_bound = fl / by > PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    call_name = f"nvfp4_gemm M={dom['M']} N={N} K={K}"
+    traffic = read_traffic_record(call_name, dom["plan"])
     if mfma_bound:
         roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_F16_TFLOPS, unit="TFLOP/s",
-                        frac=round(dom["tflops"] / PEAK_F16_TFLOPS, 4), traffic=None,
-                        kernel_call=f"nvfp4_gemm M={dom['M']} N={N} K={K} ({dom['plan']})")
+                        frac=round(dom["tflops"] / PEAK_F16_TFLOPS, 4), traffic=traffic,
+                        kernel_call=f"{call_name} ({dom['plan']})", algorithmic_bytes=by,
+                        algorithmic_flops=fl)
     else:
         roofline = dict(bound="hbm", achieved=dom["gbps"], peak=PEAK_HBM_GBPS, unit="GB/s",
-                        frac=round(dom["gbps"] / PEAK_HBM_GBPS, 4), traffic=None,
-                        kernel_call=f"nvfp4_gemm M={dom['M']} N={N} K={K} ({dom['plan']})")
-    del graphs
+                        frac=round(dom["gbps"] / PEAK_HBM_GBPS, 4), traffic=traffic,
+                        kernel_call=f"{call_name} ({dom['plan']})", algorithmic_bytes=by,
+                        algorithmic_flops=fl)
+    del multi, single
     del sets, outs, wss
     torch.cuda.empty_cache()
 
@@ -164,6 +199,99 @@ def main():
         out["other_workloads"] = other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_headline_dominant_call.json")
+COPY_BYTES = 256 << 20
+
+
+def kernel_sources_digest():
+    """sha256 over the library's kernel sources: a traffic record only holds
+    for the kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "nvfp4_block_scaled_07_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def profile_call(torch, nv, sweep_inputs, call, m, graph=False):
+    """Workload of the profiler runs: a plain 256 MiB copy (its FETCH_SIZE and
+    WRITE_SIZE calibrate the counters), then 8 cold calls of one headline GEMM,
+    or (graph=True) the per-call timing of the headline: a graph of 64 calls
+    over the rotating sets, replayed 8 times, with its HIP-event time printed."""
+    x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+    name = "attn_proj_n768_k6144"
+    w, sets, alpha, outs, wss = sweep_inputs(name)
+    if m not in outs:
+        raise SystemExit(f"M={m} is not a shape of {name}: {list(outs)}")
+    if graph:
+        reps = min(len(sets), 64)
+        g = capture(torch, lambda: [call(w, sets[i], alpha, outs, wss, m) for i in range(reps)])
+        us = replay_us(torch, torch.cuda.current_stream(), g, reps, repeats=8)
+        print(json.dumps({"call": f"nvfp4_gemm M={m} N={w['n']} K={w['k']} "
+                                  f"({nv.nvfp4_gemm_plan(m, w['n'], w['k'])})", "us_per_call": round(us, 3)}))
+        return
+    for i in range(8):
+        call(w, sets[i % len(sets)], alpha, outs, wss, m)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(path, counter):
+    import csv
+    rows = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic_record(fetch_csv, write_csv, m):
+    """FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by
+    what the same counter reads for the plain copy of COPY_BYTES (which must
+    fetch and write exactly COPY_BYTES), then averaged over the GEMM dispatches."""
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        copies = [v for n, g, v in rows if "copy" in n.lower() or "elementwise" in n.lower()]
+        gemm = [(n, g, v) for n, g, v in rows if "k_gemm" in n]
+        if not copies or not gemm:
+            raise SystemExit(f"{path}: no copy or no GEMM dispatch with {counter}")
+        calib = max(copies) * 1024.0 / COPY_BYTES
+        out[counter] = dict(copy_kib=max(copies), factor=round(1.0 / calib, 6),
+                            gemm_kib_mean=sum(v for _, _, v in gemm) / len(gemm),
+                            bytes_per_launch=sum(v for _, _, v in gemm) / len(gemm) * 1024.0 / calib,
+                            dispatches=len(gemm), kernel=gemm[0][0][:160], grid=gemm[0][1])
+    rec = dict(sources_sha256_16=kernel_sources_digest(), copy_bytes=COPY_BYTES, counters=out,
+               traffic_bytes_per_launch=round(out["FETCH_SIZE"]["bytes_per_launch"] +
+                                              out["WRITE_SIZE"]["bytes_per_launch"]))
+    import nvfp4_block_scaled_07_amd as nv
+    import synth
+    w = synth.WORKLOADS["attn_proj_n768_k6144"]
+    rec["call"] = f"nvfp4_gemm M={m} N={w['n']} K={w['k']} ({nv.nvfp4_gemm_plan(m, w['n'], w['k'])})"
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_RECORD, "w"), indent=1)
+    print(json.dumps(rec))
+
+
+def read_traffic_record(call_name, plan):
+    """HBM bytes per launch of the dominant call from the committed counter
+    record, or None when it was taken for another call or other kernels."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256_16") != kernel_sources_digest() or rec.get("call") != f"{call_name} ({plan})":
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def capture(torch, fn):

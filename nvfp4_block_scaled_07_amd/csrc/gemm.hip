@@ -9,8 +9,9 @@
 //
 // Design (gfx950):
 //  * HBM -> LDS: packed codes and scale bytes go straight into LDS with
-//    global_load_lds (16 or 4 bytes per lane, no VGPR staging), STAGES-deep
-//    ring of buffers, one barrier per stage.  Code rows are stored row-major
+//    buffer_load ... lds (16 or 4 bytes per lane, no VGPR staging; rows past
+//    the operand read as zero), STAGES-deep ring of buffers, one barrier per
+//    stage.  Code rows are stored row-major
 //    with the 16-byte chunks XOR-swizzled per row, which keeps both the
 //    coalesced global loads and the MFMA-side ds_read_b128 free of bank
 //    conflicts.
@@ -23,10 +24,15 @@
 //    v_mfma_f32_16x16x32_f16 (skinny and grouped tiles) with fp32
 //    accumulators.  The e4m3 scales are not powers of two and come per 16
 //    elements, so they cannot ride the E8M0-per-32 scaled FP4 MFMA exactly.
-//  * Split-K: each split writes its fp32 partial tile to the workspace; the
-//    last split of a tile to arrive (device-scope counter) sums the partials
-//    in split order, applies alpha and stores bf16, then resets the counter.
-//    One launch, bitwise deterministic.
+//  * K-groups: KS groups of waves share each LDS stage and take different
+//    MFMA sub-steps of it; their accumulators are summed through LDS.  This
+//    gives small problems several waves per SIMD (VALU issue from a single
+//    wave is slow) without shrinking the wave tile.
+//  * Split-K: each split writes its fp32 partial tile to the workspace in the
+//    accumulators' register order; the last split of a tile to arrive
+//    (device-scope counter) sums the partials in split order, applies alpha
+//    and stores bf16, then resets the counter.  One launch, bitwise
+//    deterministic.
 //  * Work-group order is remapped so that work-groups sharing operand rows
 //    run on the same XCD (its own 4 MB L2).
 #include <stdio.h>
@@ -65,13 +71,21 @@ struct Mfma<16> {
   __device__ __forceinline__ static int row(int j, int g) { return 4 * g + j; }
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int MF_, int BK_, int STAGES_, int IL_ = 0>
+template <int BM_, int BN_, int WM_, int WN_, int MF_, int BK_, int STAGES_, int IL_ = 0, int KS_ = 1,
+          int OCC_ = 1>
 struct Cfg {
+  // OCC: waves per SIMD the register allocation must leave room for
+  static constexpr int OCC = OCC_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, BK = BK_, STAGES = STAGES_;
   // IL > 0: ask the scheduler to interleave IL VALU instructions after each
   // MFMA of a sub-step (dequantisation of the next K-step under the MFMAs)
   static constexpr int IL = IL_;
-  static constexpr int kWaves = WM * WN;
+  // KS K-groups of WM x WN waves share every LDS stage: group k takes MFMA
+  // sub-steps k, k + KS, ... of each stage, and the groups' accumulators are
+  // summed through LDS at the end.  More waves per SIMD for the same wave tile.
+  static constexpr int KS = KS_;
+  static constexpr int kGroupWaves = WM * WN;
+  static constexpr int kWaves = KS * WM * WN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kWM = BM / WM;        // rows per wave
   static constexpr int kWN = BN / WN;        // cols per wave
@@ -85,6 +99,8 @@ struct Cfg {
   static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "tile shape");
   static_assert(BK == 128 || BK == 256, "stage depth");
   static_assert(STAGES >= 2 && STAGES <= 8, "pipeline");
+  static_assert(KS == 1 || KS == 2 || KS == 4, "K-groups");
+  static_assert(kSub % KS == 0, "sub-steps per K-group");
   typedef typename Mfma<MF>::Acc Acc;
 };
 
@@ -130,24 +146,39 @@ struct DmaShape {
   static_assert(VEC == 16 || VEC == 4, "dma width");
 };
 
+// Rows between repeats of swz(r): the swizzle of row j * RPI + lr equals that
+// of row (j % 2) * RPI + lr whenever this divides 2 * RPI.
+template <int CH, int MF>
+constexpr int swz_period() {
+  return CH == 8 ? (MF == 32 ? 16 : 8) : (CH == 4 ? (MF == 32 ? 8 : 4) : 8);
+}
+
 template <int ROWS, int BYTES, int VEC, int SWZ_MF, int NWAVES, int BASE>
 __device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int64_t ld, int rows_valid, int col,
                                          int wave, int lane, int rows_dma = ROWS) {
   typedef DmaShape<ROWS, BYTES, VEC> D;
+  static_assert(SWZ_MF == 0 || (2 * D::kRowsPerInst) % swz_period<D::kPerRow, SWZ_MF>() == 0, "swizzle period");
   const rsrc_t rs = make_rsrc(base + col, (uint32_t)((int64_t)rows_valid * ld - col));
   const int lr = lane / D::kPerRow, p = lane % D::kPerRow;
+  // per-lane byte offset within a group of kRowsPerInst rows (two variants:
+  // even and odd instructions); the row step goes in the scalar offset
+  uint32_t voff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int c = p;
+    if constexpr (SWZ_MF != 0) c = p ^ swz<D::kPerRow, SWZ_MF>(h * D::kRowsPerInst + lr);
+    voff[h] = (uint32_t)(lr * ld + c * VEC);
+  }
 #pragma unroll
   for (int j = 0; j < D::kInst; ++j) {
     if ((BASE + j) % NWAVES == wave && j * D::kRowsPerInst < rows_dma) {
       const int r = j * D::kRowsPerInst + lr;
       if (D::kInst * D::kRowsPerInst == ROWS || r < ROWS) {
-        int c = p;
-        if constexpr (SWZ_MF != 0) c = p ^ swz<D::kPerRow, SWZ_MF>(r);
-        const uint32_t off = (uint32_t)(r * ld + c * VEC);
+        const uint32_t soff = (uint32_t)(j * D::kRowsPerInst * ld);
         if constexpr (VEC == 16)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 16, voff[j & 1], soff, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 4, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 4, voff[j & 1], soff, 0, 0);
       }
     }
   }
@@ -247,12 +278,14 @@ __device__ __forceinline__ void compute_stage(const Smem<C>& sm, int buf, int tm
                                               typename C::Acc (&acc)[C::TM][C::TN]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
+  const int wm = gw / C::WN, wn = gw % C::WN;
   const int r_in = lane % C::MF, g = lane / C::MF;
   const uint32_t a_base = lds_addr(sm.a[buf]), b_base = lds_addr(sm.b[buf]);
   const uint32_t as_base = lds_addr(sm.asf[buf]), bs_base = lds_addr(sm.bsf[buf]);
 #pragma unroll
-  for (int s = 0; s < C::kSub; ++s) {
+  for (int ss = 0; ss < C::kSub / C::KS; ++ss) {
+    const int s = ss * C::KS + kgrp;
     const int c = C::KG * s + g;  // chunk of this lane: K offset 32c in the stage
     u4_t ac[C::TM], bc[C::TN];
     uint32_t asw[C::TM], bsw[C::TN];
@@ -354,8 +387,8 @@ template <class C>
 __device__ __forceinline__ void store_bf16(const typename C::Acc (&acc)[C::TM][C::TN], int tm_active, float alpha,
                                            uint16_t* out, int64_t ldo, int rows_valid, int cols_valid) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = wave_id();
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int lane = tid & 63, gw = wave_id() % C::kGroupWaves;
+  const int wm = gw / C::WN, wn = gw % C::WN;
   const int n_in = lane % C::MF, g = lane / C::MF;
   if (rows_valid >= C::BM && cols_valid >= C::BN) {  // full tile (uniform)
 #pragma unroll
@@ -388,56 +421,153 @@ __device__ __forceinline__ void store_bf16(const typename C::Acc (&acc)[C::TM][C
   }
 }
 
-// Write acc as an fp32 [BM][BN] row-major tile (split-K partial).
+// Split-K partials are kept in the accumulators' own register layout: float4
+// chunk i of lane l of wave slot w (within a K-group) sits at index
+// (w * kChunks + i) * 64 + l, so every store and every load of the reduction
+// moves a contiguous 1 KB per wave.
+template <class C>
+struct PartLayout {
+  static constexpr int kAccQ = Mfma<C::MF>::kAcc / 4;      // float4 per MFMA tile
+  static constexpr int kChunks = C::TM * C::TN * kAccQ;     // float4 per lane
+  static constexpr int kQ = C::kGroupWaves * kChunks * 64;  // float4 per tile
+  static_assert(kQ * 4 == C::BM * C::BN, "partial tile size");
+};
+
 template <class C>
 __device__ __forceinline__ void store_partial(const typename C::Acc (&acc)[C::TM][C::TN], float* tile) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = wave_id();
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int n_in = lane % C::MF, g = lane / C::MF;
+  typedef PartLayout<C> P;
+  const int lane = threadIdx.x & 63, gw = wave_id() % C::kGroupWaves;
+  f4_t* dst = (f4_t*)tile + (int64_t)gw * P::kChunks * 64 + lane;
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-      const int col = wn * C::kWN + tn * C::MF + n_in;
+    for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
-      for (int j = 0; j < Mfma<C::MF>::kAcc; ++j) {
-        const int row = wm * C::kWM + tm * C::MF + Mfma<C::MF>::row(j, g);
-        tile[row * C::BN + col] = acc[tm][tn][j];
+      for (int q = 0; q < P::kAccQ; ++q) {
+        f4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[tm][tn][4 * q + e];
+        dst[((tm * C::TN + tn) * P::kAccQ + q) * 64] = v;
       }
-    }
 }
 
-// Sum the S (<= kMaxSplits) partial tiles in split order, scale by alpha,
-// store bf16 (bounds-checked).  All S loads of a 16-byte chunk are issued
-// before the first add (predicated), so one chunk costs one memory round trip.
+// Sum the S partial tiles of one output tile in split order (((p0 + p1) + p2)
+// + ...), scale by alpha and store bf16 with bounds checks.  Float4 position f
+// of the layout above is handled by thread f mod kThreads; the S loads of
+// kLoads / S positions are issued together (kLoads float4 in flight: 16, or 8
+// where four waves per SIMD must fit), so a thread needs about
+// ceil(positions * S / kLoads) memory round trips.
+template <class C, int S>
+__device__ __forceinline__ void reduce_partials_s(const float* part, float alpha, uint16_t* out, int64_t ldo,
+                                                  int rows_valid, int cols_valid) {
+  typedef PartLayout<C> P;
+  constexpr int kLoads = C::OCC >= 4 ? 8 : 16;
+  constexpr int PB = S >= kLoads ? 1 : kLoads / S;  // positions per batch
+  const f4_t* src = (const f4_t*)part;
+  for (int f0 = threadIdx.x; f0 < P::kQ; f0 += C::kThreads * PB) {
+    f4_t v[PB][S];
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      const int f = f0 + b * C::kThreads;
+      if (f < P::kQ) {
+#pragma unroll
+        for (int z = 0; z < S; ++z) v[b][z] = src[z * P::kQ + f];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      const int f = f0 + b * C::kThreads;
+      if (f >= P::kQ) continue;
+      f4_t sum = v[b][0];
+#pragma unroll
+      for (int z = 1; z < S; ++z) sum += v[b][z];
+      const int lane = f & 63, i = (f >> 6) % P::kChunks, gw = (f >> 6) / P::kChunks;
+      const int q = i % P::kAccQ, tn = (i / P::kAccQ) % C::TN, tm = (i / P::kAccQ) / C::TN;
+      const int wm = gw / C::WN, wn = gw % C::WN;
+      const int col = wn * C::kWN + tn * C::MF + lane % C::MF, g = lane / C::MF;
+      if (col >= cols_valid) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wm * C::kWM + tm * C::MF + Mfma<C::MF>::row(4 * q + e, g);
+        if (row < rows_valid) out[row * ldo + col] = f32_to_bf16_bits(alpha * sum[e]);
+      }
+    }
+  }
+}
+
 constexpr int kMaxSplits = 16;
 
 template <class C>
 __device__ __forceinline__ void reduce_partials(const float* part, int S, float alpha, uint16_t* out, int64_t ldo,
                                                 int rows_valid, int cols_valid) {
-  constexpr int kTile = C::BM * C::BN, kQ = kTile / 4, kQRow = C::BN / 4;
-  for (int q = threadIdx.x; q < kQ; q += C::kThreads) {
-    const f4_t* src = (const f4_t*)part + q;
-    f4_t v[kMaxSplits];
+  switch (S) {
+#define NVFP4_RED(n) \
+  case n: reduce_partials_s<C, n>(part, alpha, out, ldo, rows_valid, cols_valid); break;
+    NVFP4_RED(2) NVFP4_RED(3) NVFP4_RED(4) NVFP4_RED(5) NVFP4_RED(6) NVFP4_RED(7) NVFP4_RED(8) NVFP4_RED(9)
+    NVFP4_RED(10) NVFP4_RED(11) NVFP4_RED(12) NVFP4_RED(13) NVFP4_RED(14) NVFP4_RED(15) NVFP4_RED(16)
+#undef NVFP4_RED
+    default: break;
+  }
+}
+
+// Sum the KS K-groups' accumulators into group 0's (pairwise tree through LDS:
+// groups [h, 2h) store, groups [0, h) add).  Each wave stores its registers in
+// its own lane-contiguous slice, so the paired wave reads them back with the
+// same layout and no bank conflicts.  Called by every wave of the work-group
+// after all LDS reads of the main loop.
+template <class C>
+struct GroupRed {
+  static constexpr int kChunks = C::TM * C::TN * Mfma<C::MF>::kAcc / 4;  // f4 per lane
+  static constexpr int kSlotFloats = C::kGroupWaves * kChunks * 64 * 4;  // = BM * BN
+  static constexpr int kSlots = C::KS / 2;
+  static constexpr int kFloats = C::KS > 1 ? kSlots * kSlotFloats : 1;
+};
+
+template <class C>
+__device__ __forceinline__ void reduce_groups(float* red, typename C::Acc (&acc)[C::TM][C::TN]) {
+  if constexpr (C::KS > 1) {
+    typedef GroupRed<C> R;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
+    __syncthreads();  // every wave is past its last read of the stage buffers
 #pragma unroll
-    for (int z = 0; z < kMaxSplits; ++z) {
-      if (z < S) v[z] = src[z * kQ];
-    }
-    f4_t s = v[0];
+    for (int h = C::KS / 2; h >= 1; h /= 2) {
+      if (kgrp >= h && kgrp < 2 * h) {
+        f4_t* dst = (f4_t*)(red + (int64_t)(kgrp - h) * R::kSlotFloats) + (int64_t)gw * R::kChunks * 64 + lane;
 #pragma unroll
-    for (int z = 1; z < kMaxSplits; ++z) {
-      if (z < S) s += v[z];
-    }
-    const int row = q / kQRow, col = (q % kQRow) * 4;
-    if (row < rows_valid) {
-      uint16_t* o = out + row * ldo + col;
+        for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (col + i < cols_valid) o[i] = f32_to_bf16_bits(alpha * s[i]);
+          for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+            for (int q = 0; q < Mfma<C::MF>::kAcc / 4; ++q) {
+              f4_t v;
+              for (int i = 0; i < 4; ++i) v[i] = acc[tm][tn][4 * q + i];
+              dst[((tm * C::TN + tn) * (Mfma<C::MF>::kAcc / 4) + q) * 64] = v;
+            }
+      }
+      __syncthreads();
+      if (kgrp < h) {
+        const f4_t* src = (const f4_t*)(red + (int64_t)kgrp * R::kSlotFloats) + (int64_t)gw * R::kChunks * 64 + lane;
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+            for (int q = 0; q < Mfma<C::MF>::kAcc / 4; ++q) {
+              const f4_t v = src[((tm * C::TN + tn) * (Mfma<C::MF>::kAcc / 4) + q) * 64];
+              for (int i = 0; i < 4; ++i) acc[tm][tn][4 * q + i] += v[i];
+            }
+      }
+      __syncthreads();
     }
   }
 }
+
+template <class C>
+union SharedGemm {
+  Smem<C> pipe;
+  float red[GroupRed<C>::kFloats];
+};
 
 // Map a linear work-group id to a logical id so that each XCD (work-groups
 // are dispatched round-robin over 8 XCDs) gets one contiguous logical range.
@@ -447,8 +577,9 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
 }
 
 template <class C, bool SPLITK>
-__global__ __launch_bounds__(C::kThreads) void k_gemm(GemmLaunch p) {
-  __shared__ __attribute__((aligned(16))) Smem<C> sm;
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gemm(GemmLaunch p) {
+  __shared__ __attribute__((aligned(16))) SharedGemm<C> shm;
+  Smem<C>& sm = shm.pipe;
   __shared__ int last_flag;
   const int S = p.splits;
   const int G = (int)(p.tiles_m * p.tiles_n) * S;
@@ -470,10 +601,12 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(GemmLaunch p) {
   const int kt0 = (int)((int64_t)z * nk / S), kt1 = (int)((int64_t)(z + 1) * nk / S);
   typename C::Acc acc[C::TM][C::TN];
   mainloop<C>(sm, A, B, kt0, kt1, C::TM, acc);
+  reduce_groups<C>(shm.red, acc);
+  const bool lead = C::KS == 1 || wave_id() < C::kGroupWaves;  // K-group 0 holds the sum
   const float alpha = p.alpha ? *p.alpha : 1.0f;
   uint16_t* out = p.d + m0 * p.N + n0;
   if (!SPLITK || S == 1) {
-    store_bf16<C>(acc, C::TM, alpha, out, p.N, A.rows, B.rows);
+    if (lead) store_bf16<C>(acc, C::TM, alpha, out, p.N, A.rows, B.rows);
     return;
   }
   // split-K: publish this split's partial, count arrivals, last one reduces
@@ -481,7 +614,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm(GemmLaunch p) {
   constexpr int kTileFloats = C::BM * C::BN;
   int* counter = (int*)p.ws + tile;
   float* part = p.ws + kCounterBytes / 4 + (int64_t)tile * S * kTileFloats;
-  store_partial<C>(acc, part + (int64_t)z * kTileFloats);
+  if (lead) store_partial<C>(acc, part + (int64_t)z * kTileFloats);
   // every wave's partial stores reach L2, then one agent-scope release (L2
   // write-back) publishes them before the arrival is counted
   __builtin_amdgcn_s_waitcnt(0);
@@ -542,14 +675,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped(GroupedLaunch p) {
 // Plans and launchers.
 // ---------------------------------------------------------------------------
 typedef Cfg<256, 256, 2, 2, 32, 128, 4> CfgTile256;     // large M and N: 128x128 wave tiles
-typedef Cfg<128, 128, 2, 2, 32, 128, 4> CfgTile128;     // mid-large shapes (split-K)
-typedef Cfg<64, 64, 2, 2, 32, 128, 6> CfgTile64;        // mid shapes (split-K)
-typedef Cfg<16, 64, 1, 4, 16, 128, 8> CfgSkinny16;      // decode (split-K)
-typedef Cfg<32, 64, 1, 4, 16, 128, 6> CfgSkinny32;      // decode (split-K)
-typedef Cfg<64, 64, 1, 4, 16, 128, 6> CfgSkinny64;      // decode (split-K)
+typedef Cfg<128, 128, 2, 2, 32, 128, 4, 0, 1, 2> CfgTile128;  // mid-large shapes (split-K)
+typedef Cfg<64, 64, 2, 2, 32, 128, 6, 0, 1, 2> CfgTile64;      // mid shapes (split-K)
+typedef Cfg<16, 64, 1, 4, 16, 128, 8, 0, 1, 3> CfgSkinny16;    // decode (split-K)
+typedef Cfg<32, 64, 1, 4, 16, 128, 6, 0, 1, 3> CfgSkinny32;    // decode (split-K)
+typedef Cfg<64, 64, 1, 4, 16, 128, 6, 0, 1, 2> CfgSkinny64;    // decode (split-K)
 typedef Cfg<256, 256, 2, 4, 32, 128, 4> CfgTile256w8;   // large: 8 waves of 128x64 (2 per SIMD)
 typedef Cfg<256, 256, 2, 2, 32, 128, 4, 4> CfgTile256il; // large, MFMA/VALU interleave hint
-typedef Cfg<128, 128, 2, 2, 32, 128, 4, 4> CfgTile128il; // mid-large, interleave hint
+typedef Cfg<128, 128, 2, 2, 32, 128, 4, 4, 1, 2> CfgTile128il;  // mid-large, interleave hint
+typedef Cfg<64, 64, 1, 1, 32, 256, 2, 0, 4, 4> CfgTile64k4;  // mid: 4 K-groups of one 64x64 wave
 typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 
@@ -568,6 +702,7 @@ static const PlanKind kKinds[] = {
     {"tile256x256w8_mfma32", 256, 256, 128, false},
     {"tile256x256il_mfma32", 256, 256, 128, false},
     {"tile128x128il_mfma32", 128, 128, 128, true},
+    {"tile64x64k4_mfma32", 64, 64, 256, true},
 };
 static constexpr int kNumKinds = (int)(sizeof(kKinds) / sizeof(kKinds[0]));
 
@@ -576,6 +711,7 @@ static_assert(kCounterBytes / 4 >= kCUs, "split-K runs only below kCUs tiles");
 static const int64_t kMaxPartialBytesPerTile = 256 * 1024;  // one CU reduces a tile
 
 static const int64_t kTargetBlocks = 384;   // 1.5 work-groups per CU
+static const int64_t kK4Blocks = 192;
 static const int64_t kMinStagesPerSplit = 6;
 
 static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) {
@@ -585,6 +721,11 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
   if (k.splitk && tiles < kCUs) {
     if (forced > 0) {
       s = forced;
+    } else if (k.bk == 256) {
+      // K-group tiles: about 192 work-groups (three quarters of the CUs, one
+      // work-group each) measured best; more splits cost more in the reduction
+      // than they gain in occupancy
+      s = (kK4Blocks + tiles / 2) / tiles;
     } else {
       s = (kTargetBlocks + tiles - 1) / tiles;
       int64_t cap = kMaxPartialBytesPerTile / ((int64_t)k.bm * k.bn * 4);
@@ -606,20 +747,18 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
 }
 
 // Plan choice, from measured sweeps on MI355X of the pages' shapes
-// (K = 6144): skinny 16-row tiles up to M = 32, 32-row tiles up to M = 64,
-// 64x64 tiles with split-K for the mid range, 128x128 and then 256x256 tiles
-// once there are enough of them to fill the CUs twice.
+// (K = 6144, N = 768 / 2048 / 6144): skinny 16-row tiles up to M = 32, 32-row
+// tiles up to M = 64, 64x64 K-group tiles (split-K while there are fewer than
+// 192 of them) up to the point where 256x256 tiles fill the CUs twice.
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   int kind;
   int forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (M <= 32) kind = 3;
   else if (M <= 64) kind = 4;
   else if (t256 >= 2 * kCUs) kind = 0;
-  else if (t128 >= 2 * kCUs) kind = 1;
-  else kind = 2;
+  else kind = 9;
   // NVFP4_PLAN=<kind>[,<splits>] forces a plan (tuning sweeps only)
   if (const char* env = getenv("NVFP4_PLAN")) {
     int fk = -1, fs = 0;
@@ -659,7 +798,8 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
     case 5: launch_one<CfgSkinny64, true>(pl, p, stream); break;
     case 6: launch_one<CfgTile256w8, false>(pl, p, stream); break;
     case 7: launch_one<CfgTile256il, false>(pl, p, stream); break;
-    default: launch_one<CfgTile128il, true>(pl, p, stream); break;
+    case 8: launch_one<CfgTile128il, true>(pl, p, stream); break;
+    default: launch_one<CfgTile64k4, true>(pl, p, stream); break;
   }
   return hipGetLastError();
 }
