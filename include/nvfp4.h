@@ -56,15 +56,15 @@ typedef enum {
   NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
   NVFP4_ERR_SHAPE = 2,       /* negative size, K % 16 != 0, offsets/E invalid */
   NVFP4_ERR_ALIGN = 3,       /* a base pointer is not aligned as documented */
-  NVFP4_ERR_UNSUPPORTED = 4, /* valid NVFP4 call outside this build's shapes (K % 256 != 0) */
+  NVFP4_ERR_UNSUPPORTED = 4, /* valid NVFP4 call outside this build's shapes (K % 256 != 0, K > 2^22) */
   NVFP4_ERR_WORKSPACE = 5,   /* workspace missing or smaller than *_workspace_size() */
   NVFP4_ERR_HIP = 6          /* a HIP runtime call or launch failed */
 } nvfp4_status;
 
 /*
  * Single GEMM (mm_fp4).  a, b, a_sf, b_sf: 16-byte aligned;
- * d: 4-byte aligned.  K must be a multiple of 256 (ERR_UNSUPPORTED otherwise;
- * ERR_SHAPE if not a multiple of 16).  alpha: device fp32 scalar, NULL means
+ * d: 4-byte aligned.  K must be a multiple of 256 and at most 2^22
+ * (ERR_UNSUPPORTED otherwise; ERR_SHAPE if not a multiple of 16).  alpha: device fp32 scalar, NULL means
  * 1.0f.  M == 0 or N == 0 is a successful no-op.  workspace: device memory of
  * at least nvfp4_gemm_workspace_size(M, N, K) bytes (may be NULL when that
  * size is 0), 256-byte aligned.  Split-K plans keep per-tile arrival

@@ -39,6 +39,9 @@ nvfp4_status check_k(int64_t K) {
   if (K % 256 != 0)
     return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: this build needs K %% 256 == 0", (long long)K);
   if (K == 0) return fail(NVFP4_ERR_UNSUPPORTED, "K = 0 is not supported");
+  // buffer offsets inside one 256-row operand tile stay below 2^31
+  if (K > (int64_t(1) << 22))
+    return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: this build needs K <= 4194304", (long long)K);
   return NVFP4_OK;
 }
 
@@ -49,12 +52,12 @@ extern "C" {
 const char* nvfp4_last_error(void) { return g_err; }
 
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % 256) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return 0;
   return nvfp4::choose_plan(M, N, K).workspace;
 }
 
 const char* nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % 256) return "none";
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return "none";
   return nvfp4::choose_plan(M, N, K).name;
 }
 

@@ -38,6 +38,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -160,8 +162,12 @@ __device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int6
   static_assert(SWZ_MF == 0 || (2 * D::kRowsPerInst) % swz_period<D::kPerRow, SWZ_MF>() == 0, "swizzle period");
   const rsrc_t rs = make_rsrc(base + col, (uint32_t)((int64_t)rows_valid * ld - col));
   const int lr = lane / D::kPerRow, p = lane % D::kPerRow;
+  const bool full = rows_valid >= ROWS;  // uniform
   // per-lane byte offset within a group of kRowsPerInst rows (two variants:
-  // even and odd instructions); the row step goes in the scalar offset
+  // even and odd instructions); the row step goes in the scalar offset.
+  // Lanes of rows >= rows_valid get a vector offset of 2^31, out of range
+  // whether or not the hardware adds the scalar offset before its range
+  // check, so they read zero and never touch memory past the operand.
   uint32_t voff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -175,10 +181,11 @@ __device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int6
       const int r = j * D::kRowsPerInst + lr;
       if (D::kInst * D::kRowsPerInst == ROWS || r < ROWS) {
         const uint32_t soff = (uint32_t)(j * D::kRowsPerInst * ld);
+        const uint32_t vo = (full || r < rows_valid) ? voff[j & 1] : 0x80000000u;
         if constexpr (VEC == 16)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 16, voff[j & 1], soff, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 16, vo, soff, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 4, voff[j & 1], soff, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 4, vo, soff, 0, 0);
       }
     }
   }
@@ -672,6 +679,320 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped(GroupedLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped GEMM with a shared f16 A tile.  Per expert only a few rows of A
+// meet a wide slab of B, so the waves split N and every wave needs all A
+// rows: dequantising A once per stage per work-group into LDS (instead of
+// once per wave) leaves each wave only its own B columns to dequantise, and
+// the kernel stays ahead of the B stream from HBM.
+// ---------------------------------------------------------------------------
+template <class C>
+struct SmemGA {
+  Smem<C> ring;
+  // f16 bits of the stage's A rows, [BM][BK]; 16-byte chunk j of row r is
+  // stored at slot j ^ (r & 15) (16-row MFMA reads hit 16 distinct slots)
+  uint16_t af[C::BM * C::BK];
+};
+
+__device__ __forceinline__ void ds_write128(uint32_t a, const u4_t& v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
+// Dequantise rows [0, rows16) of ring stage `buf` into af.  One 16-byte code
+// chunk (32 values) per thread and step.
+template <class C>
+__device__ __forceinline__ void dequant_a_stage(const SmemGA<C>& sm, int buf, int rows16) {
+  const uint32_t a_base = lds_addr(sm.ring.a[buf]), as_base = lds_addr(sm.ring.asf[buf]);
+  const uint32_t f_base = lds_addr(sm.af);
+  const int n = rows16 * C::CH;
+  for (int q = threadIdx.x; q < n; q += C::kThreads) {
+    const int r = q / C::CH, c = q % C::CH;
+    u4_t v;
+    uint32_t sw;
+    ds_read128(v, a_base + r * C::RB + ((c ^ swz<C::CH, C::MF>(r)) << 4));
+    ds_read32(sw, as_base + r * C::SB + 4 * (c >> 1));
+    lgkm_wait();
+    pin(v);
+    pin(sw);
+    const h2_t sp = e4m3x2_to_h2(sw >> (16 * (c & 1)));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const h8_t o = dequant8(v[t], scale_pair(sp, t >> 1));
+      u4_t w;
+      __builtin_memcpy(&w, &o, 16);
+      ds_write128(f_base + (r * C::BK + (((4 * c + t) ^ (r & 15)) << 3)) * 2, w);
+    }
+  }
+}
+
+// One stage: A operands straight from af (f16), B dequantised per wave.
+template <class C>
+__device__ __forceinline__ void compute_stage_ga(const SmemGA<C>& sm, int buf, int tm_active,
+                                                 typename C::Acc (&acc)[C::TM][C::TN]) {
+  static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wn = wave % C::WN;
+  const int r_in = lane % C::MF, g = lane / C::MF;
+  const uint32_t b_base = lds_addr(sm.ring.b[buf]), bs_base = lds_addr(sm.ring.bsf[buf]);
+  const uint32_t f_base = lds_addr(sm.af);
+#pragma unroll
+  for (int s = 0; s < C::kSub; ++s) {
+    const int c = C::KG * s + g;
+    u4_t bc[C::TN];
+    uint32_t bsw[C::TN];
+    u4_t af[C::TM][4];
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int row = wn * C::kWN + tn * C::MF + r_in;
+      ds_read128(bc[tn], b_base + row * C::RB + ((c ^ swz<C::CH, C::MF>(row)) << 4));
+      ds_read32(bsw[tn], bs_base + row * C::SB + 4 * (c >> 1));
+    }
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      if (tm < tm_active) {
+        const int row = tm * C::MF + r_in;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ds_read128(af[tm][t], f_base + (row * C::BK + (((4 * c + t) ^ (row & 15)) << 3)) * 2);
+      }
+    }
+    lgkm_wait();
+    h2_t bsp[C::TN];
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      pin(bc[tn]);
+      pin(bsw[tn]);
+      bsp[tn] = e4m3x2_to_h2(bsw[tn] >> (16 * (c & 1)));
+    }
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+      if (tm < tm_active)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pin(af[tm][t]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const h8_t bf = dequant8(bc[tn][t], scale_pair(bsp[tn], t >> 1));
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) {
+          if (tm < tm_active) {
+            h8_t a;
+            __builtin_memcpy(&a, &af[tm][t], 16);
+            acc[tm][tn] = Mfma<C::MF>::run(a, bf, acc[tm][tn]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// LDS writes of this wave done, then a work-group barrier; loads in flight
+// (vmcnt) are left alone.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads, 1) void k_grouped_a16(GroupedLaunch p) {
+  __shared__ __attribute__((aligned(16))) SmemGA<C> sm;
+  const int tiles_n = (int)((p.N + C::BN - 1) / C::BN);
+  const int L = xcd_remap(blockIdx.x, tiles_n * p.E);
+  const int e = L / tiles_n;
+  const int64_t n0 = (int64_t)(L % tiles_n) * C::BN;
+  const int64_t lo = p.offsets[e], hi = p.offsets[e + 1];
+  if (lo < 0 || hi <= lo || hi > p.rows) return;  // empty or invalid expert
+  const int64_t ld = p.K / 2, lds = p.K / 16;
+  const float alpha = p.alpha ? p.alpha[e] : 1.0f;
+  Operand B{p.b + ((int64_t)e * p.N + n0) * ld, p.b_sf + ((int64_t)e * p.N + n0) * lds, ld, lds,
+            (int)min<int64_t>(C::BN, p.N - n0)};
+  const int n = (int)(p.K / C::BK);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  for (int64_t mc = lo; mc < hi; mc += C::BM) {
+    const int rows_c = (int)min<int64_t>(C::BM, hi - mc);
+    const int tm_active = (rows_c + C::MF - 1) / C::MF;
+    Operand A{p.a + mc * ld, p.a_sf + mc * lds, ld, lds, rows_c};
+    typename C::Acc acc[C::TM][C::TN];
+    zero_acc<C>(acc);
+    wait_vm_barrier<0>();  // the previous row chunk is done with every buffer
+#pragma unroll
+    for (int i = 0; i < C::STAGES - 1; ++i)
+      if (i < n) issue_stage<C>(sm.ring, i, A, B, i, wave, lane, tm_active * C::MF);
+    stage_ready<C>(min(C::STAGES - 2, n - 1));
+    for (int i = 0; i < n; ++i) {
+      const int pre = i + C::STAGES - 1;
+      if (pre < n) issue_stage<C>(sm.ring, pre % C::STAGES, A, B, pre, wave, lane, tm_active * C::MF);
+      dequant_a_stage<C>(sm, i % C::STAGES, tm_active * C::MF);
+      lds_barrier();
+      compute_stage_ga<C>(sm, i % C::STAGES, tm_active, acc);
+      if (i + 1 < n) stage_ready<C>(min(C::STAGES - 2, n - 2 - i));
+    }
+    store_bf16<C>(acc, tm_active, alpha, p.d + mc * p.N + n0, p.N, rows_c, B.rows);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM streaming B through registers.  Every B element is used by
+// exactly one wave, so B skips LDS: each lane loads its own 16-byte code
+// chunks and scale words D stages ahead (buffer loads, rows past the expert's
+// N read as zero), which keeps D stages of the weight stream in flight per
+// wave.  A (a few rows per expert) is loaded the same way by one thread per
+// 16-byte chunk, dequantised once per stage into a double-buffered f16 LDS
+// tile and read by every wave.  No DMA and no manual wait counts: the
+// compiler orders every load.
+// ---------------------------------------------------------------------------
+template <class C>
+struct SmemGR {
+  // f16 bits of one stage's A rows, [BM][BK]; 16-byte chunk j of row r sits at
+  // slot j ^ (r & 15)
+  uint16_t af[2][C::BM * C::BK];
+};
+
+template <class C, int D>
+struct GRegs {
+  // A: each 16-byte code chunk of the stage's A tile is split over kAP threads
+  static constexpr int kAP = C::kThreads / (C::BM * C::CH);
+  static_assert(kAP * C::BM * C::CH == C::kThreads && (kAP == 1 || kAP == 2 || kAP == 4), "A chunk split");
+  typedef uint32_t u1_t __attribute__((ext_vector_type(1)));
+  typedef typename std::conditional<kAP == 1, u4_t, typename std::conditional<kAP == 2, u2_t, u1_t>::type>::type AQ;
+  u4_t bq[D][C::TN][C::kSub];
+  uint32_t bs[D][C::TN][C::kSub];
+  AQ aq[D];
+  uint32_t as[D];
+};
+
+// Loads of stage kt into register slot u.  Always the same instructions (so
+// the compiler can count outstanding loads exactly); a dead stage (live ==
+// false, past the end of K) uses out-of-range offsets, which return zero
+// without a memory access.
+template <class C, int D>
+__device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const rsrc_t& rb, const rsrc_t& rbs,
+                                        const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
+                                        const rsrc_t& ra, const rsrc_t& ras, uint32_t va, uint32_t vas) {
+  constexpr uint32_t kOut = 0x80000000u;
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+    for (int s = 0; s < C::kSub; ++s) {
+      R.bq[u][tn][s] = __builtin_bit_cast(
+          u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn][s] : kOut, kt * C::RB, 0));
+      R.bs[u][tn][s] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][s] : kOut, kt * C::SB, 0);
+    }
+  typedef typename GRegs<C, D>::AQ AQ;
+  if constexpr (GRegs<C, D>::kAP == 1)
+    R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va : kOut, kt * C::RB, 0));
+  else if constexpr (GRegs<C, D>::kAP == 2)
+    R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b64(ra, live ? va : kOut, kt * C::RB, 0));
+  else
+    R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b32(ra, live ? va : kOut, kt * C::RB, 0));
+  R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * C::SB, 0);
+}
+
+template <class C, int D>
+__global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p) {
+  static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
+  static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
+  static_assert(C::BM * C::CH <= C::kThreads, "one A chunk per thread");
+  __shared__ __attribute__((aligned(16))) SmemGR<C> sm;
+  const int tiles_n = (int)((p.N + C::BN - 1) / C::BN);
+  const int L = xcd_remap(blockIdx.x, tiles_n * p.E);
+  const int e = L / tiles_n;
+  const int64_t n0 = (int64_t)(L % tiles_n) * C::BN;
+  const int64_t lo = p.offsets[e], hi = p.offsets[e + 1];
+  if (lo < 0 || hi <= lo || hi > p.rows) return;  // empty or invalid expert
+  const int64_t ld = p.K / 2, lds = p.K / 16;
+  const float alpha = p.alpha ? p.alpha[e] : 1.0f;
+  const int b_rows = (int)min<int64_t>(C::BN, p.N - n0);
+  const uint8_t* bt = p.b + ((int64_t)e * p.N + n0) * ld;
+  const uint8_t* bst = p.b_sf + ((int64_t)e * p.N + n0) * lds;
+  const rsrc_t rb = make_rsrc(bt, (uint32_t)(b_rows * ld)), rbs = make_rsrc(bst, (uint32_t)(b_rows * lds));
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wn = wave % C::WN, r_in = lane % C::MF, g = lane / C::MF;
+  // per-lane B offsets (row part included; rows >= b_rows masked out of range)
+  uint32_t vb[C::TN][C::kSub], vbs[C::TN][C::kSub];
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const int row = wn * C::kWN + tn * C::MF + r_in;
+#pragma unroll
+    for (int s = 0; s < C::kSub; ++s) {
+      const int c = C::KG * s + g;
+      vb[tn][s] = row < b_rows ? (uint32_t)(row * ld + c * 16) : 0x80000000u;
+      vbs[tn][s] = row < b_rows ? (uint32_t)(row * lds + 4 * (c >> 1)) : 0x80000000u;
+    }
+  }
+  const int n = (int)(p.K / C::BK);
+  typedef GRegs<C, D> RT;
+  // this thread's part (ah of kAP) of A code chunk ac of row ar
+  const int q = threadIdx.x / RT::kAP, ah = threadIdx.x % RT::kAP, ar = q / C::CH, ac = q % C::CH;
+  for (int64_t mc = lo; mc < hi; mc += C::BM) {
+    const int rows_c = (int)min<int64_t>(C::BM, hi - mc);
+    const int tm_active = (rows_c + C::MF - 1) / C::MF;
+    const rsrc_t ra = make_rsrc(p.a + mc * ld, (uint32_t)(rows_c * ld));
+    const rsrc_t ras = make_rsrc(p.a_sf + mc * lds, (uint32_t)(rows_c * lds));
+    // every row block is computed (the kernel waits on HBM, not on MFMA), so
+    // the loop has no per-block branches; rows past the expert load as zero
+    // and their outputs are never stored
+    const uint32_t va = ar < rows_c ? (uint32_t)(ar * ld + ac * 16 + ah * (16 / RT::kAP)) : 0x80000000u;
+    const uint32_t vas = ar < rows_c ? (uint32_t)(ar * lds + 4 * (ac >> 1)) : 0x80000000u;
+    typename C::Acc acc[C::TM][C::TN];
+    zero_acc<C>(acc);
+    GRegs<C, D> R;
+    __syncthreads();  // the previous row chunk is done with both A tiles
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      gr_load<C, D>(R, u, u, true, rb, rbs, vb, vbs, ra, ras, va, vas);
+      __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
+    }
+    for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int st = i0 + u;  // < n: the launcher picks this kernel only when D divides n
+        {
+          uint16_t* af = sm.af[u & 1];
+          {
+            const h2_t sp = e4m3x2_to_h2(R.as[u] >> (16 * (ac & 1)));
+#pragma unroll
+            for (int tt = 0; tt < 4 / RT::kAP; ++tt) {
+              const int t = ah * (4 / RT::kAP) + tt;  // 8-value group of the chunk
+              const h8_t o = dequant8(R.aq[u][tt], scale_pair(sp, t >> 1));
+              *(h8_t*)(af + ar * C::BK + (((4 * ac + t) ^ (ar & 15)) << 3)) = o;
+            }
+          }
+          // LDS-only barrier: a __syncthreads() fence would also wait for the
+          // prefetched loads (loads and stores share one counter)
+          lds_barrier();
+#pragma unroll
+          for (int s = 0; s < C::kSub; ++s) {
+            const int c = C::KG * s + g;
+            h2_t bsp[C::TN];
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn) bsp[tn] = e4m3x2_to_h2(R.bs[u][tn][s] >> (16 * (c & 1)));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              h8_t a[C::TM];
+#pragma unroll
+              for (int tm = 0; tm < C::TM; ++tm) {
+                const int row = tm * C::MF + r_in;
+                a[tm] = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
+              }
+#pragma unroll
+              for (int tn = 0; tn < C::TN; ++tn) {
+                const h8_t bf = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
+#pragma unroll
+                for (int tm = 0; tm < C::TM; ++tm) acc[tm][tn] = Mfma<C::MF>::run(a[tm], bf, acc[tm][tn]);
+              }
+            }
+          }
+          // keep the reload of slot u after its last reads, so old and new
+          // contents share registers (no copies that would wait on the load)
+          __builtin_amdgcn_sched_barrier(0);
+          gr_load<C, D>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, ra, ras, va, vas);
+        }
+      }
+    }
+    store_bf16<C>(acc, tm_active, alpha, p.d + mc * p.N + n0, p.N, rows_c, b_rows);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Plans and launchers.
 // ---------------------------------------------------------------------------
 typedef Cfg<256, 256, 2, 2, 32, 128, 4> CfgTile256;     // large M and N: 128x128 wave tiles
@@ -686,6 +1007,8 @@ typedef Cfg<128, 128, 2, 2, 32, 128, 4, 4, 1, 2> CfgTile128il;  // mid-large, in
 typedef Cfg<64, 64, 1, 1, 32, 256, 2, 0, 4, 4> CfgTile64k4;  // mid: 4 K-groups of one 64x64 wave
 typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
+typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass
+typedef Cfg<32, 256, 1, 8, 16, 256, 2> CfgGroupedReg;    // MoE experts, B streamed through registers
 
 struct PlanKind {
   const char* name;
@@ -811,9 +1134,27 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
     if (err != hipSuccess) return err;
   }
   if (!compute) return hipSuccess;
-  const unsigned tiles_n = (unsigned)((p.N + CfgGrouped::BN - 1) / CfgGrouped::BN);
-  hipLaunchKernelGGL(k_grouped<CfgGrouped>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGrouped::kThreads), 0, stream,
-                     p);
+  // Kernel choice, measured on the 256-expert top-8 workload (K = 6144):
+  // B streamed through registers (2 stages ahead, 4 waves per SIMD) when 2
+  // divides K / 256, else the shared-f16-A kernel.  NVFP4_GPLAN=<0|1|2>
+  // forces the per-wave-dequant, shared-f16-A or register kernel (tuning and
+  // tests only).
+  int gk = (p.K / 256) % 2 == 0 ? 2 : 1;
+  if (const char* env = getenv("NVFP4_GPLAN")) gk = atoi(env);
+  if (gk == 2 && (p.K / 256) % 2) gk = 1;
+  if (gk == 0) {
+    const unsigned tiles_n = (unsigned)((p.N + CfgGrouped::BN - 1) / CfgGrouped::BN);
+    hipLaunchKernelGGL(k_grouped<CfgGrouped>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGrouped::kThreads), 0, stream,
+                       p);
+  } else if (gk == 2) {
+    const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
+    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2>), dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedReg::kThreads),
+                       0, stream, p);
+  } else {
+    const unsigned tiles_n = (unsigned)((p.N + CfgGroupedA16::BN - 1) / CfgGroupedA16::BN);
+    hipLaunchKernelGGL(k_grouped_a16<CfgGroupedA16>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedA16::kThreads),
+                       0, stream, p);
+  }
   return hipGetLastError();
 }
 

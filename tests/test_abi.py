@@ -48,6 +48,8 @@ def test_gemm_error_paths():
     assert _gemm(M=-1) == 2
     assert _gemm(K=128) == 4 and "256" in nv.nvfp4_last_error()
     assert _gemm(K=0) == 4
+    assert _gemm(K=(1 << 22) + 256) == 4 and "4194304" in nv.nvfp4_last_error()
+    assert nv.nvfp4_gemm_workspace_size(16, 768, (1 << 22) + 256) == 0
     assert _gemm(a=None) == 1
     assert _gemm(d=None) == 1
     assert _gemm(a=FAKE + 8) == 3

@@ -117,3 +117,23 @@ def test_invalid_offsets_reported_and_skipped():
     d2, st2 = _grouped(dev(a), dev(asf), dev(b), dev(bsf), dev(off2), dev(alpha), 300, 192, 512, 8)
     assert int(host(st2)[0]) == 8
     assert (bits(d2)[70:] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("gplan,K", [(0, 768), (1, 768), (2, 1536), (2, 768)])
+def test_every_grouped_kernel(gplan, K, monkeypatch):
+    # each grouped kernel (forced through NVFP4_GPLAN; K = 1536 lets the
+    # register kernel's prefetch depth 2 divide K / 256, K = 768 does not and
+    # must fall back), ragged N, experts of 0, 1, 5, 65 and 129 rows (several
+    # row passes)
+    monkeypatch.setenv("NVFP4_GPLAN", str(gplan))
+    rows, E, N = 300, 8, 330
+    off, a, asf, b, bsf, alpha = _small_problem([0, 0, 5, 5, 70, 70, 71, 200, 250], rows, E, N, K, seed=40)
+    say("grouped kernel", gplan, "K", K)
+    d, st = _grouped(dev(a), dev(asf), dev(b), dev(bsf), dev(off), dev(alpha), rows, N, K, E)
+    assert int(host(st)[0]) == 0
+    db = bits(d)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], alpha[e], f"gplan {gplan} expert {e}")
+    assert (db[250:] == SENTINEL).all()
