@@ -241,5 +241,8 @@ def test_every_plan_kind_forced(monkeypatch):
             say("forced plan", kind, splits, plan, nv.nvfp4_gemm_workspace_size(M, N, K))
             d = gpu_gemm(at, asft, bt, bsft, scalar(1.25), M, N, K, d_fill=0x7FC1)
             check_gemm(bits(d), a, asf, b, bsf, np.float32(1.25), f"plan {plan} splits {splits}")
+            # bitwise deterministic: a second call (fresh workspace) repeats every bit
+            d2 = gpu_gemm(at, asft, bt, bsft, scalar(1.25), M, N, K, d_fill=0x1234)
+            np.testing.assert_array_equal(bits(d2), bits(d), err_msg=f"plan {plan} splits {splits} rerun")
     monkeypatch.delenv("NVFP4_PLAN")
     assert len(seen) >= 6

@@ -99,3 +99,36 @@ def test_all_zero_tensor_scale_is_one():
     x = torch.zeros(1000, dtype=torch.float32, device="cuda")
     say("zero tensor scale")
     assert host(gpu_global_scale(x))[0] == np.float32(1.0)
+
+
+def _anchored_blocks(vals: np.ndarray, anchor: float) -> np.ndarray:
+    """Blocks of 16 whose first element is `anchor` (|anchor| = 6 sets the
+    block scale to exactly 1 at gs = 1, so r = 1 and the codes are e2m1(x))
+    and whose other 15 elements are `vals` (|v| <= 6), as rows of 64."""
+    n = -(-len(vals) // 15)
+    blk = np.zeros((n, 16), np.float32)
+    blk[:, 0] = anchor
+    body = np.zeros(n * 15, np.float32)
+    body[:len(vals)] = vals
+    blk[:, 1:] = body.reshape(n, 15)
+    flat = blk.reshape(-1)
+    flat = np.concatenate([flat, np.zeros((-len(flat)) % 64, np.float32)])
+    return flat.reshape(-1, 64)
+
+
+def test_e2m1_rounding_sweep_over_fp32_patterns():
+    # every 61st fp32 bit pattern in [0, 6] (about 17.8 million values) plus a
+    # dense window of +-2048 patterns around each rounding threshold, in both
+    # signs: the GPU's e2m1 rounding must give the oracle's codes everywhere
+    hi = int(np.float32(6.0).view(np.uint32))
+    bits = np.arange(0, hi + 1, 61, dtype=np.uint32)
+    windows = [np.arange(int(np.float32(t).view(np.uint32)) - 2048, int(np.float32(t).view(np.uint32)) + 2049,
+                         dtype=np.uint32) for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0)]
+    bits = np.concatenate([bits, np.arange(0, 4096, dtype=np.uint32)] + windows)
+    vals = bits.view(np.float32)
+    vals = vals[np.abs(vals) <= 6.0]
+    for sign, anchor in ((1.0, 6.0), (-1.0, -6.0)):
+        x = _anchored_blocks((vals * np.float32(sign)).astype(np.float32), anchor)
+        for lo in range(0, x.shape[0], 1 << 16):
+            part = np.ascontiguousarray(x[lo:lo + (1 << 16)])
+            _check_quant(part, np.float32(1), None, f"e2m1 sweep sign {sign:+.0f} rows {lo}")
