@@ -115,6 +115,40 @@ nvfp4_status nvfp4_grouped_gemm(const uint8_t* a, const uint8_t* a_sf,
 size_t nvfp4_grouped_workspace_size(int64_t rows, int64_t N, int64_t K, int32_t E);
 
 /*
+ * Grouped GEMM on pre-packed weights.  The pages run the MoE expert GEMM
+ * over static expert weights ("When a Benchmark Crashes: The Elusive FP4 GEMM
+ * Comparison on Blackwell SM120", section "Why This Message Was Written": 256
+ * experts, per-expert batches of 16-64 tokens), which makes it bound by the
+ * weight stream from HBM.  Rearranging those weights once, so that each
+ * 256-element K stage of each 256-row slab of an expert is one contiguous
+ * block, lets the kernel stream them in long runs.  The arithmetic is that of
+ * nvfp4_grouped_gemm; only the weight layout differs.
+ *
+ * nvfp4_grouped_packed_size: bytes of the packed codes (return value) and of
+ * the packed scales (*sf_bytes, if non-NULL) for E experts of N x K weights;
+ * 0 when the shape is not supported (K % 512 != 0, K > 2^22, N, E <= 0).
+ *
+ * nvfp4_grouped_pack_b: b uint8 [E][N][K/2] and b_sf uint8 [E][N][K/16]
+ * (the nvfp4_grouped_gemm layout) -> packed, packed_sf (caller-allocated,
+ * sizes from nvfp4_grouped_packed_size).  Layout, per expert e, slab
+ * t = 0 .. ceil(N/256)-1 and stage k = 0 .. K/256-1: block
+ * (e * ceil(N/256) + t) * (K/256) + k holds rows t*256 .. t*256+255 of expert
+ * e, 128 code bytes (K elements 256k .. 256k+255) per row, and likewise 16
+ * scale bytes per row; rows past N are zero.  All pointers 16-byte aligned.
+ * K % 512 == 0 (ERR_UNSUPPORTED otherwise).  Asynchronous on stream.
+ *
+ * nvfp4_grouped_gemm_packed: as nvfp4_grouped_gemm with b, b_sf replaced by
+ * the packed buffers; no workspace.  K % 512 == 0.
+ */
+size_t nvfp4_grouped_packed_size(int64_t N, int64_t K, int32_t E, size_t* sf_bytes);
+nvfp4_status nvfp4_grouped_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64_t K, int32_t E,
+                                  uint8_t* packed, uint8_t* packed_sf, void* stream);
+nvfp4_status nvfp4_grouped_gemm_packed(const uint8_t* a, const uint8_t* a_sf, const uint8_t* packed,
+                                       const uint8_t* packed_sf, const int32_t* offsets, const float* alpha,
+                                       uint16_t* d, int64_t rows, int64_t N, int64_t K, int32_t E,
+                                       int32_t* status, void* stream);
+
+/*
  * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
  * The pages never quantise (their test used random bytes); this follows the
  * block_size 16 and e4m3fn scale format of the pages above with these steps,

@@ -31,6 +31,10 @@ SIGNATURES = {
     "nvfp4_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
                                           _vp, _vp]),
     "nvfp4_grouped_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "nvfp4_grouped_packed_size": (_sz, [_i64, _i64, _i32, _vp]),
+    "nvfp4_grouped_pack_b": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "nvfp4_grouped_gemm_packed": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp,
+                                                 _vp]),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_global_scale": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_alpha_from_scales": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
@@ -130,6 +134,38 @@ def nvfp4_grouped_gemm(a, a_sf, b, b_sf, offsets, alpha, d, rows: int, N: int, K
     st = lib().nvfp4_grouped_gemm(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(offsets), _ptr(alpha), _ptr(d),
                                   rows, N, K, E, _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
     _check(st, "nvfp4_grouped_gemm")
+    return d
+
+
+def nvfp4_grouped_packed_size(N: int, K: int, E: int):
+    """(code bytes, scale bytes) of the packed expert weights (0, 0 if unsupported)."""
+    sf = ctypes.c_size_t(0)
+    code = int(lib().nvfp4_grouped_packed_size(N, K, E, ctypes.byref(sf)))
+    return code, int(sf.value)
+
+
+def nvfp4_grouped_pack_b(b, b_sf, N: int, K: int, E: int, packed, packed_sf, stream=None):
+    st = lib().nvfp4_grouped_pack_b(_ptr(b), _ptr(b_sf), N, K, E, _ptr(packed), _ptr(packed_sf), _stream(stream))
+    _check(st, "nvfp4_grouped_pack_b")
+    return packed, packed_sf
+
+
+def grouped_pack(b, b_sf, N: int, K: int, E: int, device="cuda"):
+    """Allocate and fill the packed expert weights for nvfp4_grouped_gemm_packed."""
+    import torch
+    cb, sb = nvfp4_grouped_packed_size(N, K, E)
+    if cb == 0:
+        raise Nvfp4Error(4, "grouped_pack", f"N={N}, K={K}, E={E} cannot be packed (needs K % 512 == 0)")
+    packed = torch.empty(cb, dtype=torch.uint8, device=device)
+    packed_sf = torch.empty(sb, dtype=torch.uint8, device=device)
+    return nvfp4_grouped_pack_b(b, b_sf, N, K, E, packed, packed_sf)
+
+
+def nvfp4_grouped_gemm_packed(a, a_sf, packed, packed_sf, offsets, alpha, d, rows: int, N: int, K: int, E: int,
+                              status=None, stream=None):
+    st = lib().nvfp4_grouped_gemm_packed(_ptr(a), _ptr(a_sf), _ptr(packed), _ptr(packed_sf), _ptr(offsets),
+                                         _ptr(alpha), _ptr(d), rows, N, K, E, _ptr(status), _stream(stream))
+    _check(st, "nvfp4_grouped_gemm_packed")
     return d
 
 

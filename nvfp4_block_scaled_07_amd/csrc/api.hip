@@ -127,6 +127,63 @@ nvfp4_status nvfp4_grouped_gemm(const uint8_t* a, const uint8_t* a_sf, const uin
   return hip_status(nvfp4::launch_grouped(p, status, (hipStream_t)stream, true), "nvfp4_grouped_gemm launch");
 }
 
+size_t nvfp4_grouped_packed_size(int64_t N, int64_t K, int32_t E, size_t* sf_bytes) {
+  if (N <= 0 || K <= 0 || E <= 0 || K % 512 || K > (int64_t(1) << 22) || N > (1ll << 30) || E > 65535) {
+    if (sf_bytes) *sf_bytes = 0;
+    return 0;
+  }
+  return nvfp4::packed_b_bytes(N, K, E, sf_bytes);
+}
+
+namespace {
+nvfp4_status check_packed_shape(int64_t N, int64_t K, int32_t E) {
+  if (N < 0 || E < 0) return fail(NVFP4_ERR_SHAPE, "N = %lld, E = %d must be >= 0", (long long)N, E);
+  nvfp4_status s = check_k(K);
+  if (s != NVFP4_OK) return s;
+  if (K % 512) return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: packed weights need K %% 512 == 0", (long long)K);
+  if (N > (1ll << 30) || E > 65535) return fail(NVFP4_ERR_UNSUPPORTED, "N above 2^30 or E > 65535 not supported");
+  return NVFP4_OK;
+}
+}  // namespace
+
+nvfp4_status nvfp4_grouped_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64_t K, int32_t E,
+                                  uint8_t* packed, uint8_t* packed_sf, void* stream) {
+  nvfp4_status s = check_packed_shape(N, K, E);
+  if (s != NVFP4_OK) return s;
+  if (N == 0 || E == 0) return ok();
+  if (!b || !b_sf || !packed || !packed_sf) return fail(NVFP4_ERR_NULL, "b, b_sf, packed and packed_sf must be non-NULL");
+  if (!aligned(b, 16) || !aligned(b_sf, 16) || !aligned(packed, 16) || !aligned(packed_sf, 16))
+    return fail(NVFP4_ERR_ALIGN, "b, b_sf, packed and packed_sf must be 16-byte aligned");
+  return hip_status(nvfp4::launch_pack_b(b, b_sf, N, K, E, packed, packed_sf, (hipStream_t)stream),
+                    "nvfp4_grouped_pack_b launch");
+}
+
+nvfp4_status nvfp4_grouped_gemm_packed(const uint8_t* a, const uint8_t* a_sf, const uint8_t* packed,
+                                       const uint8_t* packed_sf, const int32_t* offsets, const float* alpha,
+                                       uint16_t* d, int64_t rows, int64_t N, int64_t K, int32_t E, int32_t* status,
+                                       void* stream) {
+  if (rows < 0) return fail(NVFP4_ERR_SHAPE, "rows = %lld must be >= 0", (long long)rows);
+  nvfp4_status s = check_packed_shape(N, K, E);
+  if (s != NVFP4_OK) return s;
+  if (!offsets && E > 0) return fail(NVFP4_ERR_NULL, "offsets must be non-NULL");
+  if (!aligned(offsets, 4) || !aligned(status, 4))
+    return fail(NVFP4_ERR_ALIGN, "offsets and status must be 4-byte aligned");
+  if (E == 0 || N == 0 || rows == 0) {
+    nvfp4::GroupedLaunch p{a, a_sf, packed, packed_sf, offsets, alpha, d, rows, N, K, E};
+    return hip_status(nvfp4::launch_grouped_packed(p, status, (hipStream_t)stream, false),
+                      "nvfp4_grouped_gemm_packed status");
+  }
+  if (!a || !a_sf || !packed || !packed_sf || !d)
+    return fail(NVFP4_ERR_NULL, "a, a_sf, packed, packed_sf and d must be non-NULL (alpha and status may be NULL)");
+  if (!aligned(a, 16) || !aligned(packed, 16) || !aligned(a_sf, 16) || !aligned(packed_sf, 16))
+    return fail(NVFP4_ERR_ALIGN, "a, packed, a_sf and packed_sf must be 16-byte aligned");
+  if (!aligned(d, 4) || !aligned(alpha, 4)) return fail(NVFP4_ERR_ALIGN, "d and alpha must be 4-byte aligned");
+  if (rows > (1ll << 30)) return fail(NVFP4_ERR_UNSUPPORTED, "rows above 2^30 are not supported");
+  nvfp4::GroupedLaunch p{a, a_sf, packed, packed_sf, offsets, alpha, d, rows, N, K, E};
+  return hip_status(nvfp4::launch_grouped_packed(p, status, (hipStream_t)stream, true),
+                    "nvfp4_grouped_gemm_packed launch");
+}
+
 nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K, const float* global_scale, uint8_t* q,
                             uint8_t* sf, void* stream) {
   if (R < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "R = %lld, K = %lld must be >= 0", (long long)R, (long long)K);

@@ -866,15 +866,16 @@ struct GRegs {
 template <class C, int D>
 __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const rsrc_t& rb, const rsrc_t& rbs,
                                         const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
-                                        const rsrc_t& ra, const rsrc_t& ras, uint32_t va, uint32_t vas) {
+                                        uint32_t b_step, uint32_t bs_step, const rsrc_t& ra, const rsrc_t& ras,
+                                        uint32_t va, uint32_t vas) {
   constexpr uint32_t kOut = 0x80000000u;
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
       R.bq[u][tn][s] = __builtin_bit_cast(
-          u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn][s] : kOut, kt * C::RB, 0));
-      R.bs[u][tn][s] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][s] : kOut, kt * C::SB, 0);
+          u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn][s] : kOut, kt * b_step, 0));
+      R.bs[u][tn][s] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][s] : kOut, kt * bs_step, 0);
     }
   typedef typename GRegs<C, D>::AQ AQ;
   if constexpr (GRegs<C, D>::kAP == 1)
@@ -886,7 +887,9 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
   R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * C::SB, 0);
 }
 
-template <class C, int D>
+// PACKED: B (codes and scales) in the stage-contiguous layout written by
+// k_pack_b (each stage of a 256-row slab is one block; rows past N are zero).
+template <class C, int D, bool PACKED>
 __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p) {
   static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
   static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
@@ -901,9 +904,30 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p)
   const int64_t ld = p.K / 2, lds = p.K / 16;
   const float alpha = p.alpha ? p.alpha[e] : 1.0f;
   const int b_rows = (int)min<int64_t>(C::BN, p.N - n0);
-  const uint8_t* bt = p.b + ((int64_t)e * p.N + n0) * ld;
-  const uint8_t* bst = p.b_sf + ((int64_t)e * p.N + n0) * lds;
-  const rsrc_t rb = make_rsrc(bt, (uint32_t)(b_rows * ld)), rbs = make_rsrc(bst, (uint32_t)(b_rows * lds));
+  const int n = (int)(p.K / C::BK);
+  const uint8_t *bt, *bst;
+  uint32_t b_bytes, bs_bytes, b_step, bs_step, b_ld, bs_ld;
+  if constexpr (PACKED) {
+    const int64_t slab = (int64_t)e * tiles_n + L % tiles_n;
+    b_step = C::BN * C::RB;
+    bs_step = C::BN * C::SB;
+    bt = p.b + slab * n * b_step;
+    bst = p.b_sf + slab * n * bs_step;
+    b_bytes = (uint32_t)(n * b_step);
+    bs_bytes = (uint32_t)(n * bs_step);
+    b_ld = C::RB;
+    bs_ld = C::SB;
+  } else {
+    b_step = C::RB;
+    bs_step = C::SB;
+    bt = p.b + ((int64_t)e * p.N + n0) * ld;
+    bst = p.b_sf + ((int64_t)e * p.N + n0) * lds;
+    b_bytes = (uint32_t)(b_rows * ld);
+    bs_bytes = (uint32_t)(b_rows * lds);
+    b_ld = (uint32_t)ld;
+    bs_ld = (uint32_t)lds;
+  }
+  const rsrc_t rb = make_rsrc(bt, b_bytes), rbs = make_rsrc(bst, bs_bytes);
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wn = wave % C::WN, r_in = lane % C::MF, g = lane / C::MF;
   // per-lane B offsets (row part included; rows >= b_rows masked out of range)
@@ -914,11 +938,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p)
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
       const int c = C::KG * s + g;
-      vb[tn][s] = row < b_rows ? (uint32_t)(row * ld + c * 16) : 0x80000000u;
-      vbs[tn][s] = row < b_rows ? (uint32_t)(row * lds + 4 * (c >> 1)) : 0x80000000u;
+      vb[tn][s] = row < b_rows ? (uint32_t)(row * b_ld + c * 16) : 0x80000000u;
+      vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * (c >> 1)) : 0x80000000u;
     }
   }
-  const int n = (int)(p.K / C::BK);
   typedef GRegs<C, D> RT;
   // this thread's part (ah of kAP) of A code chunk ac of row ar
   const int q = threadIdx.x / RT::kAP, ah = threadIdx.x % RT::kAP, ar = q / C::CH, ac = q % C::CH;
@@ -938,7 +961,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p)
     __syncthreads();  // the previous row chunk is done with both A tiles
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      gr_load<C, D>(R, u, u, true, rb, rbs, vb, vbs, ra, ras, va, vas);
+      gr_load<C, D>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
     for (int i0 = 0; i0 < n; i0 += D) {
@@ -984,7 +1007,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p)
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
           __builtin_amdgcn_sched_barrier(0);
-          gr_load<C, D>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, ra, ras, va, vas);
+          gr_load<C, D>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
         }
       }
     }
@@ -1148,13 +1171,74 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
                        p);
   } else if (gk == 2) {
     const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
-    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2>), dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedReg::kThreads),
+    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, false>), dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedReg::kThreads),
                        0, stream, p);
   } else {
     const unsigned tiles_n = (unsigned)((p.N + CfgGroupedA16::BN - 1) / CfgGroupedA16::BN);
     hipLaunchKernelGGL(k_grouped_a16<CfgGroupedA16>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedA16::kThreads),
                        0, stream, p);
   }
+  return hipGetLastError();
+}
+
+// Weight pre-pack for the grouped GEMM: [E][N][K/2] codes and [E][N][K/16]
+// scales -> per (expert, 256-row slab, 256-element K stage) one contiguous
+// block of 256 rows x 128 code bytes (and 256 x 16 scale bytes), rows past N
+// zero.  One 16-byte chunk per thread and step.
+constexpr int kPackRows = CfgGroupedReg::BN, kPackK = CfgGroupedReg::BK;
+
+__global__ __launch_bounds__(256) void k_pack_b(const u4_t* __restrict__ b, const u4_t* __restrict__ b_sf, int64_t N,
+                                                int64_t K, int32_t E, u4_t* __restrict__ pb,
+                                                u4_t* __restrict__ psf) {
+  const int64_t tiles = (N + kPackRows - 1) / kPackRows, nst = K / kPackK;
+  const int64_t code_chunks = (int64_t)E * tiles * nst * kPackRows * 8;  // 8 x 16 B per row and stage
+  const int64_t sf_chunks = (int64_t)E * tiles * nst * kPackRows;       // 16 B per row and stage
+  const int64_t ld16 = K / 32, lds16 = K / 256;                          // 16-byte chunks per row
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < code_chunks + sf_chunks; q += stride) {
+    const bool code = q < code_chunks;
+    const int64_t qq = code ? q : q - code_chunks;
+    const int c = code ? (int)(qq % 8) : 0;
+    const int64_t blk = code ? qq / 8 : qq;          // (slab, stage, row)
+    const int r = (int)(blk % kPackRows);
+    const int64_t kst = (blk / kPackRows) % nst, slab = blk / kPackRows / nst;
+    const int64_t e = slab / tiles, row = (slab % tiles) * kPackRows + r;
+    u4_t v = {0u, 0u, 0u, 0u};
+    if (row < N) v = code ? b[(e * N + row) * ld16 + kst * 8 + c] : b_sf[(e * N + row) * lds16 + kst];
+    if (code) pb[qq] = v;
+    else psf[qq] = v;
+  }
+}
+
+size_t packed_b_bytes(int64_t N, int64_t K, int32_t E, size_t* sf_bytes) {
+  const int64_t tiles = (N + kPackRows - 1) / kPackRows;
+  if (sf_bytes) *sf_bytes = (size_t)E * tiles * kPackRows * (K / 16);
+  return (size_t)E * tiles * kPackRows * (K / 2);
+}
+
+hipError_t launch_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64_t K, int32_t E, uint8_t* pb,
+                         uint8_t* psf, hipStream_t stream) {
+  size_t sfb = 0;
+  const size_t cb = packed_b_bytes(N, K, E, &sfb);
+  const int64_t chunks = (int64_t)((cb + sfb) / 16);
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_b, dim3((unsigned)blocks), dim3(256), 0, stream, (const u4_t*)b, (const u4_t*)b_sf, N, K,
+                     E, (u4_t*)pb, (u4_t*)psf);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_packed(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute) {
+  if (status) {
+    hipLaunchKernelGGL(k_check_offsets, dim3(1), dim3(64), 0, stream, p.offsets, p.E, p.rows, status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (!compute) return hipSuccess;
+  const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
+  hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, true>), dim3(tiles_n * (unsigned)p.E),
+                     dim3(CfgGroupedReg::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -44,6 +44,11 @@ struct GemmPlan {
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
 hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
+// Grouped GEMM on weights pre-packed by launch_pack_b (K % 512 == 0).
+hipError_t launch_grouped_packed(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
+size_t packed_b_bytes(int64_t N, int64_t K, int32_t E, size_t* sf_bytes);
+hipError_t launch_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64_t K, int32_t E, uint8_t* pb,
+                         uint8_t* psf, hipStream_t stream);
 size_t grouped_workspace(int64_t rows, int64_t N, int64_t K, int32_t E);
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);
 

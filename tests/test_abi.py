@@ -101,3 +101,25 @@ def test_plan_and_workspace_queries():
     ws = nv.nvfp4_gemm_workspace_size(16, 768, 6144)
     tiles = 768 // 64
     assert ws > 4096 and (ws - 4096) % (tiles * 16 * 64 * 4) == 0
+
+
+def test_packed_grouped_error_paths():
+    L = nv.lib()
+    # sizes: codes and scales of E experts padded to 256-row slabs; K % 512 required
+    assert nv.nvfp4_grouped_packed_size(2048, 6144, 256) == (256 * 2048 * 3072, 256 * 2048 * 384)
+    assert nv.nvfp4_grouped_packed_size(330, 1024, 8) == (8 * 512 * 512, 8 * 512 * 64)
+    assert nv.nvfp4_grouped_packed_size(330, 768, 8) == (0, 0)
+    pack = lambda **k: L.nvfp4_grouped_pack_b(k.get("b", FAKE), FAKE, k.get("N", 64), k.get("K", 512), k.get("E", 2),
+                                              k.get("p", FAKE), FAKE, None)
+    assert pack(K=768) == 4 and "512" in nv.nvfp4_last_error()
+    assert pack(K=40) == 2
+    assert pack(N=-1) == 2
+    assert pack(b=None) == 1
+    assert pack(p=FAKE + 8) == 3
+    assert pack(E=0, b=None) == 0
+    gemm = lambda **k: L.nvfp4_grouped_gemm_packed(FAKE, FAKE, FAKE, FAKE, k.get("off", FAKE), None, k.get("d", FAKE),
+                                                   k.get("rows", 64), 64, k.get("K", 512), 4, None, None)
+    assert gemm(K=256) == 4
+    assert gemm(off=None) == 1
+    assert gemm(d=None) == 1
+    assert gemm(rows=-1) == 2

@@ -137,3 +137,61 @@ def test_every_grouped_kernel(gplan, K, monkeypatch):
         if hi > lo:
             check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], alpha[e], f"gplan {gplan} expert {e}")
     assert (db[250:] == SENTINEL).all()
+
+
+def _np_pack(b, bsf, N, K, E):
+    """Reference of the packed weight layout (numpy rearrangement)."""
+    T, n = -(-N // 256), K // 256
+    bp = np.zeros((E, T * 256, K // 2), np.uint8)
+    bp[:, :N] = b
+    sp = np.zeros((E, T * 256, K // 16), np.uint8)
+    sp[:, :N] = bsf
+    pb = bp.reshape(E, T, 256, n, 128).transpose(0, 1, 3, 2, 4).reshape(-1)
+    psf = sp.reshape(E, T, 256, n, 16).transpose(0, 1, 3, 2, 4).reshape(-1)
+    return pb, psf
+
+
+@pytest.mark.parametrize("kind", ["alternate", [0, 0, 5, 5, 70, 70, 71, 200, 250]])
+def test_packed_weights_layout_and_gemm(kind):
+    rows, E, N, K = 300, 8, 330, 1024
+    off, a, asf, b, bsf, alpha = _small_problem(kind, rows, E, N, K, seed=60)
+    say("grouped packed", kind)
+    b_t, bsf_t = dev(b), dev(bsf)
+    pb, psf = nv.grouped_pack(b_t, bsf_t, N, K, E)
+    want_pb, want_psf = _np_pack(b, bsf, N, K, E)
+    np.testing.assert_array_equal(host(pb), want_pb)
+    np.testing.assert_array_equal(host(psf), want_psf)
+    d = torch.full((rows, N), SENTINEL, dtype=torch.int16, device="cuda")
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    nv.nvfp4_grouped_gemm_packed(dev(a), dev(asf), pb, psf, dev(off), dev(alpha), d, rows, N, K, E, st)
+    assert int(host(st)[0]) == 0
+    db = bits(d)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], alpha[e], f"packed {kind} expert {e}")
+    assert (db[int(off[-1]):] == SENTINEL).all()
+    # same bits as the unpacked grouped kernel (same arithmetic, same order)
+    d2, _ = _grouped(dev(a), dev(asf), b_t, bsf_t, dev(off), dev(alpha), rows, N, K, E)
+    np.testing.assert_array_equal(bits(d2), db)
+
+
+def test_packed_moe_workload_sampled_experts():
+    g = synth.GROUPED
+    T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
+    tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
+    rows = int(off[-1])
+    say("packed moe")
+    a = synth.random_codes(71, rows, K)
+    asf = synth.random_scale_bytes(72, rows, K, lo=0x30, hi=0x40)
+    b = synth.random_codes(g["seed_expert_base"], E * N, K).reshape(E, N, K // 2)
+    bsf = synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, lo=0x20, hi=0x38).reshape(E, N, K // 16)
+    pb, psf = nv.grouped_pack(dev(b), dev(bsf), N, K, E)
+    d = torch.full((rows, N), SENTINEL, dtype=torch.int16, device="cuda")
+    nv.nvfp4_grouped_gemm_packed(dev(a), dev(asf), pb, psf, dev(off), None, d, rows, N, K, E)
+    db = bits(d)
+    for e in (0, 17, 128, 255, int(np.argmax(np.diff(off)))):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], np.float32(1), f"packed moe expert {e}")
+    assert not (db == SENTINEL).any()
