@@ -938,7 +938,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p)
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
       const int c = C::KG * s + g;
-      vb[tn][s] = row < b_rows ? (uint32_t)(row * b_ld + c * 16) : 0x80000000u;
+      uint32_t off = (uint32_t)(row * b_ld + c * 16);
+      if constexpr (PACKED) off = (uint32_t)(((wn * C::TN + tn) * C::kSub + s) * 64 + lane) * 16;  // lane order
+      vb[tn][s] = row < b_rows ? off : 0x80000000u;
       vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * (c >> 1)) : 0x80000000u;
     }
   }
@@ -1184,8 +1186,17 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
 // Weight pre-pack for the grouped GEMM: [E][N][K/2] codes and [E][N][K/16]
 // scales -> per (expert, 256-row slab, 256-element K stage) one contiguous
 // block of 256 rows x 128 code bytes (and 256 x 16 scale bytes), rows past N
-// zero.  One 16-byte chunk per thread and step.
+// zero.  Inside a code block the 16-byte chunks are in the order the grouped
+// kernel's lanes load them (wave, column block, sub-step, lane), so each load
+// instruction reads 1 KB in one run; scale rows stay in row order.  One
+// 16-byte chunk per thread and step.
 constexpr int kPackRows = CfgGroupedReg::BN, kPackK = CfgGroupedReg::BK;
+
+// position of chunk c (0..7) of row r (0..255) inside a packed code block
+__host__ __device__ constexpr int packed_chunk(int r, int c) {
+  typedef CfgGroupedReg G;
+  return (((r / G::kWN) * G::TN + (r % G::kWN) / G::MF) * G::kSub + c / G::KG) * 64 + (c % G::KG) * G::MF + r % G::MF;
+}
 
 __global__ __launch_bounds__(256) void k_pack_b(const u4_t* __restrict__ b, const u4_t* __restrict__ b_sf, int64_t N,
                                                 int64_t K, int32_t E, u4_t* __restrict__ pb,
@@ -1195,17 +1206,20 @@ __global__ __launch_bounds__(256) void k_pack_b(const u4_t* __restrict__ b, cons
   const int64_t sf_chunks = (int64_t)E * tiles * nst * kPackRows;       // 16 B per row and stage
   const int64_t ld16 = K / 32, lds16 = K / 256;                          // 16-byte chunks per row
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // q enumerates source chunks: code chunk c of row r of (slab, stage), then
+  // the scale chunks
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < code_chunks + sf_chunks; q += stride) {
     const bool code = q < code_chunks;
     const int64_t qq = code ? q : q - code_chunks;
     const int c = code ? (int)(qq % 8) : 0;
     const int64_t blk = code ? qq / 8 : qq;          // (slab, stage, row)
     const int r = (int)(blk % kPackRows);
-    const int64_t kst = (blk / kPackRows) % nst, slab = blk / kPackRows / nst;
+    const int64_t block = blk / kPackRows;           // slab * nst + stage
+    const int64_t kst = block % nst, slab = block / nst;
     const int64_t e = slab / tiles, row = (slab % tiles) * kPackRows + r;
     u4_t v = {0u, 0u, 0u, 0u};
     if (row < N) v = code ? b[(e * N + row) * ld16 + kst * 8 + c] : b_sf[(e * N + row) * lds16 + kst];
-    if (code) pb[qq] = v;
+    if (code) pb[block * (kPackRows * 8) + packed_chunk(r, c)] = v;
     else psf[qq] = v;
   }
 }

@@ -146,7 +146,14 @@ def _np_pack(b, bsf, N, K, E):
     bp[:, :N] = b
     sp = np.zeros((E, T * 256, K // 16), np.uint8)
     sp[:, :N] = bsf
-    pb = bp.reshape(E, T, 256, n, 128).transpose(0, 1, 3, 2, 4).reshape(-1)
+    blocks = bp.reshape(E, T, 256, n, 8, 16).transpose(0, 1, 3, 2, 4, 5)  # [E][T][n][row][chunk][16 B]
+    # inside a block, 16-byte chunk c of row r goes to position
+    # (((r // 32) * 2 + (r % 32) // 16) * 2 + c // 4) * 64 + (c % 4) * 16 + r % 16
+    r, c = np.meshgrid(np.arange(256), np.arange(8), indexing="ij")
+    pos = (((r // 32) * 2 + (r % 32) // 16) * 2 + c // 4) * 64 + (c % 4) * 16 + r % 16
+    out = np.zeros((E, T, n, 2048, 16), np.uint8)
+    out[:, :, :, pos.reshape(-1), :] = blocks.reshape(E, T, n, 2048, 16)
+    pb = out.reshape(-1)
     psf = sp.reshape(E, T, 256, n, 16).transpose(0, 1, 3, 2, 4).reshape(-1)
     return pb, psf
 
