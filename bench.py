@@ -51,17 +51,23 @@ def main():
     ap.add_argument("--profile-call", type=int, default=0, metavar="M",
                     help="for hardware-counter runs: one 256 MiB device copy (counter calibration), then 8 "
                          "cold calls of the headline GEMM at this M; prints nothing else")
+    ap.add_argument("--profile-grouped", action="store_true",
+                    help="for profiler runs: one 256 MiB device copy (counter calibration), then the grouped "
+                         "MoE GEMM on packed weights (graph of 10 calls, replayed 4 times); prints its time")
     ap.add_argument("--graph", action="store_true",
                     help="with --profile-call: time the call as the headline does (graphs of 64 calls over "
                          "the rotating sets, replayed 8 times) instead of 8 eager calls")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter CSVs of a --profile-call run (FETCH_SIZE, "
-                         "WRITE_SIZE) into the HBM traffic record read by the roofline (no GPU needed)")
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --profile-call or "
+                         "--profile-grouped run into the HBM traffic record the bench reads (no GPU needed)")
+    ap.add_argument("--requests", metavar="REQ_CSV",
+                    help="with --traffic: a third counter CSV of the same run with TCC_EA0_RDREQ_32B_sum, "
+                         "TCC_EA0_RDREQ_64B_sum, TCC_EA0_RDREQ_128B_sum, as a cross-check of the copy scaling")
     args = ap.parse_args()
     if args.traffic:
-        if not args.profile_call:
-            raise SystemExit("--traffic needs the --profile-call M the counters were taken with")
-        write_traffic_record(*args.traffic, m=args.profile_call)
+        if not args.profile_call and not args.profile_grouped:
+            raise SystemExit("--traffic needs the --profile-call M or --profile-grouped the counters were taken with")
+        write_traffic_record(*args.traffic, args.requests, "grouped" if args.profile_grouped else args.profile_call)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
@@ -110,6 +116,9 @@ def main():
 
     if args.profile_call:
         profile_call(torch, nv, sweep_inputs, call, args.profile_call, args.graph)
+        return
+    if args.profile_grouped:
+        profile_grouped(torch, nv, synth, quantise, stream)
         return
 
     # ---------------- headline: attention-projection sweep -----------------
@@ -171,7 +180,7 @@ def main():
     by = algo_bytes(dom["M"], N, K)
     mfma_bound = fl / by > PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
     call_name = f"nvfp4_gemm M={dom['M']} N={N} K={K}"
-    traffic = read_traffic_record(call_name, dom["plan"])
+    traffic = read_traffic_record(TRAFFIC_RECORD, f"{call_name} ({dom['plan']})")
     if mfma_bound:
         roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_F16_TFLOPS, unit="TFLOP/s",
                         frac=round(dom["tflops"] / PEAK_F16_TFLOPS, 4), traffic=traffic,
@@ -202,6 +211,7 @@ def main():
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_headline_dominant_call.json")
+GROUPED_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_grouped_moe_packed.json")
 COPY_BYTES = 256 << 20
 
 
@@ -218,17 +228,23 @@ def kernel_sources_digest():
     return h.hexdigest()[:16]
 
 
-def profile_call(torch, nv, sweep_inputs, call, m, graph=False):
-    """Workload of the profiler runs: a plain 256 MiB copy (its FETCH_SIZE and
-    WRITE_SIZE calibrate the counters), then 8 cold calls of one headline GEMM,
-    or (graph=True) the per-call timing of the headline: a graph of 64 calls
-    over the rotating sets, replayed 8 times, with its HIP-event time printed."""
+def calibration_copy(torch):
+    """A plain device copy of COPY_BYTES: it must fetch and write exactly
+    COPY_BYTES, which calibrates the traffic counters."""
     x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     y = torch.empty_like(x)
     torch.cuda.synchronize()
     y.copy_(x)
     torch.cuda.synchronize()
     del x, y
+
+
+def profile_call(torch, nv, sweep_inputs, call, m, graph=False):
+    """Workload of the profiler runs: a plain 256 MiB copy (its FETCH_SIZE and
+    WRITE_SIZE calibrate the counters), then 8 cold calls of one headline GEMM,
+    or (graph=True) the per-call timing of the headline: a graph of 64 calls
+    over the rotating sets, replayed 8 times, with its HIP-event time printed."""
+    calibration_copy(torch)
     name = "attn_proj_n768_k6144"
     w, sets, alpha, outs, wss = sweep_inputs(name)
     if m not in outs:
@@ -245,6 +261,48 @@ def profile_call(torch, nv, sweep_inputs, call, m, graph=False):
     torch.cuda.synchronize()
 
 
+def grouped_inputs(torch, nv, synth, quantise, dev):
+    """The grouped MoE workload: 512 tokens routed top-8 over 256 experts,
+    activations quantised on the GPU and gathered per expert, random expert
+    codes and scales, per-expert alpha."""
+    g = synth.GROUPED
+    T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
+    tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
+    rows = int(off[-1])
+    qa_tok, sfa_tok, gsa = quantise(synth.token_activations(T, K))
+    tok_t = torch.from_numpy(tok).to(dev)
+    qa, sfa = qa_tok[tok_t].contiguous(), sfa_tok[tok_t].contiguous()
+    b = torch.from_numpy(synth.random_codes(g["seed_expert_base"], E * N, K)).to(dev)
+    bsf = torch.from_numpy(synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, 0x20, 0x38)).to(dev)
+    active = int((np.diff(off) > 0).sum())
+    return dict(rows=rows, N=N, K=K, E=E, qa=qa, sfa=sfa, b=b, bsf=bsf, off=torch.from_numpy(off).to(dev),
+                alpha=torch.full((E,), 1.0, dtype=torch.float32, device=dev) / gsa,
+                d=torch.empty((rows, N), dtype=torch.int16, device=dev), active=active,
+                rows_per_expert_max=int(np.diff(off).max()),
+                # expert weights of the active experts, activations, bf16 out, offsets, alphas
+                bytes=active * N * K * 9 // 16 + rows * K * 9 // 16 + 2 * rows * N + 4 * (E + 1) + 4 * E,
+                flops=2.0 * rows * N * K)
+
+
+def grouped_call_name(rows, N, K, E):
+    return f"nvfp4_grouped_gemm_packed rows={rows} N={N} K={K} E={E}"
+
+
+def profile_grouped(torch, nv, synth, quantise, stream):
+    """Workload of the grouped profiler runs: the 256 MiB calibration copy,
+    then the grouped MoE GEMM on packed expert weights, timed as the bench
+    times it (a graph of 10 calls); prints the call and its time."""
+    calibration_copy(torch)
+    gi = grouped_inputs(torch, nv, synth, quantise, torch.device("cuda"))
+    rows, N, K, E = gi["rows"], gi["N"], gi["K"], gi["E"]
+    pb, psf = nv.grouped_pack(gi["b"], gi["bsf"], N, K, E)
+    del gi["b"], gi["bsf"]
+    us = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_packed(gi["qa"], gi["sfa"], pb, psf, gi["off"],
+                                                                      gi["alpha"], gi["d"], rows, N, K, E), 10)
+    print(json.dumps({"call": grouped_call_name(rows, N, K, E), "us_per_call": round(us, 2),
+                      "algorithmic_bytes": gi["bytes"], "gbps": round(gi["bytes"] / us / 1e3, 1)}))
+
+
 def _counter_rows(path, counter):
     import csv
     rows = []
@@ -254,42 +312,74 @@ def _counter_rows(path, counter):
     return rows
 
 
-def write_traffic_record(fetch_csv, write_csv, m):
+def _is_copy(name):
+    return "copybuffer" in name.lower()
+
+
+def write_traffic_record(fetch_csv, write_csv, requests_csv, target):
     """FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by
     what the same counter reads for the plain copy of COPY_BYTES (which must
-    fetch and write exactly COPY_BYTES), then averaged over the GEMM dispatches."""
+    fetch and write exactly COPY_BYTES), then averaged over the dispatches of
+    the profiled kernel.  With a third CSV of read requests by size
+    (TCC_EA0_RDREQ_{32B,64B,128B}_sum), the fetched bytes are also summed
+    request by request, for the copy and for the kernel, as a cross-check of
+    the copy scaling (which assumes the kernel's request sizes match the copy's)."""
+    import nvfp4_block_scaled_07_amd as nv
+    import synth
+    if target == "grouped":
+        g = synth.GROUPED
+        _, off = synth.routing(g["seed_router"], g["tokens"], g["experts"], g["top_k"])
+        call = grouped_call_name(int(off[-1]), g["n"], g["k"], g["experts"])
+        match, path_out = "k_grouped", GROUPED_TRAFFIC_RECORD
+    else:
+        w = synth.WORKLOADS["attn_proj_n768_k6144"]
+        call = f"nvfp4_gemm M={target} N={w['n']} K={w['k']} ({nv.nvfp4_gemm_plan(target, w['n'], w['k'])})"
+        match, path_out = "k_gemm", TRAFFIC_RECORD
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, counter)
-        copies = [v for n, g, v in rows if "copy" in n.lower() or "elementwise" in n.lower()]
-        gemm = [(n, g, v) for n, g, v in rows if "k_gemm" in n]
-        if not copies or not gemm:
-            raise SystemExit(f"{path}: no copy or no GEMM dispatch with {counter}")
+        copies = [v for n, g_, v in rows if _is_copy(n)]
+        kern = [(n, g_, v) for n, g_, v in rows if match in n]
+        if not copies or not kern:
+            raise SystemExit(f"{path}: no copy or no {match} dispatch with {counter}")
         calib = max(copies) * 1024.0 / COPY_BYTES
         out[counter] = dict(copy_kib=max(copies), factor=round(1.0 / calib, 6),
-                            gemm_kib_mean=sum(v for _, _, v in gemm) / len(gemm),
-                            bytes_per_launch=sum(v for _, _, v in gemm) / len(gemm) * 1024.0 / calib,
-                            dispatches=len(gemm), kernel=gemm[0][0][:160], grid=gemm[0][1])
-    rec = dict(sources_sha256_16=kernel_sources_digest(), copy_bytes=COPY_BYTES, counters=out,
+                            kernel_kib_mean=sum(v for _, _, v in kern) / len(kern),
+                            bytes_per_launch=sum(v for _, _, v in kern) / len(kern) * 1024.0 / calib,
+                            dispatches=len(kern), kernel=kern[0][0][:160], grid=kern[0][1])
+    rec = dict(sources_sha256_16=kernel_sources_digest(), call=call, copy_bytes=COPY_BYTES, counters=out,
                traffic_bytes_per_launch=round(out["FETCH_SIZE"]["bytes_per_launch"] +
                                               out["WRITE_SIZE"]["bytes_per_launch"]))
-    import nvfp4_block_scaled_07_amd as nv
-    import synth
-    w = synth.WORKLOADS["attn_proj_n768_k6144"]
-    rec["call"] = f"nvfp4_gemm M={m} N={w['n']} K={w['k']} ({nv.nvfp4_gemm_plan(m, w['n'], w['k'])})"
-    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
-    json.dump(rec, open(TRAFFIC_RECORD, "w"), indent=1)
+    if requests_csv:
+        import csv
+        per = {}
+        for r in csv.DictReader(open(requests_csv)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+
+        def read_bytes(c):
+            return (32 * c.get("TCC_EA0_RDREQ_32B_sum", 0) + 64 * c.get("TCC_EA0_RDREQ_64B_sum", 0) +
+                    128 * c.get("TCC_EA0_RDREQ_128B_sum", 0))
+        copy = max((read_bytes(c), c) for (i, n), c in per.items() if _is_copy(n))
+        kern = [c for (i, n), c in per.items() if match in n]
+        rec["read_requests"] = dict(
+            copy_read_bytes=copy[0], copy_requests=copy[1],
+            kernel_read_bytes_mean=sum(read_bytes(c) for c in kern) / len(kern),
+            kernel_requests_mean={k: sum(c.get(k, 0) for c in kern) / len(kern) for k in sorted(kern[0])},
+            dispatches=len(kern))
+    os.makedirs(os.path.dirname(path_out), exist_ok=True)
+    json.dump(rec, open(path_out, "w"), indent=1)
     print(json.dumps(rec))
 
 
-def read_traffic_record(call_name, plan):
-    """HBM bytes per launch of the dominant call from the committed counter
-    record, or None when it was taken for another call or other kernels."""
+def read_traffic_record(path, call):
+    """HBM bytes per launch of `call` from a committed counter record, or None
+    when the record was taken for another call or for other kernel sources."""
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256_16") != kernel_sources_digest() or rec.get("call") != f"{call_name} ({plan})":
+    if rec.get("sources_sha256_16") != kernel_sources_digest() or rec.get("call") != call:
         return None
     return rec["traffic_bytes_per_launch"]
 
@@ -351,42 +441,81 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
         torch.cuda.empty_cache()
 
     # grouped MoE: 512 tokens, top-8 of 256 experts, [rows_e, 6144] x [6144, 2048] per expert
-    g = synth.GROUPED
-    T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
-    tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
-    rows = int(off[-1])
-    qa_tok, sfa_tok, gsa = quantise(synth.token_activations(T, K))
-    tok_t = torch.from_numpy(tok).to(dev)
-    qa, sfa = qa_tok[tok_t].contiguous(), sfa_tok[tok_t].contiguous()
-    b = torch.from_numpy(synth.random_codes(g["seed_expert_base"], E * N, K)).to(dev)
-    bsf = torch.from_numpy(synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, 0x20, 0x38)).to(dev)
-    off_t = torch.from_numpy(off).to(dev)
-    alpha = torch.full((E,), 1.0, dtype=torch.float32, device=dev) / gsa
-    d = torch.empty((rows, N), dtype=torch.int16, device=dev)
+    gi = grouped_inputs(torch, nv, synth, quantise, dev)
+    rows, N, K, E = gi["rows"], gi["N"], gi["K"], gi["E"]
+    qa, sfa, b, bsf, off_t, alpha, d = (gi[k] for k in ("qa", "sfa", "b", "bsf", "off", "alpha", "d"))
     need = nv.nvfp4_grouped_workspace_size(rows, N, K, E)
     ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     us = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm(qa, sfa, b, bsf, off_t, alpha, d, rows, N, K, E, ws),
                10)
-    active = int((np.diff(off) > 0).sum())
-    by = active * N * K * 9 // 16 + rows * K * 9 // 16 + 2 * rows * N + 4 * (E + 1) + 4 * E
-    fl = 2.0 * rows * N * K
-    res["grouped_moe_512tok_256exp_top8"] = dict(rows=rows, active_experts=active, N=N, K=K, us=round(us, 2),
+    by, fl = gi["bytes"], gi["flops"]
+    res["grouped_moe_512tok_256exp_top8"] = dict(rows=rows, active_experts=gi["active"], N=N, K=K, us=round(us, 2),
                                                  gbps=round(by / us / 1e3, 1),
                                                  frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4),
                                                  tflops=round(fl / us / 1e6, 2),
-                                                 rows_per_expert_max=int(np.diff(off).max()))
+                                                 rows_per_expert_max=gi["rows_per_expert_max"],
+                                                 algorithmic_bytes=by)
     # the same call on weights packed once into the stage-contiguous layout
     # (packing is a one-time weight transform, outside the timed region)
     pb, psf = nv.grouped_pack(b, bsf, N, K, E)
-    del b, bsf
+    del b, bsf, gi
     torch.cuda.empty_cache()
     us_p = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_packed(qa, sfa, pb, psf, off_t, alpha, d, rows, N, K,
                                                                        E), 10)
     res["grouped_moe_512tok_256exp_top8"]["packed_weights"] = dict(
         us=round(us_p, 2), gbps=round(by / us_p / 1e3, 1), frac_hbm=round(by / us_p / 1e3 / PEAK_HBM_GBPS, 4),
-        tflops=round(fl / us_p / 1e6, 2))
+        tflops=round(fl / us_p / 1e6, 2),
+        traffic=read_traffic_record(GROUPED_TRAFFIC_RECORD, grouped_call_name(rows, N, K, E)))
     del pb, psf, qa, sfa, d
     torch.cuda.empty_cache()
+
+    # grouped calls with the same rows in every expert, weights >= 512 MB
+    uni = []
+    for u in synth.GROUPED_UNIFORM:
+        N, K, E, me = u["n"], u["k"], u["experts"], u["rows_per_expert"]
+        rows = E * me
+        off = synth.uniform_offsets(me, E)
+        qa = torch.from_numpy(synth.random_codes(u["seed"], rows, K)).to(dev)
+        sfa = torch.from_numpy(synth.random_scale_bytes(u["seed"] + 1, rows, K, 0x20, 0x38)).to(dev)
+        b = torch.from_numpy(synth.random_codes(u["seed"] + 2, E * N, K)).to(dev)
+        bsf = torch.from_numpy(synth.random_scale_bytes(u["seed"] + 3, E * N, K, 0x20, 0x38)).to(dev)
+        off_t = torch.from_numpy(off).to(dev)
+        d = torch.empty((rows, N), dtype=torch.int16, device=dev)
+        by = E * N * K * 9 // 16 + rows * K * 9 // 16 + 2 * rows * N + 4 * (E + 1)
+        fl = 2.0 * rows * N * K
+        need = nv.nvfp4_grouped_workspace_size(rows, N, K, E)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        us = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm(qa, sfa, b, bsf, off_t, None, d, rows, N, K, E, ws),
+                   10)
+        pb, psf = nv.grouped_pack(b, bsf, N, K, E)
+        del b, bsf
+        us_p = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_packed(qa, sfa, pb, psf, off_t, None, d, rows, N,
+                                                                           K, E), 10)
+        uni.append(dict(E=E, rows_per_expert=me, N=N, K=K, algorithmic_bytes=by,
+                        us=round(us, 2), frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4),
+                        packed_us=round(us_p, 2), packed_gbps=round(by / us_p / 1e3, 1),
+                        packed_frac_hbm=round(by / us_p / 1e3 / PEAK_HBM_GBPS, 4),
+                        packed_tflops=round(fl / us_p / 1e6, 2)))
+        del pb, psf, qa, sfa, d, ws
+        torch.cuda.empty_cache()
+    res["grouped_uniform_experts"] = dict(cache="cold (weights >= 512 MB)", shapes=uni)
+
+    # context: the vendor bf16 GEMM (torch.matmul -> hipBLASLt) on already
+    # dequantised operands at the same shapes, cold as above (the MI355X
+    # counterpart of the pages' FP4-vs-BF16 throughput comparison)
+    ref = []
+    for (m, n, k) in [(m, 768, 6144) for m in synth.WORKLOADS["attn_proj_n768_k6144"]["ms"]] + [(8192, 6144, 6144)]:
+        per = (m * k + k * n) * 2
+        nsets = max(1, min(64, (ROTATE_BYTES + per - 1) // per))
+        xa = [torch.randn(m, k, device=dev, dtype=torch.bfloat16) for _ in range(nsets)]
+        xb = [torch.randn(k, n, device=dev, dtype=torch.bfloat16) for _ in range(nsets)]  # [K][N], contiguous
+        reps = max(nsets, 8) if m <= 1024 else 4
+        us = timed(torch, stream, lambda i: torch.matmul(xa[i % nsets], xb[i % nsets]), reps)
+        ref.append(dict(M=m, N=n, K=k, us=round(us, 2), tflops=round(2.0 * m * n * k / us / 1e6, 1)))
+        del xa, xb
+        torch.cuda.empty_cache()
+    res["bf16_matmul_reference"] = dict(note="torch.matmul bf16 x bf16 -> bf16 (hipBLASLt), operands already "
+                                             "dequantised; context only", shapes=ref)
 
     # quantiser (prologue): 16384 x 6144 fp32 -> NVFP4
     x = torch.from_numpy(synth.normal_f32(4001, (16384, 6144))).to(dev)

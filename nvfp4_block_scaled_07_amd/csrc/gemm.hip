@@ -890,7 +890,8 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 // PACKED: B (codes and scales) in the stage-contiguous layout written by
 // k_pack_b (each stage of a 256-row slab is one block; rows past N are zero).
 template <class C, int D, bool PACKED>
-__global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p) {
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_grouped_reg(
+    GroupedLaunch p) {
   static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
   static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
   static_assert(C::BM * C::CH <= C::kThreads, "one A chunk per thread");
@@ -992,17 +993,32 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_reg(GroupedLaunch p)
             for (int tn = 0; tn < C::TN; ++tn) bsp[tn] = e4m3x2_to_h2(R.bs[u][tn][s] >> (16 * (c & 1)));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              h8_t a[C::TM];
+              if constexpr (C::TM <= 2) {
+                h8_t a[C::TM];
 #pragma unroll
-              for (int tm = 0; tm < C::TM; ++tm) {
-                const int row = tm * C::MF + r_in;
-                a[tm] = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
-              }
+                for (int tm = 0; tm < C::TM; ++tm) {
+                  const int row = tm * C::MF + r_in;
+                  a[tm] = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
+                }
 #pragma unroll
-              for (int tn = 0; tn < C::TN; ++tn) {
-                const h8_t bf = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
+                for (int tn = 0; tn < C::TN; ++tn) {
+                  const h8_t bf = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
 #pragma unroll
-                for (int tm = 0; tm < C::TM; ++tm) acc[tm][tn] = Mfma<C::MF>::run(a[tm], bf, acc[tm][tn]);
+                  for (int tm = 0; tm < C::TM; ++tm) acc[tm][tn] = Mfma<C::MF>::run(a[tm], bf, acc[tm][tn]);
+                }
+              } else {
+                // taller tiles: dequantise the B fragments first, then stream
+                // one A fragment at a time (fewer live registers)
+                h8_t bf[C::TN];
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn) bf[tn] = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
+#pragma unroll
+                for (int tm = 0; tm < C::TM; ++tm) {
+                  const int row = tm * C::MF + r_in;
+                  const h8_t a = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
+#pragma unroll
+                  for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<C::MF>::run(a, bf[tn], acc[tm][tn]);
+                }
               }
             }
           }
@@ -1034,6 +1050,7 @@ typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 ro
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass
 typedef Cfg<32, 256, 1, 8, 16, 256, 2> CfgGroupedReg;    // MoE experts, B streamed through registers
+typedef Cfg<64, 256, 1, 8, 16, 256, 2, 0, 1, 2> CfgGroupedReg64;  // the same with 64-row passes over each expert
 
 struct PlanKind {
   const char* name;
@@ -1152,6 +1169,10 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The host sees only the total row count: experts averaging more than 40
+// rows get 64-row passes.
+static bool tall_experts(const GroupedLaunch& p) { return p.rows > 40 * (int64_t)p.E; }
+
 hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute) {
   if (status) {
     hipLaunchKernelGGL(k_check_offsets, dim3(1), dim3(64), 0, stream, p.offsets, p.E, p.rows, status);
@@ -1159,14 +1180,17 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
     if (err != hipSuccess) return err;
   }
   if (!compute) return hipSuccess;
-  // Kernel choice, measured on the 256-expert top-8 workload (K = 6144):
-  // B streamed through registers (2 stages ahead, 4 waves per SIMD) when 2
-  // divides K / 256, else the shared-f16-A kernel.  NVFP4_GPLAN=<0|1|2>
-  // forces the per-wave-dequant, shared-f16-A or register kernel (tuning and
-  // tests only).
-  int gk = (p.K / 256) % 2 == 0 ? 2 : 1;
+  // Kernel choice, measured on the 256-expert top-8 workload and on uniform
+  // 16/32/64-row experts (K = 6144): B streamed through registers (2 stages
+  // ahead) when 2 divides K / 256, else the shared-f16-A kernel.  The
+  // register kernel takes 32-row passes over each expert (4 waves per SIMD);
+  // when the experts average more than 40 rows, 64-row passes (2 waves per
+  // SIMD, but every weight byte read once for up to 64 rows) are faster.
+  // NVFP4_GPLAN=<0|1|2|3> forces the per-wave-dequant, shared-f16-A,
+  // 32-row or 64-row register kernel (tuning and tests only).
+  int gk = (p.K / 256) % 2 == 0 ? (tall_experts(p) ? 3 : 2) : 1;
   if (const char* env = getenv("NVFP4_GPLAN")) gk = atoi(env);
-  if (gk == 2 && (p.K / 256) % 2) gk = 1;
+  if (gk >= 2 && (p.K / 256) % 2) gk = 1;
   if (gk == 0) {
     const unsigned tiles_n = (unsigned)((p.N + CfgGrouped::BN - 1) / CfgGrouped::BN);
     hipLaunchKernelGGL(k_grouped<CfgGrouped>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGrouped::kThreads), 0, stream,
@@ -1175,6 +1199,10 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
     const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
     hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, false>), dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedReg::kThreads),
                        0, stream, p);
+  } else if (gk == 3) {
+    const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg64::BN - 1) / CfgGroupedReg64::BN);
+    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false>), dim3(tiles_n * (unsigned)p.E),
+                       dim3(CfgGroupedReg64::kThreads), 0, stream, p);
   } else {
     const unsigned tiles_n = (unsigned)((p.N + CfgGroupedA16::BN - 1) / CfgGroupedA16::BN);
     hipLaunchKernelGGL(k_grouped_a16<CfgGroupedA16>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedA16::kThreads),
@@ -1250,9 +1278,19 @@ hipError_t launch_grouped_packed(GroupedLaunch p, int32_t* status, hipStream_t s
     if (err != hipSuccess) return err;
   }
   if (!compute) return hipSuccess;
+  static_assert(CfgGroupedReg64::BN == CfgGroupedReg::BN && CfgGroupedReg64::WN == CfgGroupedReg::WN &&
+                    CfgGroupedReg64::BK == CfgGroupedReg::BK,
+                "both row heights read the same packed layout");
   const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
-  hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, true>), dim3(tiles_n * (unsigned)p.E),
-                     dim3(CfgGroupedReg::kThreads), 0, stream, p);
+  // row passes of 32 or 64 rows, chosen as for the unpacked weights
+  int gk = tall_experts(p) ? 3 : 2;
+  if (const char* env = getenv("NVFP4_GPLAN")) gk = atoi(env);
+  if (gk == 3)
+    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, true>), dim3(tiles_n * (unsigned)p.E),
+                       dim3(CfgGroupedReg64::kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, true>), dim3(tiles_n * (unsigned)p.E),
+                       dim3(CfgGroupedReg::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

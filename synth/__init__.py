@@ -43,6 +43,20 @@ GROUPED = dict(tokens=512, experts=NUM_EXPERTS, top_k=TOP_K, n=N_EXPERT, k=K_HID
                seed_a=5001, seed_router=5003, seed_expert_base=5000 + 10000, sigma_b=0.02)
 
 
+# Grouped calls of E experts with the same row count each: per-expert rows
+# 16, 32, 64 at both expert widths, with weights totalling >= 512 MB so that
+# they stream from HBM (256 experts x 768 x 6144 -> 679 MB; 80 x 2048 x 6144
+# -> 566 MB).  Random code bytes and scale bytes 0x20..0x38 on both sides.
+GROUPED_UNIFORM = [dict(n=n, rows_per_expert=m, experts=e, k=K_HIDDEN, seed=7000 + 10 * i)
+                   for i, (n, e, m) in enumerate([(768, 256, 16), (768, 256, 32), (768, 256, 64),
+                                                  (2048, 80, 16), (2048, 80, 32), (2048, 80, 64)])]
+
+
+def uniform_offsets(rows_per_expert: int, experts: int) -> np.ndarray:
+    """offsets int32[experts+1] with rows_per_expert rows in every expert."""
+    return (np.arange(experts + 1, dtype=np.int64) * rows_per_expert).astype(np.int32)
+
+
 def normal_f32(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
     """N(0, sigma^2) float32 draws from PCG64(seed)."""
     rng = np.random.default_rng(seed)

@@ -119,12 +119,12 @@ def test_invalid_offsets_reported_and_skipped():
     assert (bits(d2)[70:] == SENTINEL).all()
 
 
-@pytest.mark.parametrize("gplan,K", [(0, 768), (1, 768), (2, 1536), (2, 768)])
+@pytest.mark.parametrize("gplan,K", [(0, 768), (1, 768), (2, 1536), (2, 768), (3, 1024), (3, 1536), (3, 768)])
 def test_every_grouped_kernel(gplan, K, monkeypatch):
     # each grouped kernel (forced through NVFP4_GPLAN; K = 1536 lets the
-    # register kernel's prefetch depth 2 divide K / 256, K = 768 does not and
+    # register kernels' prefetch depth 2 divide K / 256, K = 768 does not and
     # must fall back), ragged N, experts of 0, 1, 5, 65 and 129 rows (several
-    # row passes)
+    # row passes of 32 or 64 rows)
     monkeypatch.setenv("NVFP4_GPLAN", str(gplan))
     rows, E, N = 300, 8, 330
     off, a, asf, b, bsf, alpha = _small_problem([0, 0, 5, 5, 70, 70, 71, 200, 250], rows, E, N, K, seed=40)
@@ -158,11 +158,14 @@ def _np_pack(b, bsf, N, K, E):
     return pb, psf
 
 
+@pytest.mark.parametrize("gplan", [2, 3])
 @pytest.mark.parametrize("kind", ["alternate", [0, 0, 5, 5, 70, 70, 71, 200, 250]])
-def test_packed_weights_layout_and_gemm(kind):
+def test_packed_weights_layout_and_gemm(kind, gplan, monkeypatch):
+    # gplan 2 / 3: passes of 32 / 64 rows over each expert's packed weights
+    monkeypatch.setenv("NVFP4_GPLAN", str(gplan))
     rows, E, N, K = 300, 8, 330, 1024
     off, a, asf, b, bsf, alpha = _small_problem(kind, rows, E, N, K, seed=60)
-    say("grouped packed", kind)
+    say("grouped packed", kind, "gplan", gplan)
     b_t, bsf_t = dev(b), dev(bsf)
     pb, psf = nv.grouped_pack(b_t, bsf_t, N, K, E)
     want_pb, want_psf = _np_pack(b, bsf, N, K, E)
