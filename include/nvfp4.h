@@ -81,7 +81,8 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf,
                         int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes nvfp4_gemm needs for this shape (0 for most large shapes). */
+/* Workspace bytes nvfp4_gemm needs for this shape: 0 unless the plan splits K
+ * across work-groups (mid M with few output tiles, e.g. 512 x 768 x 6144). */
 size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* Zero-fill a workspace on `stream` with a kernel (safe inside graph capture). */
@@ -161,7 +162,8 @@ nvfp4_status nvfp4_grouped_gemm_packed(const uint8_t* a, const uint8_t* a_sf, co
  *   r  = gs / E4M3(sf)  (0 if E4M3(sf) == 0, correctly rounded division)
  *   code = e2m1_rne_saturating(x * r)   (sign bit kept, so -0 -> 0x8)
  * global_scale: device fp32 encode scale gs; NULL means 1.0f.  K % 16 == 0;
- * x 16-byte aligned; non-finite inputs are outside the contract.
+ * x 16-byte aligned, q 8-byte aligned (ERR_ALIGN otherwise); non-finite
+ * inputs are outside the contract.
  */
 nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K,
                             const float* global_scale, uint8_t* q, uint8_t* sf,

@@ -190,8 +190,8 @@ nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K, const float* g
   if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
   if (R == 0 || K == 0) return ok();
   if (!x || !q || !sf) return fail(NVFP4_ERR_NULL, "x, q and sf must be non-NULL");
-  if (!aligned(x, 16) || !aligned(q, 2) || !aligned(global_scale, 4))
-    return fail(NVFP4_ERR_ALIGN, "x must be 16-byte aligned, q 2-byte aligned, global_scale 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(global_scale, 4))
+    return fail(NVFP4_ERR_ALIGN, "x must be 16-byte aligned, q 8-byte aligned, global_scale 4-byte aligned");
   return hip_status(nvfp4::launch_quantize(x, R, K, global_scale, q, sf, (hipStream_t)stream),
                     "nvfp4_quantize launch");
 }

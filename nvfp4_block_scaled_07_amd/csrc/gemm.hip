@@ -1034,6 +1034,163 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 }
 
 // ---------------------------------------------------------------------------
+// Register-streamed K-group GEMM for small and mid M (no LDS staging, no
+// split-K).  A work-group owns one BM x BN output tile and the whole K range;
+// its KS waves are K-groups: wave w takes the 128-element K units w, w + KS,
+// w + 2 KS, ... .  Every lane loads its own 16-byte code chunks (one per
+// 16-row block of A and of B per unit) and their scale words straight into
+// registers, D units ahead, dequantises them and issues 16x16x32 f16 MFMAs on
+// its wave's full tile.  The KS partial tiles are then summed through LDS in
+// wave order (deterministic) and written as bf16.  Many waves per SIMD hide
+// both the memory latency and the slow issue of the dequantisation VALU,
+// without the partial-tile traffic of a cross-work-group split.
+//
+// Lane l of a wave handles row (or column) l % 16 of each 16-row block and
+// chunk g = l / 16 (K elements 32 g .. 32 g + 31) of every unit; MFMA t of a
+// unit multiplies elements 8 t .. 8 t + 7 of each lane's chunk, i.e. the 32
+// K elements {32 g + 8 t + i}, the same set for A and B.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int KS_, int D_, int OCC_, int ORDER_ = 0>
+struct KCfg {
+  static constexpr int BM = BM_, BN = BN_, KS = KS_, D = D_, OCC = OCC_;
+  // ORDER 0: wave w takes units w, w + KS, ...; 1: a contiguous run of units
+  static constexpr int ORDER = ORDER_;
+  static constexpr int TM = BM / 16, TN = BN / 16;
+  static constexpr int kThreads = KS * 64;
+  static constexpr int kTileFloats = BM * BN;        // one wave's partial tile
+  static constexpr int kUnit = 128;                  // K elements per unit
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row MFMA blocks");
+  static_assert(KS >= 1 && KS <= 16, "waves per work-group");
+  __device__ static int unit(int wave, int i, int per_wave) { return ORDER ? wave * per_wave + i : wave + i * KS; }
+  static_assert(KS * kTileFloats * 4 <= 65536, "partial tiles fit in 64 KB of LDS");
+};
+
+template <class C>
+struct KRegs {
+  uint32_t aq[C::D][C::TM][4], bq[C::D][C::TN][4];  // 16-byte code chunks as 4 words
+  uint32_t as[C::D][C::TM], bs[C::D][C::TN];        // scale words (2 e4m3 per chunk)
+};
+
+// Loads of unit `unit` into slot u; dead units (past the end of K) read out of
+// range, which returns zero without a memory access, so every iteration
+// issues the same loads.
+template <class C>
+__device__ __forceinline__ void kreg_load(KRegs<C>& R, int u, int unit, bool live, const rsrc_t& ra,
+                                          const rsrc_t& ras, const rsrc_t& rb, const rsrc_t& rbs,
+                                          const uint32_t (&va)[C::TM], const uint32_t (&vas)[C::TM],
+                                          const uint32_t (&vb)[C::TN], const uint32_t (&vbs)[C::TN]) {
+  constexpr uint32_t kOut = 0x80000000u;
+  const int so = unit * (C::kUnit / 2), sso = unit * (C::kUnit / 16);
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm) {
+    const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va[tm] : kOut, so, 0));
+    R.aq[u][tm][0] = v[0]; R.aq[u][tm][1] = v[1]; R.aq[u][tm][2] = v[2]; R.aq[u][tm][3] = v[3];
+    R.as[u][tm] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas[tm] : kOut, sso, 0);
+  }
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn] : kOut, so, 0));
+    R.bq[u][tn][0] = v[0]; R.bq[u][tn][1] = v[1]; R.bq[u][tn][2] = v[2]; R.bq[u][tn][3] = v[3];
+    R.bs[u][tn] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn] : kOut, sso, 0);
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gemm_kreg(
+    GemmLaunch p) {
+  __shared__ __attribute__((aligned(16))) float red[C::KS * C::kTileFloats];
+  const int tiles_n = (int)p.tiles_n;
+  const int L = xcd_remap(blockIdx.x, (int)(p.tiles_m * p.tiles_n));
+  const int64_t m0 = (int64_t)(L / tiles_n) * C::BM, n0 = (int64_t)(L % tiles_n) * C::BN;
+  const int64_t ld = p.K / 2, lds = p.K / 16;
+  const int rows_a = (int)min<int64_t>(C::BM, p.M - m0), rows_b = (int)min<int64_t>(C::BN, p.N - n0);
+  const rsrc_t ra = make_rsrc(p.a + m0 * ld, (uint32_t)(rows_a * ld));
+  const rsrc_t ras = make_rsrc(p.a_sf + m0 * lds, (uint32_t)(rows_a * lds));
+  const rsrc_t rb = make_rsrc(p.b + n0 * ld, (uint32_t)(rows_b * ld));
+  const rsrc_t rbs = make_rsrc(p.b_sf + n0 * lds, (uint32_t)(rows_b * lds));
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int r_in = lane & 15, g = lane >> 4;
+  uint32_t va[C::TM], vas[C::TM], vb[C::TN], vbs[C::TN];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm) {
+    const int r = tm * 16 + r_in;
+    va[tm] = r < rows_a ? (uint32_t)(r * ld + g * 16) : 0x80000000u;
+    vas[tm] = r < rows_a ? (uint32_t)(r * lds + 4 * (g >> 1)) : 0x80000000u;
+  }
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const int r = tn * 16 + r_in;
+    vb[tn] = r < rows_b ? (uint32_t)(r * ld + g * 16) : 0x80000000u;
+    vbs[tn] = r < rows_b ? (uint32_t)(r * lds + 4 * (g >> 1)) : 0x80000000u;
+  }
+  const int nu = (int)(p.K / C::kUnit);
+  // every wave runs the same number of iterations (a multiple of D); units
+  // past the end are dead
+  const int per_wave = (nu + C::KS - 1) / C::KS;
+  const int iters = (per_wave + C::D - 1) / C::D * C::D;
+  Mfma<16>::Acc acc[C::TM][C::TN];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<16>::Acc{0.f, 0.f, 0.f, 0.f};
+  KRegs<C> R;
+#pragma unroll
+  for (int u = 0; u < C::D; ++u) {
+    const int unit = C::unit(wave, u, per_wave);
+    kreg_load<C>(R, u, unit, u < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int sh = 16 * (g & 1);
+  for (int i0 = 0; i0 < iters; i0 += C::D) {
+#pragma unroll
+    for (int u = 0; u < C::D; ++u) {
+      h2_t asp[C::TM], bsp[C::TN];
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm) asp[tm] = e4m3x2_to_h2(R.as[u][tm] >> sh);
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) bsp[tn] = e4m3x2_to_h2(R.bs[u][tn] >> sh);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        h8_t bf[C::TN];
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) bf[tn] = dequant8(R.bq[u][tn][t], scale_pair(bsp[tn], t >> 1));
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) {
+          const h8_t af = dequant8(R.aq[u][tm][t], scale_pair(asp[tm], t >> 1));
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<16>::run(af, bf[tn], acc[tm][tn]);
+        }
+      }
+      // the slot's reload stays after its last reads (old and new contents
+      // share registers; no copies that would wait on the load)
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = i0 + u + C::D;
+      const int unit = C::unit(wave, i, per_wave);
+      kreg_load<C>(R, u, unit, i < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+    }
+  }
+  // K-group sum: wave w's partial tile at red[w][.], element (tm, tn, lane, j)
+  // at ((tm * TN + tn) * 64 + lane) * 4 + j
+  float* mine = red + wave * C::kTileFloats;
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) *(f4_t*)(mine + ((tm * C::TN + tn) * 64 + lane) * 4) = acc[tm][tn];
+  __syncthreads();
+  const float alpha = p.alpha ? *p.alpha : 1.0f;
+  for (int x = threadIdx.x; x < C::kTileFloats; x += C::kThreads) {
+    // output (row, col), columns fastest so the stores are contiguous
+    const int row = x / C::BN, col = x % C::BN;
+    const int rr = row & 15, cc = col & 15;
+    const int idx = (((row >> 4) * C::TN + (col >> 4)) * 64 + (rr >> 2) * 16 + cc) * 4 + (rr & 3);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::KS; ++w) sum += red[w * C::kTileFloats + idx];
+    if (row < rows_a && col < rows_b) p.d[(m0 + row) * p.N + n0 + col] = f32_to_bf16_bits(alpha * sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Plans and launchers.
 // ---------------------------------------------------------------------------
 typedef Cfg<256, 256, 2, 2, 32, 128, 4> CfgTile256;     // large M and N: 128x128 wave tiles
@@ -1046,6 +1203,12 @@ typedef Cfg<256, 256, 2, 4, 32, 128, 4> CfgTile256w8;   // large: 8 waves of 128
 typedef Cfg<256, 256, 2, 2, 32, 128, 4, 4> CfgTile256il; // large, MFMA/VALU interleave hint
 typedef Cfg<128, 128, 2, 2, 32, 128, 4, 4, 1, 2> CfgTile128il;  // mid-large, interleave hint
 typedef Cfg<64, 64, 1, 1, 32, 256, 2, 0, 4, 4> CfgTile64k4;  // mid: 4 K-groups of one 64x64 wave
+// register-streamed K-group tiles: 8 or 16 waves, 3 units in flight per wave
+typedef KCfg<16, 16, 8, 3, 4, 1> KReg16x16;
+typedef KCfg<32, 16, 16, 3, 4> KReg32x16;
+typedef KCfg<64, 16, 16, 3, 4> KReg64x16;
+typedef KCfg<32, 32, 8, 3, 4, 1> KReg32x32;
+typedef KCfg<64, 32, 8, 3, 2> KReg64x32;
 typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass
@@ -1056,6 +1219,7 @@ struct PlanKind {
   const char* name;
   int bm, bn, bk;
   bool splitk;
+  bool kreg;  // register-streamed K-group kernel (no workspace)
 };
 static const PlanKind kKinds[] = {
     {"tile256x256_mfma32", 256, 256, 128, false},
@@ -1068,6 +1232,11 @@ static const PlanKind kKinds[] = {
     {"tile256x256il_mfma32", 256, 256, 128, false},
     {"tile128x128il_mfma32", 128, 128, 128, true},
     {"tile64x64k4_mfma32", 64, 64, 256, true},
+    {"kreg16x16_mfma16", 16, 16, 128, false, true},
+    {"kreg32x16_mfma16", 32, 16, 128, false, true},
+    {"kreg64x16_mfma16", 64, 16, 128, false, true},
+    {"kreg32x32_mfma16", 32, 32, 128, false, true},
+    {"kreg64x32_mfma16", 64, 32, 128, false, true},
 };
 static constexpr int kNumKinds = (int)(sizeof(kKinds) / sizeof(kKinds[0]));
 
@@ -1111,19 +1280,33 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
   }
 }
 
-// Plan choice, from measured sweeps on MI355X of the pages' shapes
-// (K = 6144, N = 768 / 2048 / 6144): skinny 16-row tiles up to M = 32, 32-row
-// tiles up to M = 64, 64x64 K-group tiles (split-K while there are fewer than
-// 192 of them) up to the point where 256x256 tiles fill the CUs twice.
+// Plan choice, from cold sweeps on MI355X of the pages' shapes (K = 6144,
+// N = 768 / 2048 / 6144): up to M = 256, the register-streamed K-group tile
+// (16 waves per work-group, no split-K), the smallest of 16x16, 32x16, 32x32,
+// 64x32 that needs at most one work-group per CU; above that, 64x64 K-group
+// tiles (split-K while there are fewer than 192 of them) up to the point
+// where 256x256 tiles fill the CUs twice.
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
-  int kind;
+  int kind = -1;
   int forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (M <= 32) kind = 3;
-  else if (M <= 64) kind = 4;
-  else if (t256 >= 2 * kCUs) kind = 0;
-  else kind = 9;
+  if (M <= 256) {
+    static const int kreg_kinds[] = {10, 11, 13, 14};  // 16x16, 32x16, 32x32, 64x32
+    for (int kk : kreg_kinds) {
+      const PlanKind& k = kKinds[kk];
+      if (((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) <= kCUs) {
+        kind = kk;
+        break;
+      }
+    }
+  }
+  if (kind < 0) {
+    if (M <= 32) kind = 3;
+    else if (M <= 64) kind = 4;
+    else if (t256 >= 2 * kCUs) kind = 0;
+    else kind = 9;
+  }
   // NVFP4_PLAN=<kind>[,<splits>] forces a plan (tuning sweeps only)
   if (const char* env = getenv("NVFP4_PLAN")) {
     int fk = -1, fs = 0;
@@ -1141,6 +1324,12 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   if (!k.splitk || pl.tiles_m * pl.tiles_n >= kCUs) forced_splits = 1;
   plan_splits(pl, k, K, forced_splits);
   return pl;
+}
+
+template <class C>
+static void launch_kreg(const GemmPlan& pl, const GemmLaunch& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)(pl.tiles_m * pl.tiles_n);
+  hipLaunchKernelGGL(k_gemm_kreg<C>, dim3(grid), dim3(C::kThreads), 0, stream, p);
 }
 
 template <class C, bool SPLITK>
@@ -1164,6 +1353,11 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
     case 6: launch_one<CfgTile256w8, false>(pl, p, stream); break;
     case 7: launch_one<CfgTile256il, false>(pl, p, stream); break;
     case 8: launch_one<CfgTile128il, true>(pl, p, stream); break;
+    case 10: launch_kreg<KReg16x16>(pl, p, stream); break;
+    case 11: launch_kreg<KReg32x16>(pl, p, stream); break;
+    case 12: launch_kreg<KReg64x16>(pl, p, stream); break;
+    case 13: launch_kreg<KReg32x32>(pl, p, stream); break;
+    case 14: launch_kreg<KReg64x32>(pl, p, stream); break;
     default: launch_one<CfgTile64k4, true>(pl, p, stream); break;
   }
   return hipGetLastError();

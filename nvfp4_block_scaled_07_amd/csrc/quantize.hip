@@ -37,34 +37,53 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t code) {
   return e ? __builtin_ldexpf((float)(8 + m), e - 10) : __builtin_ldexpf((float)m, -9);
 }
 
-// fp32 y -> e2m1 code, round to nearest even, saturating at 6, sign kept.
-__device__ __forceinline__ uint32_t e2m1_encode(float y) {
-  const float a = fabsf(y);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
+// Codes of 8 consecutive scaled elements, 2 per byte (element 2j in the low
+// nibble of byte j).  The hardware f32 -> e2m1 conversion (scale 1.0: no
+// extra scaling) rounds to nearest even, saturates at +-6 and keeps the sign
+// of values that round to zero.
+__device__ __forceinline__ uint32_t e2m1x8(f4_t lo, f4_t hi, float r) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo[0] * r, lo[1] * r, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo[2] * r, lo[3] * r, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hi[0] * r, hi[1] * r, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hi[2] * r, hi[3] * r, 1.0f, 3);
+  return w;
 }
 
-// One thread per 4 consecutive elements; 4 consecutive lanes form a block.
-__global__ __launch_bounds__(256) void k_quantize(const f4_t* __restrict__ x, int64_t n4,
-                                                  const float* __restrict__ gs_p, uint16_t* __restrict__ q,
+// One thread per 16-element block (4 loads of 16 bytes, 8 code bytes and one
+// scale byte out); the block's scale is computed once.  Each thread handles
+// kQB blocks, one grid width apart, with all their loads issued first.
+constexpr int kQB = 2;
+
+__global__ __launch_bounds__(256) void k_quantize(const f4_t* __restrict__ x, int64_t nb,
+                                                  const float* __restrict__ gs_p, u2_t* __restrict__ q,
                                                   uint8_t* __restrict__ sf) {
   const float gs = gs_p ? *gs_p : 1.0f;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  // n4 is a multiple of 4 and the stride a multiple of 64, so the 4 lanes of
-  // a block are always active together.
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const f4_t v = x[i];
-    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-    a = fmaxf(a, __shfl_xor(a, 1));
-    a = fmaxf(a, __shfl_xor(a, 2));
-    const float t = (a / 6.0f) * gs;
-    const uint32_t code = e4m3_encode_pos(t);
-    const float sv = e4m3_value_pos(code);
-    const float r = sv == 0.0f ? 0.0f : gs / sv;
-    const uint32_t c0 = e2m1_encode(v[0] * r), c1 = e2m1_encode(v[1] * r);
-    const uint32_t c2 = e2m1_encode(v[2] * r), c3 = e2m1_encode(v[3] * r);
-    q[i] = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-    if ((i & 3) == 0) sf[i >> 2] = (uint8_t)code;
+  for (int64_t b0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b0 < nb; b0 += kQB * stride) {
+    f4_t v[kQB][4];
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) {
+      const int64_t b = b0 + j * stride;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[j][c] = b < nb ? x[4 * b + c] : f4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) {
+      const int64_t b = b0 + j * stride;
+      float a = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[j][c][0]), fabsf(v[j][c][1])), fmaxf(fabsf(v[j][c][2]), fabsf(v[j][c][3]))));
+      const float t = (a / 6.0f) * gs;
+      const uint32_t code = e4m3_encode_pos(t);
+      const float sv = e4m3_value_pos(code);
+      const float r = sv == 0.0f ? 0.0f : gs / sv;
+      if (b < nb) {
+        q[b] = u2_t{e2m1x8(v[j][0], v[j][1], r), e2m1x8(v[j][2], v[j][3], r)};
+        sf[b] = (uint8_t)code;
+      }
+    }
   }
 }
 
@@ -73,20 +92,35 @@ __global__ void k_zero_word(uint32_t* w) {
 }
 
 // max |x| as fp32 bits (non-negative floats order like their bit patterns).
+// Reduced per wave, then per work-group through LDS: one atomic per
+// work-group (atomics on one word serialise in L2).
 __global__ __launch_bounds__(256) void k_amax(const float* __restrict__ x, int64_t n, uint32_t* __restrict__ out) {
+  __shared__ float wmax[4];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t n4 = n / 4;
   float a = 0.0f;
   const f4_t* x4 = (const f4_t*)x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {  // four 1 KB loads in flight per wave
+    const f4_t v0 = x4[i], v1 = x4[i + stride], v2 = x4[i + 2 * stride], v3 = x4[i + 3 * stride];
+    const f4_t m = {fmaxf(fmaxf(fabsf(v0[0]), fabsf(v1[0])), fmaxf(fabsf(v2[0]), fabsf(v3[0]))),
+                    fmaxf(fmaxf(fabsf(v0[1]), fabsf(v1[1])), fmaxf(fabsf(v2[1]), fabsf(v3[1]))),
+                    fmaxf(fmaxf(fabsf(v0[2]), fabsf(v1[2])), fmaxf(fabsf(v2[2]), fabsf(v3[2]))),
+                    fmaxf(fmaxf(fabsf(v0[3]), fabsf(v1[3])), fmaxf(fabsf(v2[3]), fabsf(v3[3])))};
+    a = fmaxf(a, fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+  }
+  for (; i < n4; i += stride) {
     const f4_t v = x4[i];
     a = fmaxf(a, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
   }
-  for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    a = fmaxf(a, fabsf(x[i]));
+  for (int64_t j = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride)
+    a = fmaxf(a, fabsf(x[j]));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(a));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(out, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 __global__ void k_finish_scale(float* gs) {
@@ -103,12 +137,13 @@ __global__ void k_alpha(const float* __restrict__ gs_a, const float* __restrict_
 
 hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs, uint8_t* q, uint8_t* sf,
                            hipStream_t stream) {
-  const int64_t n4 = R * K / 4;
-  if (n4 == 0) return hipSuccess;
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, (const f4_t*)x, n4, gs,
-                     (uint16_t*)q, sf);
+  const int64_t nb = R * K / 16;
+  if (nb == 0) return hipSuccess;
+  // about 8 work-groups (32 waves) per CU
+  int64_t blocks = (nb + 256 * kQB - 1) / (256 * kQB);
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, (const f4_t*)x, nb, gs, (u2_t*)q,
+                     sf);
   return hipGetLastError();
 }
 
@@ -117,9 +152,9 @@ hipError_t launch_global_scale(const float* x, int64_t n, float* gs, hipStream_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (n > 0) {
-    int64_t blocks = (n / 4 + 255) / 256;
+    int64_t blocks = (n / 4 + 1023) / 1024;
     if (blocks < 1) blocks = 1;
-    if (blocks > 2048) blocks = 2048;
+    if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(k_amax, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, (uint32_t*)gs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -55,12 +55,12 @@ def test_gemm_error_paths():
     assert _gemm(a=FAKE + 8) == 3
     assert _gemm(bsf=FAKE + 4) == 3
     assert _gemm(d=FAKE + 2) == 3
-    # small M needs a split-K workspace
-    need = nv.nvfp4_gemm_workspace_size(16, 768, 6144)
+    # a split-K plan (M = 512: 64x64 K-group tiles split in two) needs a workspace
+    need = nv.nvfp4_gemm_workspace_size(512, 768, 6144)
     assert need > 0
-    assert _gemm(N=768, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
-    assert _gemm(N=768, K=6144, ws=FAKE, wsb=need - 1) == 5
-    assert _gemm(N=768, K=6144, ws=FAKE + 16, wsb=need) == 3
+    assert _gemm(M=512, N=768, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
+    assert _gemm(M=512, N=768, K=6144, ws=FAKE, wsb=need - 1) == 5
+    assert _gemm(M=512, N=768, K=6144, ws=FAKE + 16, wsb=need) == 3
     # empty problems succeed without touching anything
     assert _gemm(M=0, a=None, d=None) == 0
     assert _gemm(N=0) == 0
@@ -85,6 +85,7 @@ def test_quantize_and_scale_error_paths():
     assert L.nvfp4_quantize(FAKE, 4, 24, None, FAKE, FAKE, None) == 2
     assert L.nvfp4_quantize(None, 4, 32, None, FAKE, FAKE, None) == 1
     assert L.nvfp4_quantize(FAKE + 4, 4, 32, None, FAKE, FAKE, None) == 3
+    assert L.nvfp4_quantize(FAKE, 4, 32, None, FAKE + 4, FAKE, None) == 3  # codes 8-byte aligned
     assert L.nvfp4_quantize(None, 0, 32, None, None, None, None) == 0
     assert L.nvfp4_global_scale(FAKE, -1, FAKE, None) == 2
     assert L.nvfp4_global_scale(FAKE, 10, None, None) == 1
@@ -94,13 +95,16 @@ def test_quantize_and_scale_error_paths():
 
 def test_plan_and_workspace_queries():
     assert nv.nvfp4_gemm_plan(16384, 6144, 6144).startswith("tile")
-    assert nv.nvfp4_gemm_plan(16, 768, 6144).startswith("skinny16x64")
+    assert nv.nvfp4_gemm_plan(16, 768, 6144).startswith("kreg16x16")
+    assert nv.nvfp4_gemm_plan(64, 2048, 6144).startswith("kreg32x16")
+    assert nv.nvfp4_gemm_plan(1024, 768, 6144).startswith("tile64x64k4")
+    assert nv.nvfp4_gemm_workspace_size(16, 768, 6144) == 0  # register K-group tiles: no workspace
     assert nv.nvfp4_gemm_plan(16, 768, 100) == "none"
     assert nv.nvfp4_gemm_workspace_size(16384, 6144, 6144) == 0
     # split-K plans: a 4096-byte counter block, then fp32 partial tiles
-    ws = nv.nvfp4_gemm_workspace_size(16, 768, 6144)
-    tiles = 768 // 64
-    assert ws > 4096 and (ws - 4096) % (tiles * 16 * 64 * 4) == 0
+    ws = nv.nvfp4_gemm_workspace_size(512, 768, 6144)
+    tiles = (512 // 64) * (768 // 64)
+    assert ws > 4096 and (ws - 4096) % (tiles * 64 * 64 * 4) == 0
 
 
 def test_packed_grouped_error_paths():

@@ -166,14 +166,26 @@ def test_zero_sized_calls_are_noops():
     assert (host(d) == 7).all()
 
 
-def test_split_k_workspace_reuse_and_counters_return_to_zero():
-    # one workspace, zero-filled once, serves several split-K shapes in a row;
+def test_split_k_workspace_reuse_and_counters_return_to_zero(monkeypatch):
+    # one workspace, zero-filled once, serves several split-K shapes in a row
+    # (auto plans, and the skinny split-K tile forced for M = 16 and 64);
     # afterwards every arrival counter is back at zero
-    shapes = [(16, 768, 6144), (64, 2048, 6144), (300, 384, 1024), (16, 768, 6144)]
-    need = max(nv.nvfp4_gemm_workspace_size(*s) for s in shapes)
-    assert need > 0
+    shapes = [(16, 768, 6144, "3"), (512, 768, 6144, None), (64, 2048, 6144, "4"), (300, 384, 1024, None),
+              (16, 768, 6144, "3")]
+    need = 0
+    for (M, N, K, forced) in shapes:
+        if forced:
+            monkeypatch.setenv("NVFP4_PLAN", forced)
+        else:
+            monkeypatch.delenv("NVFP4_PLAN", raising=False)
+        assert nv.nvfp4_gemm_workspace_size(M, N, K) > 0, (M, N, K)
+        need = max(need, nv.nvfp4_gemm_workspace_size(M, N, K))
     ws = nv.nvfp4_workspace_init(torch.empty(need, dtype=torch.uint8, device="cuda"))
-    for (M, N, K) in shapes:
+    for (M, N, K, forced) in shapes:
+        if forced:
+            monkeypatch.setenv("NVFP4_PLAN", forced)
+        else:
+            monkeypatch.delenv("NVFP4_PLAN", raising=False)
         a, b = synth.random_codes(M, M, K), synth.random_codes(N, N, K)
         asf = synth.random_scale_bytes(M + 1, M, K, lo=0x30, hi=0x40)
         bsf = synth.random_scale_bytes(N + 1, N, K, lo=0x30, hi=0x40)
@@ -188,9 +200,10 @@ def test_split_k_workspace_reuse_and_counters_return_to_zero():
 
 
 def test_graph_capture_replays_match_eager():
-    # split-K and single-pass plans captured in one HIP graph; each replay,
+    # register K-group, split-K and single-pass plans captured in one HIP
+    # graph (M = 512 splits K in two); each replay,
     # with eager work and synchronisation in between, must equal the eager run
-    cases = [(16, 768, 6144), (256, 768, 6144), (2048, 2048, 512)]
+    cases = [(16, 768, 6144), (512, 768, 6144), (256, 768, 6144), (2048, 2048, 512)]
     ins, outs, eager = [], [], []
     for (M, N, K) in cases:
         a, b = synth.random_codes(M + 5, M, K), synth.random_codes(N + 5, N, K)
@@ -231,7 +244,7 @@ def test_every_plan_kind_forced(monkeypatch):
     bsf = synth.random_scale_bytes(94, N, K, lo=0x28, hi=0x48)
     at, asft, bt, bsft = dev(a), dev(asf), dev(b), dev(bsf)
     seen = set()
-    for kind in range(16):
+    for kind in range(24):  # past the last kind the plan falls back to auto (deduplicated)
         for splits in (1, 3):
             monkeypatch.setenv("NVFP4_PLAN", f"{kind},{splits}")
             plan = nv.nvfp4_gemm_plan(M, N, K)
