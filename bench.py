@@ -54,6 +54,9 @@ def main():
     ap.add_argument("--profile-grouped", action="store_true",
                     help="for profiler runs: one 256 MiB device copy (counter calibration), then the grouped "
                          "MoE GEMM on packed weights (graph of 10 calls, replayed 4 times); prints its time")
+    ap.add_argument("--profile-mx", type=int, default=0, metavar="M",
+                    help="for profiler runs: the MXFP4 GEMM M x 6144 x 6144 (graph of 10 calls, replayed 6 times); "
+                         "prints its time")
     ap.add_argument("--graph", action="store_true",
                     help="with --profile-call: time the call as the headline does (graphs of 64 calls over "
                          "the rotating sets, replayed 8 times) instead of 8 eager calls")
@@ -119,6 +122,9 @@ def main():
         return
     if args.profile_grouped:
         profile_grouped(torch, nv, synth, quantise, stream)
+        return
+    if args.profile_mx:
+        profile_mx(torch, nv, synth, stream, args.profile_mx)
         return
 
     # ---------------- headline: attention-projection sweep -----------------
@@ -282,6 +288,23 @@ def grouped_inputs(torch, nv, synth, quantise, dev):
                 # expert weights of the active experts, activations, bf16 out, offsets, alphas
                 bytes=active * N * K * 9 // 16 + rows * K * 9 // 16 + 2 * rows * N + 4 * (E + 1) + 4 * E,
                 flops=2.0 * rows * N * K)
+
+
+def profile_mx(torch, nv, synth, stream, m):
+    """Workload of the MXFP4 profiler runs: one M x 6144 x 6144 call, random
+    codes and E8M0 scales in [120, 134], timed as the bench's large shapes."""
+    N = K = 6144
+    dev = torch.device("cuda")
+    a = torch.from_numpy(synth.random_codes(9100, m, K)).to(dev)
+    asf = torch.from_numpy(synth.random_scale_bytes(9101, m, 2 * K, 120, 134)[:, : K // 32].copy()).to(dev)
+    b = torch.from_numpy(synth.random_codes(9102, N, K)).to(dev)
+    bsf = torch.from_numpy(synth.random_scale_bytes(9103, N, 2 * K, 120, 134)[:, : K // 32].copy()).to(dev)
+    d = torch.empty((m, N), dtype=torch.int16, device=dev)
+    ws = nv.mx_gemm_workspace(m, N, K)
+    us = timed(torch, stream, lambda i: nv.nvfp4_mx_gemm(a, asf, b, bsf, None, d, m, N, K, ws), 10)
+    fl = 2.0 * m * N * K
+    print(json.dumps({"call": f"nvfp4_mx_gemm M={m} N={N} K={K} ({nv.nvfp4_mx_gemm_plan(m, N, K)})",
+                      "us_per_call": round(us, 2), "tflops": round(fl / us / 1e6, 1)}))
 
 
 def grouped_call_name(rows, N, K, E):
@@ -499,6 +522,40 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
         del pb, psf, qa, sfa, d, ws
         torch.cuda.empty_cache()
     res["grouped_uniform_experts"] = dict(cache="cold (weights >= 512 MB)", shapes=uni)
+
+    # MXFP4 (E8M0 scale per 32 elements, the scaled FP4 MFMA): the attention
+    # sweep (cold, rotating sets) and the large shapes, random codes and scales
+    mxr = {}
+    for name, rotate, reps in (("attn_proj_n768_k6144", True, 64), ("large_n6144_k6144", False, 10)):
+        w = synth.WORKLOADS[name]
+        N, K = w["n"], w["k"]
+        rows = []
+        for m in w["ms"]:
+            per = (m + N) * K * 17 // 32
+            nsets = max(1, -(-ROTATE_BYTES // per)) if rotate else 1
+            sets = []
+            for i in range(nsets):
+                sd = 9000 + 10 * i if i < 2 else None
+                if sd is None:
+                    sets.append(tuple(t.clone() for t in sets[i % 2]))
+                    continue
+                sets.append((torch.from_numpy(synth.random_codes(sd, m, K)).to(dev),
+                             torch.from_numpy(synth.random_scale_bytes(sd + 1, m, 2 * K, 120, 134)[:, : K // 32]
+                                              .copy()).to(dev),
+                             torch.from_numpy(synth.random_codes(sd + 2, N, K)).to(dev),
+                             torch.from_numpy(synth.random_scale_bytes(sd + 3, N, 2 * K, 120, 134)[:, : K // 32]
+                                              .copy()).to(dev)))
+            d = torch.empty((m, N), dtype=torch.int16, device=dev)
+            ws = nv.mx_gemm_workspace(m, N, K)
+            r = min(reps, max(len(sets), 8)) if rotate else reps
+            us = timed(torch, stream, lambda i: nv.nvfp4_mx_gemm(*sets[i % len(sets)], None, d, m, N, K, ws), r)
+            fl = 2.0 * m * N * K
+            rows.append(dict(M=m, N=N, K=K, plan=nv.nvfp4_mx_gemm_plan(m, N, K), us=round(us, 2),
+                             tflops=round(fl / us / 1e6, 2), frac_fp4_peak=round(fl / us / 1e6 / PEAK_FP4_TFLOPS, 4)))
+            del sets, d, ws
+            torch.cuda.empty_cache()
+        mxr[name] = dict(cache="cold (rotating sets)" if rotate else "warm", shapes=rows)
+    res["mxfp4"] = mxr
 
     # context: the vendor bf16 GEMM (torch.matmul -> hipBLASLt) on already
     # dequantised operands at the same shapes, cold as above (the MI355X

@@ -187,6 +187,37 @@ nvfp4_status nvfp4_alpha_from_scales(const float* gs_a, const float* gs_b,
 /* Name of the kernel plan nvfp4_gemm picks for a shape (static string). */
 const char* nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K);
 
+/*
+ * MXFP4 GEMM: the format the signature of mm_fp4 switches to with
+ * use_nvfp4 = False ("The Art of Reading the Manual: Debugging FP4 GEMM
+ * Kernels on Blackwell SM120", section "The Message").  The pages do not
+ * describe it; this follows the OCP Microscaling Formats (MX) v1.0 MXFP4
+ * element and scale types:
+ *   D[m][n] = bf16_rne(alpha * sum_k E2M1(a[m][k]) * 2^(a_sf[m][k/32] - 127)
+ *                                    * E2M1(b[n][k]) * 2^(b_sf[n][k/32] - 127))
+ * a uint8 [M][K/2], b uint8 [N][K/2] (two codes per byte, element 2j in the
+ * low nibble of byte j; b is the column-major K x N operand, as in
+ * nvfp4_gemm), a_sf uint8 [M][K/32], b_sf uint8 [N][K/32] (E8M0 exponents).
+ * The hardware scaled FP4 MFMA applies the scales and accumulates in fp32.
+ * Scale byte 0xFF (NaN) and products outside the fp32 range are outside
+ * the contract.  K % 256 == 0 and K <= 2^22 (ERR_UNSUPPORTED; ERR_SHAPE if
+ * not a multiple of 32); a, b 16-byte aligned; a_sf, b_sf 4-byte aligned;
+ * d, alpha 4-byte aligned.  alpha, workspace, ownership and stream as for
+ * nvfp4_gemm (the workspace query below; split-K plans keep their counters
+ * in the first 4096 bytes, which every completed call leaves at zero).
+ */
+nvfp4_status nvfp4_mx_gemm(const uint8_t* a, const uint8_t* a_sf,
+                           const uint8_t* b, const uint8_t* b_sf,
+                           const float* alpha, uint16_t* d,
+                           int64_t M, int64_t N, int64_t K,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes nvfp4_mx_gemm needs for this shape (0 unless it splits K). */
+size_t nvfp4_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Name of the kernel plan nvfp4_mx_gemm picks for a shape (static string). */
+const char* nvfp4_mx_gemm_plan(int64_t M, int64_t N, int64_t K);
+
 /* Message describing the calling thread's last error ("" if none). */
 const char* nvfp4_last_error(void);
 

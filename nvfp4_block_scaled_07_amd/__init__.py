@@ -39,6 +39,9 @@ SIGNATURES = {
     "nvfp4_global_scale": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_alpha_from_scales": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
     "nvfp4_gemm_plan": (ctypes.c_char_p, [_i64, _i64, _i64]),
+    "nvfp4_mx_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "nvfp4_mx_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_mx_gemm_plan": (ctypes.c_char_p, [_i64, _i64, _i64]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
 }
 
@@ -110,6 +113,36 @@ def gemm_workspace(M: int, N: int, K: int, device="cuda"):
         return None
     ws = torch.empty(need, dtype=torch.uint8, device=device)
     return nvfp4_workspace_init(ws)
+
+
+def nvfp4_mx_gemm_plan(M: int, N: int, K: int) -> str:
+    return lib().nvfp4_mx_gemm_plan(M, N, K).decode()
+
+
+def nvfp4_mx_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_mx_gemm_workspace_size(M, N, K))
+
+
+def mx_gemm_workspace(M: int, N: int, K: int, device="cuda"):
+    """Allocate and zero-fill the workspace nvfp4_mx_gemm needs (None if none)."""
+    import torch
+    need = nvfp4_mx_gemm_workspace_size(M, N, K)
+    if need == 0:
+        return None
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return nvfp4_workspace_init(ws)
+
+
+def nvfp4_mx_gemm(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, workspace=None, stream=None):
+    """MXFP4 GEMM (E8M0 scales per 32 elements); see include/nvfp4.h.
+    a: uint8 [M][K/2], a_sf: uint8 [M][K/32], b: uint8 [N][K/2],
+    b_sf: uint8 [N][K/32], alpha: fp32 device scalar tensor or None,
+    d: caller-allocated [M][N] bf16 (or int16/uint16) tensor, returned."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_mx_gemm(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(d), M, N, K,
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nvfp4_mx_gemm")
+    return d
 
 
 def nvfp4_grouped_workspace_size(rows: int, N: int, K: int, E: int) -> int:

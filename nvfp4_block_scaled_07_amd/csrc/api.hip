@@ -86,6 +86,43 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
   return hip_status(nvfp4::launch_gemm(plan, p, (hipStream_t)stream), "nvfp4_gemm launch");
 }
 
+size_t nvfp4_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return 0;
+  return nvfp4::choose_mx_plan(M, N, K).workspace;
+}
+
+const char* nvfp4_mx_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return "none";
+  return nvfp4::choose_mx_plan(M, N, K).name;
+}
+
+nvfp4_status nvfp4_mx_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                           const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0) return fail(NVFP4_ERR_SHAPE, "M = %lld, N = %lld must be >= 0", (long long)M, (long long)N);
+  if (K < 0 || K % 32 != 0)
+    return fail(NVFP4_ERR_SHAPE, "K = %lld is not a non-negative multiple of the MX block size 32", (long long)K);
+  nvfp4_status s = check_k(K);
+  if (s != NVFP4_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  if (!a || !a_sf || !b || !b_sf || !d)
+    return fail(NVFP4_ERR_NULL, "a, a_sf, b, b_sf and d must be non-NULL (alpha may be NULL)");
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_sf, 4) || !aligned(b_sf, 4))
+    return fail(NVFP4_ERR_ALIGN, "a and b must be 16-byte aligned, a_sf and b_sf 4-byte aligned");
+  if (!aligned(d, 4) || !aligned(alpha, 4)) return fail(NVFP4_ERR_ALIGN, "d and alpha must be 4-byte aligned");
+  if (M > (1ll << 30) || N > (1ll << 30))
+    return fail(NVFP4_ERR_UNSUPPORTED, "dimensions above 2^30 are not supported");
+  const nvfp4::GemmPlan plan = nvfp4::choose_mx_plan(M, N, K);
+  if (plan.workspace > 0) {
+    if (!workspace || workspace_bytes < plan.workspace)
+      return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu workspace bytes, got %zu", plan.name, plan.workspace,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 0, 1, 1};
+  return hip_status(nvfp4::launch_mx_gemm(plan, p, (hipStream_t)stream), "nvfp4_mx_gemm launch");
+}
+
 nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (workspace_bytes == 0) return ok();
   if (!workspace) return fail(NVFP4_ERR_NULL, "workspace must be non-NULL");

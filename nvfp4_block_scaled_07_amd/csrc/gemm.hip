@@ -74,8 +74,12 @@ struct Mfma<16> {
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int MF_, int BK_, int STAGES_, int IL_ = 0, int KS_ = 1,
-          int OCC_ = 1>
+          int OCC_ = 1, int SBLK_ = 16>
 struct Cfg {
+  // SBLK: elements per scale: 16 (NVFP4, e4m3 scales, f16 MFMA after
+  // dequantisation) or 32 (MXFP4, E8M0 scales, scaled FP4 MFMA)
+  static constexpr int SBLK = SBLK_;
+  static constexpr bool kMx = SBLK_ == 32;
   // OCC: waves per SIMD the register allocation must leave room for
   static constexpr int OCC = OCC_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, BK = BK_, STAGES = STAGES_;
@@ -96,13 +100,14 @@ struct Cfg {
   static constexpr int KG = 64 / MF;         // lane groups along K in one MFMA
   static constexpr int CH = BK / 32;         // 16-byte code chunks per row per stage
   static constexpr int RB = BK / 2;          // code bytes per row per stage
-  static constexpr int SB = BK / 16;         // scale bytes per row per stage
+  static constexpr int SB = BK / SBLK;       // scale bytes per row per stage
   static constexpr int kSub = CH / KG;       // MFMA sub-steps per stage (4 K-steps each)
   static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "tile shape");
   static_assert(BK == 128 || BK == 256, "stage depth");
   static_assert(STAGES >= 2 && STAGES <= 8, "pipeline");
   static_assert(KS == 1 || KS == 2 || KS == 4, "K-groups");
   static_assert(kSub % KS == 0, "sub-steps per K-group");
+  static_assert(SBLK == 16 || (SBLK == 32 && MF == 32 && IL == 0), "MX tiles use the 32x32x64 scaled MFMA");
   typedef typename Mfma<MF>::Acc Acc;
 };
 
@@ -280,9 +285,72 @@ __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // row blocks that are computed (grouped experts with few rows).  Per K-step
 // only the A operands and one B operand are live, which keeps the 128x128
 // wave tile of the large plan inside the register file.
+// MXFP4 stage: per 64-element sub-step, one v_mfma_scale_f32_32x32x64_f8f6f4
+// per (tm, tn).  Lane l supplies the 32 codes of row l % 32 in K block
+// l / 32 of the sub-step (one 16-byte chunk, low nibble first, exactly the
+// stored layout) and that block's E8M0 scale in the low byte of its scale
+// operand; the hardware applies both scales and accumulates in fp32.
+template <class C>
+__device__ __forceinline__ void compute_stage_mx(const Smem<C>& sm, int buf, typename C::Acc (&acc)[C::TM][C::TN]) {
+  typedef int v8i_t __attribute__((ext_vector_type(8)));
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
+  const int wm = gw / C::WN, wn = gw % C::WN;
+  const int r_in = lane % 32, g = lane / 32;
+  const uint32_t a_base = lds_addr(sm.a[buf]), b_base = lds_addr(sm.b[buf]);
+  const uint32_t as_base = lds_addr(sm.asf[buf]), bs_base = lds_addr(sm.bsf[buf]);
+#pragma unroll
+  for (int ss = 0; ss < C::kSub / C::KS; ++ss) {
+    const int s = ss * C::KS + kgrp;
+    const int c = C::KG * s + g;  // chunk = MX block of this lane in the stage
+    u4_t ac[C::TM], bc[C::TN];
+    uint32_t asw[C::TM], bsw[C::TN];
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      const int row = wm * C::kWM + tm * 32 + r_in;
+      ds_read128(ac[tm], a_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
+      ds_read32(asw[tm], as_base + row * C::SB + 4 * (c >> 2));
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int row = wn * C::kWN + tn * 32 + r_in;
+      ds_read128(bc[tn], b_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
+      ds_read32(bsw[tn], bs_base + row * C::SB + 4 * (c >> 2));
+    }
+    lgkm_wait();
+    const int sh = 8 * (c & 3);
+    v8i_t av[C::TM], bv[C::TN];
+    int sa[C::TM], sb[C::TN];
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      pin(ac[tm]);
+      pin(asw[tm]);
+      av[tm] = v8i_t{(int)ac[tm][0], (int)ac[tm][1], (int)ac[tm][2], (int)ac[tm][3], 0, 0, 0, 0};
+      sa[tm] = (int)(asw[tm] >> sh);
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      pin(bc[tn]);
+      pin(bsw[tn]);
+      bv[tn] = v8i_t{(int)bc[tn][0], (int)bc[tn][1], (int)bc[tn][2], (int)bc[tn][3], 0, 0, 0, 0};
+      sb[tn] = (int)(bsw[tn] >> sh);
+    }
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[tm], bv[tn], acc[tm][tn], 4, 4, 0, sa[tm],
+                                                                       0, sb[tn]);
+  }
+}
+
 template <class C>
 __device__ __forceinline__ void compute_stage(const Smem<C>& sm, int buf, int tm_active,
                                               typename C::Acc (&acc)[C::TM][C::TN]) {
+  if constexpr (C::kMx) {
+    compute_stage_mx<C>(sm, buf, acc);
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
   const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
@@ -601,7 +669,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   const int tile = tmi * tiles_n + tni;
 
   const int64_t m0 = (int64_t)tmi * C::BM, n0 = (int64_t)tni * C::BN;
-  const int64_t ld = p.K / 2, lds = p.K / 16;
+  const int64_t ld = p.K / 2, lds = p.K / C::SBLK;
   Operand A{p.a + m0 * ld, p.a_sf + m0 * lds, ld, lds, (int)min<int64_t>(C::BM, p.M - m0)};
   Operand B{p.b + n0 * ld, p.b_sf + n0 * lds, ld, lds, (int)min<int64_t>(C::BN, p.N - n0)};
   const int nk = (int)(p.K / C::BK);
@@ -1209,6 +1277,12 @@ typedef KCfg<32, 16, 16, 3, 4> KReg32x16;
 typedef KCfg<64, 16, 16, 3, 4> KReg64x16;
 typedef KCfg<32, 32, 8, 3, 4, 1> KReg32x32;
 typedef KCfg<64, 32, 8, 3, 2> KReg64x32;
+// MXFP4 tiles (E8M0 scale per 32 elements, scaled FP4 MFMA)
+typedef Cfg<256, 256, 2, 2, 32, 256, 2, 0, 1, 1, 32> CfgMx256;      // 4 waves x 128x128, 136 KB LDS
+typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx128;      // 4 waves x 64x64, 68 KB (split-K)
+typedef Cfg<64, 64, 2, 2, 32, 256, 3, 0, 1, 2, 32> CfgMx64;         // 4 waves x 32x32 (split-K)
+typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2, 32> CfgMx256w8;    // 8 waves x 128x64
+typedef Cfg<256, 256, 2, 4, 32, 128, 4, 0, 1, 2, 32> CfgMx256w8s4;  // the same, 4 stages of 128
 typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass
@@ -1220,6 +1294,7 @@ struct PlanKind {
   int bm, bn, bk;
   bool splitk;
   bool kreg;  // register-streamed K-group kernel (no workspace)
+  bool mx;    // MXFP4 tile
 };
 static const PlanKind kKinds[] = {
     {"tile256x256_mfma32", 256, 256, 128, false},
@@ -1238,6 +1313,14 @@ static const PlanKind kKinds[] = {
     {"kreg32x32_mfma16", 32, 32, 128, false, true},
     {"kreg64x32_mfma16", 64, 32, 128, false, true},
 };
+static const PlanKind kMxKinds[] = {
+    {"mx256x256_fp4mfma", 256, 256, 256, false, false, true},
+    {"mx128x128_fp4mfma", 128, 128, 256, true, false, true},
+    {"mx64x64_fp4mfma", 64, 64, 256, true, false, true},
+    {"mx256x256w8_fp4mfma", 256, 256, 256, false, false, true},
+    {"mx256x256w8s4_fp4mfma", 256, 256, 128, false, false, true},
+};
+static constexpr int kNumMxKinds = (int)(sizeof(kMxKinds) / sizeof(kMxKinds[0]));
 static constexpr int kNumKinds = (int)(sizeof(kKinds) / sizeof(kKinds[0]));
 
 static const int kCUs = 256;
@@ -1255,7 +1338,7 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
   if (k.splitk && tiles < kCUs) {
     if (forced > 0) {
       s = forced;
-    } else if (k.bk == 256) {
+    } else if (k.bk == 256 && !k.mx) {
       // K-group tiles: about 192 work-groups (three quarters of the CUs, one
       // work-group each) measured best; more splits cost more in the reduction
       // than they gain in occupancy
@@ -1359,6 +1442,49 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
     case 13: launch_kreg<KReg32x32>(pl, p, stream); break;
     case 14: launch_kreg<KReg64x32>(pl, p, stream); break;
     default: launch_one<CfgTile64k4, true>(pl, p, stream); break;
+  }
+  return hipGetLastError();
+}
+
+// MXFP4 plan, from cold sweeps at K = 6144: 256x256 tiles of 8 waves while
+// they fill the CUs twice, then 128x128 (two work-groups per CU) while they
+// fill them once, else 64x64 with split-K up to about 1.5 work-groups per CU.
+// NVFP4_MX_PLAN=<kind>[,<splits>] forces one (tuning sweeps only).
+GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K) {
+  GemmPlan pl;
+  int kind = 2, forced_splits = 0;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t256 >= 2 * kCUs) kind = 4;
+  else if (t128 >= kCUs) kind = 1;
+  if (const char* env = getenv("NVFP4_MX_PLAN")) {
+    int fk = -1, fs = 0;
+    if (sscanf(env, "%d,%d", &fk, &fs) >= 1 && fk >= 0 && fk < kNumMxKinds) {
+      kind = fk;
+      forced_splits = fs;
+    }
+  }
+  const PlanKind& k = kMxKinds[kind];
+  pl.kind = kind;
+  pl.name = k.name;
+  pl.tiles_m = (M + k.bm - 1) / k.bm;
+  pl.tiles_n = (N + k.bn - 1) / k.bn;
+  pl.group_m = 8;
+  if (!k.splitk || pl.tiles_m * pl.tiles_n >= kCUs) forced_splits = 1;
+  plan_splits(pl, k, K, forced_splits);
+  return pl;
+}
+
+hipError_t launch_mx_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
+  p.tiles_m = pl.tiles_m;
+  p.tiles_n = pl.tiles_n;
+  p.splits = pl.splits;
+  p.group_m = pl.group_m;
+  switch (pl.kind) {
+    case 0: launch_one<CfgMx256, false>(pl, p, stream); break;
+    case 1: launch_one<CfgMx128, true>(pl, p, stream); break;
+    case 3: launch_one<CfgMx256w8, false>(pl, p, stream); break;
+    case 4: launch_one<CfgMx256w8s4, false>(pl, p, stream); break;
+    default: launch_one<CfgMx64, true>(pl, p, stream); break;
   }
   return hipGetLastError();
 }

@@ -43,6 +43,9 @@ struct GemmPlan {
 
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
+// MXFP4 (E8M0 scales per 32 elements): GemmLaunch with a_sf / b_sf of K/32 bytes per row.
+GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mx_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
 hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
 // Grouped GEMM on weights pre-packed by launch_pack_b (K % 512 == 0).
 hipError_t launch_grouped_packed(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
