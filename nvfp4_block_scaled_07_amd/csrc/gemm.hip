@@ -180,9 +180,15 @@ __device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int6
     if constexpr (SWZ_MF != 0) c = p ^ swz<D::kPerRow, SWZ_MF>(h * D::kRowsPerInst + lr);
     voff[h] = (uint32_t)(lr * ld + c * VEC);
   }
+  // only this wave's instructions: j = j0, j0 + NWAVES, ... (a loop over
+  // every j with a per-j wave test costs a scalar branch per instruction of
+  // the whole stage in every wave)
+  const int j0 = ((wave - BASE) % NWAVES + NWAVES) % NWAVES;
+  constexpr int kPerWave = (D::kInst + NWAVES - 1) / NWAVES;
 #pragma unroll
-  for (int j = 0; j < D::kInst; ++j) {
-    if ((BASE + j) % NWAVES == wave && j * D::kRowsPerInst < rows_dma) {
+  for (int jj = 0; jj < kPerWave; ++jj) {
+    const int j = j0 + jj * NWAVES;
+    if (j < D::kInst && j * D::kRowsPerInst < rows_dma) {
       const int r = j * D::kRowsPerInst + lr;
       if (D::kInst * D::kRowsPerInst == ROWS || r < ROWS) {
         const uint32_t soff = (uint32_t)(j * D::kRowsPerInst * ld);
@@ -1447,14 +1453,14 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
 }
 
 // MXFP4 plan, from cold sweeps at K = 6144: 256x256 tiles of 8 waves while
-// they fill the CUs twice, then 128x128 (two work-groups per CU) while they
-// fill them once, else 64x64 with split-K up to about 1.5 work-groups per CU.
+// they fill the CUs, then 128x128 (two work-groups per CU) while those fill
+// them, else 64x64 with split-K up to about 1.5 work-groups per CU.
 // NVFP4_MX_PLAN=<kind>[,<splits>] forces one (tuning sweeps only).
 GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   int kind = 2, forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (t256 >= 2 * kCUs) kind = 4;
+  if (t256 >= kCUs) kind = 3;
   else if (t128 >= kCUs) kind = 1;
   if (const char* env = getenv("NVFP4_MX_PLAN")) {
     int fk = -1, fs = 0;
