@@ -1173,9 +1173,11 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gemm_kreg(
     GemmLaunch p) {
   __shared__ __attribute__((aligned(16))) float red[C::KS * C::kTileFloats];
-  const int tiles_n = (int)p.tiles_n;
-  const int L = xcd_remap(blockIdx.x, (int)(p.tiles_m * p.tiles_n));
-  const int64_t m0 = (int64_t)(L / tiles_n) * C::BM, n0 = (int64_t)(L % tiles_n) * C::BN;
+  __shared__ int last_flag;
+  const int tiles_n = (int)p.tiles_n, S = p.splits;
+  const int L = xcd_remap(blockIdx.x, (int)(p.tiles_m * p.tiles_n) * S);
+  const int tile = L / S, z = L % S;
+  const int64_t m0 = (int64_t)(tile / tiles_n) * C::BM, n0 = (int64_t)(tile % tiles_n) * C::BN;
   const int64_t ld = p.K / 2, lds = p.K / 16;
   const int rows_a = (int)min<int64_t>(C::BM, p.M - m0), rows_b = (int)min<int64_t>(C::BN, p.N - n0);
   const rsrc_t ra = make_rsrc(p.a + m0 * ld, (uint32_t)(rows_a * ld));
@@ -1197,7 +1199,10 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     vb[tn] = r < rows_b ? (uint32_t)(r * ld + g * 16) : 0x80000000u;
     vbs[tn] = r < rows_b ? (uint32_t)(r * lds + 4 * (g >> 1)) : 0x80000000u;
   }
-  const int nu = (int)(p.K / C::kUnit);
+  // this work-group's K units [u_lo, u_hi): all of K, or split z of S
+  const int nu_all = (int)(p.K / C::kUnit);
+  const int u_lo = (int)((int64_t)z * nu_all / S), u_hi = (int)((int64_t)(z + 1) * nu_all / S);
+  const int nu = u_hi - u_lo;
   // every wave runs the same number of iterations (a multiple of D); units
   // past the end are dead
   const int per_wave = (nu + C::KS - 1) / C::KS;
@@ -1211,7 +1216,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 #pragma unroll
   for (int u = 0; u < C::D; ++u) {
     const int unit = C::unit(wave, u, per_wave);
-    kreg_load<C>(R, u, unit, u < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+    kreg_load<C>(R, u, u_lo + unit, u < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int sh = 16 * (g & 1);
@@ -1240,7 +1245,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       __builtin_amdgcn_sched_barrier(0);
       const int i = i0 + u + C::D;
       const int unit = C::unit(wave, i, per_wave);
-      kreg_load<C>(R, u, unit, i < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+      kreg_load<C>(R, u, u_lo + unit, i < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
     }
   }
   // K-group sum: wave w's partial tile at red[w][.], element (tm, tn, lane, j)
@@ -1252,16 +1257,40 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     for (int tn = 0; tn < C::TN; ++tn) *(f4_t*)(mine + ((tm * C::TN + tn) * 64 + lane) * 4) = acc[tm][tn];
   __syncthreads();
   const float alpha = p.alpha ? *p.alpha : 1.0f;
+  // the work-group's tile, row-major, columns fastest (contiguous stores)
+  float* part = p.ws + kCounterBytes / 4 + ((int64_t)tile * S + z) * C::kTileFloats;
   for (int x = threadIdx.x; x < C::kTileFloats; x += C::kThreads) {
-    // output (row, col), columns fastest so the stores are contiguous
     const int row = x / C::BN, col = x % C::BN;
     const int rr = row & 15, cc = col & 15;
     const int idx = (((row >> 4) * C::TN + (col >> 4)) * 64 + (rr >> 2) * 16 + cc) * 4 + (rr & 3);
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < C::KS; ++w) sum += red[w * C::kTileFloats + idx];
+    if (S > 1) part[x] = sum;
+    else if (row < rows_a && col < rows_b) p.d[(m0 + row) * p.N + n0 + col] = f32_to_bf16_bits(alpha * sum);
+  }
+  if (S == 1) return;
+  // split K: publish the partial, count arrivals, the last split sums all S
+  // partials in split order and stores bf16 (then resets the counter)
+  int* counter = (int*)p.ws + tile;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = prev == S - 1;
+    if (prev == S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  const float* parts = p.ws + kCounterBytes / 4 + (int64_t)tile * S * C::kTileFloats;
+  for (int x = threadIdx.x; x < C::kTileFloats; x += C::kThreads) {
+    const int row = x / C::BN, col = x % C::BN;
+    float sum = 0.f;
+    for (int zz = 0; zz < S; ++zz) sum += parts[(int64_t)zz * C::kTileFloats + x];
     if (row < rows_a && col < rows_b) p.d[(m0 + row) * p.N + n0 + col] = f32_to_bf16_bits(alpha * sum);
   }
+  if (threadIdx.x == 0) *counter = 0;  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -1299,8 +1328,9 @@ struct PlanKind {
   const char* name;
   int bm, bn, bk;
   bool splitk;
-  bool kreg;  // register-streamed K-group kernel (no workspace)
+  bool kreg;  // register-streamed K-group kernel
   bool mx;    // MXFP4 tile
+  int ks;     // waves (K-groups) of a register-streamed tile
 };
 static const PlanKind kKinds[] = {
     {"tile256x256_mfma32", 256, 256, 128, false},
@@ -1313,11 +1343,11 @@ static const PlanKind kKinds[] = {
     {"tile256x256il_mfma32", 256, 256, 128, false},
     {"tile128x128il_mfma32", 128, 128, 128, true},
     {"tile64x64k4_mfma32", 64, 64, 256, true},
-    {"kreg16x16_mfma16", 16, 16, 128, false, true},
-    {"kreg32x16_mfma16", 32, 16, 128, false, true},
-    {"kreg64x16_mfma16", 64, 16, 128, false, true},
-    {"kreg32x32_mfma16", 32, 32, 128, false, true},
-    {"kreg64x32_mfma16", 64, 32, 128, false, true},
+    {"kreg16x16_mfma16", 16, 16, 128, true, true, false, KReg16x16::KS},
+    {"kreg32x16_mfma16", 32, 16, 128, true, true, false, KReg32x16::KS},
+    {"kreg64x16_mfma16", 64, 16, 128, true, true, false, KReg64x16::KS},
+    {"kreg32x32_mfma16", 32, 32, 128, true, true, false, KReg32x32::KS},
+    {"kreg64x32_mfma16", 64, 32, 128, true, true, false, KReg64x32::KS},
 };
 static const PlanKind kMxKinds[] = {
     {"mx256x256_fp4mfma", 256, 256, 256, false, false, true},
@@ -1344,6 +1374,13 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
   if (k.splitk && tiles < kCUs) {
     if (forced > 0) {
       s = forced;
+    } else if (k.kreg) {
+      // register K-group tiles split K across work-groups (up to 4 ways)
+      // only while there are at most a quarter as many tiles as CUs (cold
+      // sweeps: 16 x 768 x 6144 gains ~1 us, larger grids lose), and keep
+      // at least one K unit per wave in every split
+      s = tiles * 4 <= kCUs ? (kCUs / tiles < 4 ? kCUs / tiles : 4) : 1;
+      if (s > nk / k.ks) s = nk / k.ks;
     } else if (k.bk == 256 && !k.mx) {
       // K-group tiles: about 192 work-groups (three quarters of the CUs, one
       // work-group each) measured best; more splits cost more in the reduction
@@ -1417,7 +1454,7 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
 
 template <class C>
 static void launch_kreg(const GemmPlan& pl, const GemmLaunch& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)(pl.tiles_m * pl.tiles_n);
+  const unsigned grid = (unsigned)(pl.tiles_m * pl.tiles_n * pl.splits);
   hipLaunchKernelGGL(k_gemm_kreg<C>, dim3(grid), dim3(C::kThreads), 0, stream, p);
 }
 

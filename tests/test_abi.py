@@ -98,7 +98,10 @@ def test_plan_and_workspace_queries():
     assert nv.nvfp4_gemm_plan(16, 768, 6144).startswith("kreg16x16")
     assert nv.nvfp4_gemm_plan(64, 2048, 6144).startswith("kreg32x16")
     assert nv.nvfp4_gemm_plan(1024, 768, 6144).startswith("tile64x64k4")
-    assert nv.nvfp4_gemm_workspace_size(16, 768, 6144) == 0  # register K-group tiles: no workspace
+    assert nv.nvfp4_gemm_workspace_size(64, 768, 6144) == 0  # 192 register tiles: no split, no workspace
+    # 48 register tiles of 16x16 split K four ways: counters + fp32 partial tiles
+    assert nv.nvfp4_gemm_workspace_size(16, 768, 6144) == 4096 + 48 * 4 * 16 * 16 * 4
+    assert nv.nvfp4_gemm_workspace_size(32, 768, 6144) == 0          # 96 tiles: no split
     assert nv.nvfp4_gemm_plan(16, 768, 100) == "none"
     assert nv.nvfp4_gemm_workspace_size(16384, 6144, 6144) == 0
     # split-K plans: a 4096-byte counter block, then fp32 partial tiles

@@ -168,10 +168,11 @@ def test_zero_sized_calls_are_noops():
 
 def test_split_k_workspace_reuse_and_counters_return_to_zero(monkeypatch):
     # one workspace, zero-filled once, serves several split-K shapes in a row
-    # (auto plans, and the skinny split-K tile forced for M = 16 and 64);
+    # (auto plans: the K-group and register tiles, and the skinny split-K
+    # tile forced for M = 16 and 64);
     # afterwards every arrival counter is back at zero
     shapes = [(16, 768, 6144, "3"), (512, 768, 6144, None), (64, 2048, 6144, "4"), (300, 384, 1024, None),
-              (16, 768, 6144, "3")]
+              (16, 768, 6144, None), (32, 768, 6144, "10,2"), (16, 768, 6144, "3")]
     need = 0
     for (M, N, K, forced) in shapes:
         if forced:
