@@ -130,3 +130,27 @@ def test_packed_grouped_error_paths():
     assert gemm(off=None) == 1
     assert gemm(d=None) == 1
     assert gemm(rows=-1) == 2
+
+
+def test_mx_gemm_error_paths_and_queries():
+    L = nv.lib()
+    call = lambda **k: L.nvfp4_mx_gemm(k.get("a", FAKE), k.get("asf", FAKE), FAKE, FAKE, None, k.get("d", FAKE),
+                                       k.get("M", 16), k.get("N", 16), k.get("K", 256), k.get("ws", None),
+                                       k.get("wsb", 0), None)
+    assert call(K=48) == 2 and "32" in nv.nvfp4_last_error()      # not a multiple of the MX block
+    assert call(K=-32) == 2
+    assert call(K=160) == 4                                         # multiple of 32, not of 256
+    assert call(K=(1 << 22) + 256) == 4
+    assert call(M=-1) == 2
+    assert call(a=None) == 1
+    assert call(d=None) == 1
+    assert call(a=FAKE + 8) == 3
+    assert call(asf=FAKE + 2) == 3                                  # scales need 4-byte alignment
+    assert call(M=0, a=None) == 0                                   # empty: success before any check
+    assert nv.nvfp4_mx_gemm_plan(16, 768, 100) == "none"
+    assert nv.nvfp4_mx_gemm_plan(16384, 6144, 6144).startswith("mx256x256w8")
+    assert nv.nvfp4_mx_gemm_plan(16, 768, 6144).startswith("mx64x64")
+    need = nv.nvfp4_mx_gemm_workspace_size(16, 768, 6144)
+    assert need > 4096 and (need - 4096) % (12 * 64 * 64 * 4) == 0   # split-K partials of 12 tiles
+    assert call(M=16, N=768, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
+    assert nv.nvfp4_mx_gemm_workspace_size(16384, 6144, 6144) == 0
