@@ -1108,64 +1108,89 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 }
 
 // ---------------------------------------------------------------------------
-// Register-streamed K-group GEMM for small and mid M (no LDS staging, no
-// split-K).  A work-group owns one BM x BN output tile and the whole K range;
-// its KS waves are K-groups: wave w takes the 128-element K units w, w + KS,
-// w + 2 KS, ... .  Every lane loads its own 16-byte code chunks (one per
-// 16-row block of A and of B per unit) and their scale words straight into
-// registers, D units ahead, dequantises them and issues 16x16x32 f16 MFMAs on
-// its wave's full tile.  The KS partial tiles are then summed through LDS in
-// wave order (deterministic) and written as bf16.  Many waves per SIMD hide
-// both the memory latency and the slow issue of the dequantisation VALU,
-// without the partial-tile traffic of a cross-work-group split.
+// Register-streamed K-group GEMM for small and mid M (no LDS staging).  A
+// work-group owns one BM x BN output tile and a K range (all of K, or split z
+// of S); its KS waves are K-groups: wave w takes the 256-element K units w,
+// w + KS, w + 2 KS, ... of the range.  Every lane loads its 16-byte code
+// chunks and scale words straight into registers, D units ahead, dequantises
+// them and issues 16x16x32 f16 MFMAs on its wave's full tile.  The KS partial
+// tiles are summed through LDS in wave order (deterministic); with S > 1 the
+// last split to finish sums the S partials in split order.
 //
-// Lane l of a wave handles row (or column) l % 16 of each 16-row block and
-// chunk g = l / 16 (K elements 32 g .. 32 g + 31) of every unit; MFMA t of a
-// unit multiplies elements 8 t .. 8 t + 7 of each lane's chunk, i.e. the 32
-// K elements {32 g + 8 t + i}, the same set for A and B.
+// A unit is 128 bytes of codes per row, one cache line.  Each 16-row block is
+// loaded with two instructions that each cover 8 whole lines: lane l reads
+// row l % 8 (then row 8 + l % 8), bytes 16 (l / 8) .. 16 (l / 8) + 15.  On a
+// cold call the number of outstanding requests per CU is what limits the
+// rate, and whole-line requests carry twice the bytes of the half lines a
+// 16-row instruction would fetch.  One DPP rotation by 8 lanes within each
+// row of 16 then gives lane l = 16 g + r row r with chunks 2 g (words 0..3)
+// and 2 g + 1 (words 4..7), K elements 64 g .. 64 g + 63 of the unit; its
+// scale word is bytes 4 g .. 4 g + 3 of the row's 16 unit scales.  MFMA t of
+// chunk c multiplies elements 8 t .. 8 t + 7 of that chunk, the same K set
+// for A and B.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int KS_, int D_, int OCC_, int ORDER_ = 0>
+template <int BM_, int BN_, int KS_, int D_, int OCC_>
 struct KCfg {
   static constexpr int BM = BM_, BN = BN_, KS = KS_, D = D_, OCC = OCC_;
-  // ORDER 0: wave w takes units w, w + KS, ...; 1: a contiguous run of units
-  static constexpr int ORDER = ORDER_;
   static constexpr int TM = BM / 16, TN = BN / 16;
   static constexpr int kThreads = KS * 64;
   static constexpr int kTileFloats = BM * BN;        // one wave's partial tile
-  static constexpr int kUnit = 128;                  // K elements per unit
+  static constexpr int kUnit = 256;                  // K elements per unit
   static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row MFMA blocks");
   static_assert(KS >= 1 && KS <= 16, "waves per work-group");
-  __device__ static int unit(int wave, int i, int per_wave) { return ORDER ? wave * per_wave + i : wave + i * KS; }
   static_assert(KS * kTileFloats * 4 <= 65536, "partial tiles fit in 64 KB of LDS");
 };
 
 template <class C>
 struct KRegs {
-  uint32_t aq[C::D][C::TM][4], bq[C::D][C::TN][4];  // 16-byte code chunks as 4 words
-  uint32_t as[C::D][C::TM], bs[C::D][C::TN];        // scale words (2 e4m3 per chunk)
+  uint32_t aq[C::D][C::TM][8], bq[C::D][C::TN][8];  // two 16-byte code chunks as words
+  uint32_t as[C::D][C::TM], bs[C::D][C::TN];        // scale words (4 e4m3)
 };
 
-// Loads of unit `unit` into slot u; dead units (past the end of K) read out of
-// range, which returns zero without a memory access, so every iteration
-// issues the same loads.
+// Loads of unit `unit` into slot u; dead units (past the end of the range)
+// read out of range, which returns zero without a memory access, so every
+// iteration issues the same loads.
 template <class C>
 __device__ __forceinline__ void kreg_load(KRegs<C>& R, int u, int unit, bool live, const rsrc_t& ra,
                                           const rsrc_t& ras, const rsrc_t& rb, const rsrc_t& rbs,
-                                          const uint32_t (&va)[C::TM], const uint32_t (&vas)[C::TM],
-                                          const uint32_t (&vb)[C::TN], const uint32_t (&vbs)[C::TN]) {
+                                          const uint32_t (&va)[C::TM][2], const uint32_t (&vas)[C::TM],
+                                          const uint32_t (&vb)[C::TN][2], const uint32_t (&vbs)[C::TN]) {
   constexpr uint32_t kOut = 0x80000000u;
   const int so = unit * (C::kUnit / 2), sso = unit * (C::kUnit / 16);
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
-    const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va[tm] : kOut, so, 0));
-    R.aq[u][tm][0] = v[0]; R.aq[u][tm][1] = v[1]; R.aq[u][tm][2] = v[2]; R.aq[u][tm][3] = v[3];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va[tm][h] : kOut, so, 0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) R.aq[u][tm][4 * h + j] = v[j];
+    }
     R.as[u][tm] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas[tm] : kOut, sso, 0);
   }
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn) {
-    const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn] : kOut, so, 0));
-    R.bq[u][tn][0] = v[0]; R.bq[u][tn][1] = v[1]; R.bq[u][tn][2] = v[2]; R.bq[u][tn][3] = v[3];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn][h] : kOut, so, 0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) R.bq[u][tn][4 * h + j] = v[j];
+    }
     R.bs[u][tn] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn] : kOut, sso, 0);
+  }
+}
+
+// After the two loads a lane holds row l % 8 (words 0..3) and row 8 + l % 8
+// (words 4..7), chunk l / 8 of each.  Exchange with the lane 8 away in the
+// same row of 16 so that lane 16 g + r holds row r, chunk 2 g in words 0..3
+// and chunk 2 g + 1 in words 4..7.
+__device__ __forceinline__ void kreg_exchange(uint32_t (&w)[8], bool lo8) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t p = w[j], q = w[4 + j];
+    const uint32_t give = lo8 ? q : p;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0x128, 0xF, 0xF, false);  // row_ror:8
+    w[j] = lo8 ? p : recv;
+    w[4 + j] = lo8 ? recv : q;
   }
 }
 
@@ -1186,18 +1211,28 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   const rsrc_t rbs = make_rsrc(p.b_sf + n0 * lds, (uint32_t)(rows_b * lds));
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r_in = lane & 15, g = lane >> 4;
-  uint32_t va[C::TM], vas[C::TM], vb[C::TN], vbs[C::TN];
+  // code offsets: rows lane % 8 and 8 + lane % 8 of each 16-row block, bytes
+  // 16 (lane / 8) of the unit; scale word g of row r_in
+  uint32_t va[C::TM][2], vas[C::TM], vb[C::TN][2], vbs[C::TN];
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = tm * 16 + 8 * h + (lane & 7);
+      va[tm][h] = r < rows_a ? (uint32_t)(r * ld + 16 * (lane >> 3)) : 0x80000000u;
+    }
     const int r = tm * 16 + r_in;
-    va[tm] = r < rows_a ? (uint32_t)(r * ld + g * 16) : 0x80000000u;
-    vas[tm] = r < rows_a ? (uint32_t)(r * lds + 4 * (g >> 1)) : 0x80000000u;
+    vas[tm] = r < rows_a ? (uint32_t)(r * lds + 4 * g) : 0x80000000u;
   }
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = tn * 16 + 8 * h + (lane & 7);
+      vb[tn][h] = r < rows_b ? (uint32_t)(r * ld + 16 * (lane >> 3)) : 0x80000000u;
+    }
     const int r = tn * 16 + r_in;
-    vb[tn] = r < rows_b ? (uint32_t)(r * ld + g * 16) : 0x80000000u;
-    vbs[tn] = r < rows_b ? (uint32_t)(r * lds + 4 * (g >> 1)) : 0x80000000u;
+    vbs[tn] = r < rows_b ? (uint32_t)(r * lds + 4 * g) : 0x80000000u;
   }
   // this work-group's K units [u_lo, u_hi): all of K, or split z of S
   const int nu_all = (int)(p.K / C::kUnit);
@@ -1215,37 +1250,43 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   KRegs<C> R;
 #pragma unroll
   for (int u = 0; u < C::D; ++u) {
-    const int unit = C::unit(wave, u, per_wave);
-    kreg_load<C>(R, u, u_lo + unit, u < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+    const int unit = wave + u * C::KS;
+    kreg_load<C>(R, u, u_lo + unit, unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const int sh = 16 * (g & 1);
+  const bool lo8 = (lane & 8) == 0;
   for (int i0 = 0; i0 < iters; i0 += C::D) {
 #pragma unroll
     for (int u = 0; u < C::D; ++u) {
-      h2_t asp[C::TM], bsp[C::TN];
 #pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm) asp[tm] = e4m3x2_to_h2(R.as[u][tm] >> sh);
+      for (int tm = 0; tm < C::TM; ++tm) kreg_exchange(R.aq[u][tm], lo8);
 #pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) bsp[tn] = e4m3x2_to_h2(R.bs[u][tn] >> sh);
+      for (int tn = 0; tn < C::TN; ++tn) kreg_exchange(R.bq[u][tn], lo8);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        h8_t bf[C::TN];
+      for (int c = 0; c < 2; ++c) {
+        h2_t asp[C::TM], bsp[C::TN];
 #pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn) bf[tn] = dequant8(R.bq[u][tn][t], scale_pair(bsp[tn], t >> 1));
+        for (int tm = 0; tm < C::TM; ++tm) asp[tm] = e4m3x2_to_h2(R.as[u][tm] >> (16 * c));
 #pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm) {
-          const h8_t af = dequant8(R.aq[u][tm][t], scale_pair(asp[tm], t >> 1));
+        for (int tn = 0; tn < C::TN; ++tn) bsp[tn] = e4m3x2_to_h2(R.bs[u][tn] >> (16 * c));
 #pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<16>::run(af, bf[tn], acc[tm][tn]);
+        for (int t = 0; t < 4; ++t) {
+          h8_t bf[C::TN];
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) bf[tn] = dequant8(R.bq[u][tn][4 * c + t], scale_pair(bsp[tn], t >> 1));
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm) {
+            const h8_t af = dequant8(R.aq[u][tm][4 * c + t], scale_pair(asp[tm], t >> 1));
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<16>::run(af, bf[tn], acc[tm][tn]);
+          }
         }
       }
       // the slot's reload stays after its last reads (old and new contents
       // share registers; no copies that would wait on the load)
       __builtin_amdgcn_sched_barrier(0);
-      const int i = i0 + u + C::D;
-      const int unit = C::unit(wave, i, per_wave);
-      kreg_load<C>(R, u, u_lo + unit, i < per_wave && unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+      const int unit = wave + (i0 + u + C::D) * C::KS;
+      kreg_load<C>(R, u, u_lo + unit, unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
     }
   }
   // K-group sum: wave w's partial tile at red[w][.], element (tm, tn, lane, j)
@@ -1306,12 +1347,11 @@ typedef Cfg<256, 256, 2, 4, 32, 128, 4> CfgTile256w8;   // large: 8 waves of 128
 typedef Cfg<256, 256, 2, 2, 32, 128, 4, 4> CfgTile256il; // large, MFMA/VALU interleave hint
 typedef Cfg<128, 128, 2, 2, 32, 128, 4, 4, 1, 2> CfgTile128il;  // mid-large, interleave hint
 typedef Cfg<64, 64, 1, 1, 32, 256, 2, 0, 4, 4> CfgTile64k4;  // mid: 4 K-groups of one 64x64 wave
-// register-streamed K-group tiles: 8 or 16 waves, 3 units in flight per wave
-typedef KCfg<16, 16, 8, 3, 4, 1> KReg16x16;
-typedef KCfg<32, 16, 16, 3, 4> KReg32x16;
-typedef KCfg<64, 16, 16, 3, 4> KReg64x16;
-typedef KCfg<32, 32, 8, 3, 4, 1> KReg32x32;
-typedef KCfg<64, 32, 8, 3, 2> KReg64x32;
+// register-streamed K-group tiles: 4 waves, 2 or 3 units in flight per wave
+typedef KCfg<16, 16, 4, 3, 4> KReg16x16;
+typedef KCfg<32, 16, 4, 3, 4> KReg32x16;
+typedef KCfg<32, 32, 4, 3, 2> KReg32x32;
+typedef KCfg<64, 32, 4, 2, 2> KReg64x32;
 // MXFP4 tiles (E8M0 scale per 32 elements, scaled FP4 MFMA)
 typedef Cfg<256, 256, 2, 2, 32, 256, 2, 0, 1, 1, 32> CfgMx256;      // 4 waves x 128x128, 136 KB LDS
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx128;      // 4 waves x 64x64, 68 KB (split-K)
@@ -1343,11 +1383,10 @@ static const PlanKind kKinds[] = {
     {"tile256x256il_mfma32", 256, 256, 128, false},
     {"tile128x128il_mfma32", 128, 128, 128, true},
     {"tile64x64k4_mfma32", 64, 64, 256, true},
-    {"kreg16x16_mfma16", 16, 16, 128, true, true, false, KReg16x16::KS},
-    {"kreg32x16_mfma16", 32, 16, 128, true, true, false, KReg32x16::KS},
-    {"kreg64x16_mfma16", 64, 16, 128, true, true, false, KReg64x16::KS},
-    {"kreg32x32_mfma16", 32, 32, 128, true, true, false, KReg32x32::KS},
-    {"kreg64x32_mfma16", 64, 32, 128, true, true, false, KReg64x32::KS},
+    {"kreg16x16_mfma16", 16, 16, 256, true, true, false, KReg16x16::KS},
+    {"kreg32x16_mfma16", 32, 16, 256, true, true, false, KReg32x16::KS},
+    {"kreg32x32_mfma16", 32, 32, 256, true, true, false, KReg32x32::KS},
+    {"kreg64x32_mfma16", 64, 32, 256, true, true, false, KReg64x32::KS},
 };
 static const PlanKind kMxKinds[] = {
     {"mx256x256_fp4mfma", 256, 256, 256, false, false, true},
@@ -1375,11 +1414,11 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
     if (forced > 0) {
       s = forced;
     } else if (k.kreg) {
-      // register K-group tiles split K across work-groups (up to 4 ways)
-      // only while there are at most a quarter as many tiles as CUs (cold
-      // sweeps: 16 x 768 x 6144 gains ~1 us, larger grids lose), and keep
-      // at least one K unit per wave in every split
-      s = tiles * 4 <= kCUs ? (kCUs / tiles < 4 ? kCUs / tiles : 4) : 1;
+      // register K-group tiles split K in two only while there are at most a
+      // quarter as many tiles as CUs (cold sweeps: 16 x 768 x 6144 gains
+      // ~0.3 us; 3 or 4 splits, or 2 on larger grids, lose), keeping at
+      // least one K unit per wave in every split
+      s = tiles * 4 <= kCUs ? 2 : 1;
       if (s > nk / k.ks) s = nk / k.ks;
     } else if (k.bk == 256 && !k.mx) {
       // K-group tiles: about 192 work-groups (three quarters of the CUs, one
@@ -1407,18 +1446,18 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
 }
 
 // Plan choice, from cold sweeps on MI355X of the pages' shapes (K = 6144,
-// N = 768 / 2048 / 6144): up to M = 256, the register-streamed K-group tile
-// (16 waves per work-group, no split-K), the smallest of 16x16, 32x16, 32x32,
-// 64x32 that needs at most one work-group per CU; above that, 64x64 K-group
-// tiles (split-K while there are fewer than 192 of them) up to the point
-// where 256x256 tiles fill the CUs twice.
+// N = 768 / 2048 / 6144): up to M = 512, the register-streamed K-group tile
+// (4 waves per work-group), the smallest of 16x16, 32x16, 32x32, 64x32 that
+// needs at most one work-group per CU; above that, 64x64 K-group tiles
+// (split-K while there are fewer than 192 of them) up to the point where
+// 256x256 tiles fill the CUs twice.
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   int kind = -1;
   int forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (M <= 256) {
-    static const int kreg_kinds[] = {10, 11, 13, 14};  // 16x16, 32x16, 32x32, 64x32
+  if (M <= 512) {
+    static const int kreg_kinds[] = {10, 11, 12, 13};  // 16x16, 32x16, 32x32, 64x32
     for (int kk : kreg_kinds) {
       const PlanKind& k = kKinds[kk];
       if (((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) <= kCUs) {
@@ -1481,9 +1520,8 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
     case 8: launch_one<CfgTile128il, true>(pl, p, stream); break;
     case 10: launch_kreg<KReg16x16>(pl, p, stream); break;
     case 11: launch_kreg<KReg32x16>(pl, p, stream); break;
-    case 12: launch_kreg<KReg64x16>(pl, p, stream); break;
-    case 13: launch_kreg<KReg32x32>(pl, p, stream); break;
-    case 14: launch_kreg<KReg64x32>(pl, p, stream); break;
+    case 12: launch_kreg<KReg32x32>(pl, p, stream); break;
+    case 13: launch_kreg<KReg64x32>(pl, p, stream); break;
     default: launch_one<CfgTile64k4, true>(pl, p, stream); break;
   }
   return hipGetLastError();

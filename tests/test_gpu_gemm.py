@@ -171,7 +171,7 @@ def test_split_k_workspace_reuse_and_counters_return_to_zero(monkeypatch):
     # (auto plans: the K-group and register tiles, and the skinny split-K
     # tile forced for M = 16 and 64);
     # afterwards every arrival counter is back at zero
-    shapes = [(16, 768, 6144, "3"), (512, 768, 6144, None), (64, 2048, 6144, "4"), (300, 384, 1024, None),
+    shapes = [(16, 768, 6144, "3"), (1024, 256, 6144, None), (64, 2048, 6144, "4"), (300, 384, 1024, "11,3"),
               (16, 768, 6144, None), (32, 768, 6144, "10,2"), (16, 768, 6144, "3")]
     need = 0
     for (M, N, K, forced) in shapes:
@@ -201,10 +201,10 @@ def test_split_k_workspace_reuse_and_counters_return_to_zero(monkeypatch):
 
 
 def test_graph_capture_replays_match_eager():
-    # register K-group, split-K and single-pass plans captured in one HIP
-    # graph (M = 512 splits K in two); each replay,
+    # register K-group (M = 16 splits K in two), split-K K-group (M = 1024,
+    # N = 256) and single-pass plans captured in one HIP graph; each replay,
     # with eager work and synchronisation in between, must equal the eager run
-    cases = [(16, 768, 6144), (512, 768, 6144), (256, 768, 6144), (2048, 2048, 512)]
+    cases = [(16, 768, 6144), (512, 768, 6144), (1024, 256, 6144), (256, 768, 6144), (2048, 2048, 512)]
     ins, outs, eager = [], [], []
     for (M, N, K) in cases:
         a, b = synth.random_codes(M + 5, M, K), synth.random_codes(N + 5, N, K)
@@ -260,3 +260,26 @@ def test_every_plan_kind_forced(monkeypatch):
             np.testing.assert_array_equal(bits(d2), bits(d), err_msg=f"plan {plan} splits {splits} rerun")
     monkeypatch.delenv("NVFP4_PLAN")
     assert len(seen) >= 6
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 200, 1536), (16, 768, 6144), (1, 17, 256)])
+def test_register_tiles_split_k_forced(monkeypatch, M, N, K):
+    # the register-streamed tiles (128- and 256-element K units) with split-K
+    # forced on ragged shapes: partial rows and columns, K of one unit
+    a, b = synth.random_codes(M + 101, M, K), synth.random_codes(N + 102, N, K)
+    asf = synth.random_scale_bytes(103, M, K, lo=0x28, hi=0x48)
+    bsf = synth.random_scale_bytes(104, N, K, lo=0x28, hi=0x48)
+    at, asft, bt, bsft = dev(a), dev(asf), dev(b), dev(bsf)
+    seen = set()
+    for kind in range(10, 16):   # past the last kind the plan falls back to auto
+        for splits in (1, 2, 3):
+            monkeypatch.setenv("NVFP4_PLAN", f"{kind},{splits}")
+            key = (nv.nvfp4_gemm_plan(M, N, K), nv.nvfp4_gemm_workspace_size(M, N, K))
+            if not key[0].startswith("kreg") or key in seen:
+                continue
+            seen.add(key)
+            say("register tile", M, N, K, kind, splits, key)
+            d = gpu_gemm(at, asft, bt, bsft, scalar(0.5), M, N, K, d_fill=0x7FC1)
+            check_gemm(bits(d), a, asf, b, bsf, np.float32(0.5), f"{key} splits {splits}")
+    monkeypatch.delenv("NVFP4_PLAN")
+    assert len(seen) >= (4 if K == 256 else 11)
