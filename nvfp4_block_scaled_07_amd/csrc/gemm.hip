@@ -903,6 +903,23 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_grouped_a16(GroupedLaunch p)
   }
 }
 
+// Whole-line operand loads: two 16-byte loads per lane cover a 16-row block of
+// one 256-K unit (128 bytes per row) as 8 whole lines each, lane l reading row
+// l % 8 (words 0..3) and row 8 + l % 8 (words 4..7), chunk l / 8 of each.
+// Exchange with the lane 8 away in the same row of 16 so that lane 16 g + r
+// holds row r, chunk 2 g in words 0..3 and chunk 2 g + 1 in words 4..7: the
+// 16x16x32 MFMA operand layout, with K permuted the same way for A and B.
+__device__ __forceinline__ void kreg_exchange(uint32_t (&w)[8], bool lo8) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t p = w[j], q = w[4 + j];
+    const uint32_t give = lo8 ? q : p;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0x128, 0xF, 0xF, false);  // row_ror:8
+    w[j] = lo8 ? p : recv;
+    w[4 + j] = lo8 ? recv : q;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Grouped GEMM streaming B through registers.  Every B element is used by
 // exactly one wave, so B skips LDS: each lane loads its own 16-byte code
@@ -936,8 +953,9 @@ struct GRegs {
 // Loads of stage kt into register slot u.  Always the same instructions (so
 // the compiler can count outstanding loads exactly); a dead stage (live ==
 // false, past the end of K) uses out-of-range offsets, which return zero
-// without a memory access.
-template <class C, int D>
+// without a memory access.  With one scale word per 16-row block (WHOLE_LINES)
+// only the first sub-step's scale offset is loaded.
+template <class C, int D, bool WHOLE_LINES>
 __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const rsrc_t& rb, const rsrc_t& rbs,
                                         const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
                                         uint32_t b_step, uint32_t bs_step, const rsrc_t& ra, const rsrc_t& ras,
@@ -949,7 +967,8 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
     for (int s = 0; s < C::kSub; ++s) {
       R.bq[u][tn][s] = __builtin_bit_cast(
           u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn][s] : kOut, kt * b_step, 0));
-      R.bs[u][tn][s] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][s] : kOut, kt * bs_step, 0);
+      if (!WHOLE_LINES || s == 0)
+        R.bs[u][tn][s] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][s] : kOut, kt * bs_step, 0);
     }
   typedef typename GRegs<C, D>::AQ AQ;
   if constexpr (GRegs<C, D>::kAP == 1)
@@ -962,13 +981,20 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 }
 
 // PACKED: B (codes and scales) in the stage-contiguous layout written by
-// k_pack_b (each stage of a 256-row slab is one block; rows past N are zero).
+// k_pack_b (each stage of a 256-row slab is one block; rows past N are zero);
+// every load instruction reads 1 KB in lane order, and lane 16 g + r holds
+// chunks g and 4 + g of row r.  Unpacked `[E][N][K/2]` weights are read in
+// whole 128-byte lines as in the register K-group tile: sub-step s loads rows
+// 8 s + lane % 8 of each 16-row block, chunk lane / 8, and one DPP rotation
+// gives lane 16 g + r chunks 2 g and 2 g + 1 of row r, whose four scales are
+// one word.
 template <class C, int D, bool PACKED>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_grouped_reg(
     GroupedLaunch p) {
   static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
   static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
   static_assert(C::BM * C::CH <= C::kThreads, "one A chunk per thread");
+  static_assert(PACKED || (C::kSub == 2 && C::KG == 4), "whole-line loads pair the two sub-steps of a 256-K stage");
   __shared__ __attribute__((aligned(16))) SmemGR<C> sm;
   const int tiles_n = (int)((p.N + C::BN - 1) / C::BN);
   const int L = xcd_remap(blockIdx.x, tiles_n * p.E);
@@ -1012,13 +1038,18 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     const int row = wn * C::kWN + tn * C::MF + r_in;
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
-      const int c = C::KG * s + g;
-      uint32_t off = (uint32_t)(row * b_ld + c * 16);
-      if constexpr (PACKED) off = (uint32_t)(((wn * C::TN + tn) * C::kSub + s) * 64 + lane) * 16;  // lane order
-      vb[tn][s] = row < b_rows ? off : 0x80000000u;
-      vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * (c >> 1)) : 0x80000000u;
+      if constexpr (PACKED) {
+        const int c = C::KG * s + g;
+        vb[tn][s] = row < b_rows ? (uint32_t)(((wn * C::TN + tn) * C::kSub + s) * 64 + lane) * 16 : 0x80000000u;
+        vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * (c >> 1)) : 0x80000000u;
+      } else {
+        const int lrow = wn * C::kWN + tn * C::MF + 8 * s + (lane & 7);
+        vb[tn][s] = lrow < b_rows ? (uint32_t)(lrow * b_ld + 16 * (lane >> 3)) : 0x80000000u;
+        vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * g) : 0x80000000u;
+      }
     }
   }
+  const bool lo8 = (lane & 8) == 0;
   typedef GRegs<C, D> RT;
   // this thread's part (ah of kAP) of A code chunk ac of row ar
   const int q = threadIdx.x / RT::kAP, ah = threadIdx.x % RT::kAP, ar = q / C::CH, ac = q % C::CH;
@@ -1038,7 +1069,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     __syncthreads();  // the previous row chunk is done with both A tiles
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      gr_load<C, D>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
+      gr_load<C, D, !PACKED>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
     for (int i0 = 0; i0 < n; i0 += D) {
@@ -1059,12 +1090,24 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // LDS-only barrier: a __syncthreads() fence would also wait for the
           // prefetched loads (loads and stores share one counter)
           lds_barrier();
+          if constexpr (!PACKED) {
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn) {
+              uint32_t w[8];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) { w[j] = R.bq[u][tn][0][j]; w[4 + j] = R.bq[u][tn][1][j]; }
+              kreg_exchange(w, lo8);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) { R.bq[u][tn][0][j] = w[j]; R.bq[u][tn][1][j] = w[4 + j]; }
+            }
+          }
 #pragma unroll
           for (int s = 0; s < C::kSub; ++s) {
-            const int c = C::KG * s + g;
+            const int c = PACKED ? C::KG * s + g : 2 * g + s;
             h2_t bsp[C::TN];
 #pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn) bsp[tn] = e4m3x2_to_h2(R.bs[u][tn][s] >> (16 * (c & 1)));
+            for (int tn = 0; tn < C::TN; ++tn)
+              bsp[tn] = PACKED ? e4m3x2_to_h2(R.bs[u][tn][s] >> (16 * (c & 1))) : e4m3x2_to_h2(R.bs[u][tn][0] >> (16 * s));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               if constexpr (C::TM <= 2) {
@@ -1099,7 +1142,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
           __builtin_amdgcn_sched_barrier(0);
-          gr_load<C, D>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
+          gr_load<C, D, !PACKED>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
         }
       }
     }
@@ -1176,21 +1219,6 @@ __device__ __forceinline__ void kreg_load(KRegs<C>& R, int u, int unit, bool liv
       for (int j = 0; j < 4; ++j) R.bq[u][tn][4 * h + j] = v[j];
     }
     R.bs[u][tn] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn] : kOut, sso, 0);
-  }
-}
-
-// After the two loads a lane holds row l % 8 (words 0..3) and row 8 + l % 8
-// (words 4..7), chunk l / 8 of each.  Exchange with the lane 8 away in the
-// same row of 16 so that lane 16 g + r holds row r, chunk 2 g in words 0..3
-// and chunk 2 g + 1 in words 4..7.
-__device__ __forceinline__ void kreg_exchange(uint32_t (&w)[8], bool lo8) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t p = w[j], q = w[4 + j];
-    const uint32_t give = lo8 ? q : p;
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0x128, 0xF, 0xF, false);  // row_ror:8
-    w[j] = lo8 ? p : recv;
-    w[4 + j] = lo8 ? recv : q;
   }
 }
 
