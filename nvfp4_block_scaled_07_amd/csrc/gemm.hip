@@ -1380,6 +1380,9 @@ typedef KCfg<16, 16, 4, 3, 4> KReg16x16;
 typedef KCfg<32, 16, 4, 3, 4> KReg32x16;
 typedef KCfg<32, 32, 4, 3, 2> KReg32x32;
 typedef KCfg<64, 32, 4, 2, 2> KReg64x32;
+// large M: 256 K per stage (each row's codes one 128-byte line), 2 stages
+typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2> CfgTile256w8k256;  // 8 waves of 128x64
+typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2> CfgTile128k256;    // 4 waves of 64x64
 // MXFP4 tiles (E8M0 scale per 32 elements, scaled FP4 MFMA)
 typedef Cfg<256, 256, 2, 2, 32, 256, 2, 0, 1, 1, 32> CfgMx256;      // 4 waves x 128x128, 136 KB LDS
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx128;      // 4 waves x 64x64, 68 KB (split-K)
@@ -1398,7 +1401,7 @@ struct PlanKind {
   bool splitk;
   bool kreg;  // register-streamed K-group kernel
   bool mx;    // MXFP4 tile
-  int ks;     // waves (K-groups) of a register-streamed tile
+  int ks;     // K-groups (waves) of a register-streamed or K-group LDS tile
 };
 static const PlanKind kKinds[] = {
     {"tile256x256_mfma32", 256, 256, 128, false},
@@ -1410,11 +1413,13 @@ static const PlanKind kKinds[] = {
     {"tile256x256w8_mfma32", 256, 256, 128, false},
     {"tile256x256il_mfma32", 256, 256, 128, false},
     {"tile128x128il_mfma32", 128, 128, 128, true},
-    {"tile64x64k4_mfma32", 64, 64, 256, true},
+    {"tile64x64k4_mfma32", 64, 64, 256, true, false, false, 4},
     {"kreg16x16_mfma16", 16, 16, 256, true, true, false, KReg16x16::KS},
     {"kreg32x16_mfma16", 32, 16, 256, true, true, false, KReg32x16::KS},
     {"kreg32x32_mfma16", 32, 32, 256, true, true, false, KReg32x32::KS},
     {"kreg64x32_mfma16", 64, 32, 256, true, true, false, KReg64x32::KS},
+    {"tile256x256w8k256_mfma32", 256, 256, 256, false},
+    {"tile128x128k256_mfma32", 128, 128, 256, true},
 };
 static const PlanKind kMxKinds[] = {
     {"mx256x256_fp4mfma", 256, 256, 256, false, false, true},
@@ -1448,7 +1453,7 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
       // least one K unit per wave in every split
       s = tiles * 4 <= kCUs ? 2 : 1;
       if (s > nk / k.ks) s = nk / k.ks;
-    } else if (k.bk == 256 && !k.mx) {
+    } else if (k.ks > 1) {
       // K-group tiles: about 192 work-groups (three quarters of the CUs, one
       // work-group each) measured best; more splits cost more in the reduction
       // than they gain in occupancy
@@ -1473,17 +1478,20 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
   }
 }
 
-// Plan choice, from cold sweeps on MI355X of the pages' shapes (K = 6144,
-// N = 768 / 2048 / 6144): up to M = 512, the register-streamed K-group tile
-// (4 waves per work-group), the smallest of 16x16, 32x16, 32x32, 64x32 that
-// needs at most one work-group per CU; above that, 64x64 K-group tiles
-// (split-K while there are fewer than 192 of them) up to the point where
-// 256x256 tiles fill the CUs twice.
+// Plan choice, from sweeps on MI355X of the pages' shapes (K = 6144,
+// N = 768 / 2048 / 6144; cold below M = 4096, warm above): up to M = 512,
+// the register-streamed K-group tile (4 waves per work-group), the smallest
+// of 16x16, 32x16, 32x32, 64x32 that needs at most one work-group per CU;
+// above that, 64x64 K-group tiles (split-K while there are fewer than 192 of
+// them) until 128x128 tiles fill the CUs three times, then 128x128 tiles,
+// and 256x256 tiles of 8 waves once those fill the CUs twice (both staging
+// 256 K per stage: whole 128-byte lines per row).
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   int kind = -1;
   int forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (M <= 512) {
     static const int kreg_kinds[] = {10, 11, 12, 13};  // 16x16, 32x16, 32x32, 64x32
     for (int kk : kreg_kinds) {
@@ -1497,7 +1505,8 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   if (kind < 0) {
     if (M <= 32) kind = 3;
     else if (M <= 64) kind = 4;
-    else if (t256 >= 2 * kCUs) kind = 0;
+    else if (t256 >= 2 * kCUs) kind = 14;
+    else if (t128 >= 3 * kCUs) kind = 15;
     else kind = 9;
   }
   // NVFP4_PLAN=<kind>[,<splits>] forces a plan (tuning sweeps only)
@@ -1550,6 +1559,8 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
     case 11: launch_kreg<KReg32x16>(pl, p, stream); break;
     case 12: launch_kreg<KReg32x32>(pl, p, stream); break;
     case 13: launch_kreg<KReg64x32>(pl, p, stream); break;
+    case 14: launch_one<CfgTile256w8k256, false>(pl, p, stream); break;
+    case 15: launch_one<CfgTile128k256, true>(pl, p, stream); break;
     default: launch_one<CfgTile64k4, true>(pl, p, stream); break;
   }
   return hipGetLastError();
