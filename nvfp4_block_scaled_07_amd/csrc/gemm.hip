@@ -1171,10 +1171,20 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 // scale word is bytes 4 g .. 4 g + 3 of the row's 16 unit scales.  MFMA t of
 // chunk c multiplies elements 8 t .. 8 t + 7 of that chunk, the same K set
 // for A and B.
+//
+// MX tiles (MXFP4: one E8M0 scale per 32 elements) use the same loads and
+// exchange and no dequantisation: chunk c of every lane (32 codes, one MX
+// block) is the lane's operand of one v_mfma_scale_f32_16x16x128_f8f6f4
+// (lane 16 g + r: row r, K block g of the MFMA; its scale operand's low byte
+// applies to that row and block; the output layout is that of the 16x16 f16
+// MFMA).  Lane 16 g + r loads scale word g / 2 of the row's 8 unit scales;
+// bytes 2 g and 2 g + 1 of the unit are those of its chunks.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int KS_, int D_, int OCC_>
+template <int BM_, int BN_, int KS_, int D_, int OCC_, int MX_ = 0>
 struct KCfg {
   static constexpr int BM = BM_, BN = BN_, KS = KS_, D = D_, OCC = OCC_;
+  static constexpr bool kMx = MX_ != 0;
+  static constexpr int SBLK = kMx ? 32 : 16;        // elements per scale
   static constexpr int TM = BM / 16, TN = BN / 16;
   static constexpr int kThreads = KS * 64;
   static constexpr int kTileFloats = BM * BN;        // one wave's partial tile
@@ -1199,7 +1209,7 @@ __device__ __forceinline__ void kreg_load(KRegs<C>& R, int u, int unit, bool liv
                                           const uint32_t (&va)[C::TM][2], const uint32_t (&vas)[C::TM],
                                           const uint32_t (&vb)[C::TN][2], const uint32_t (&vbs)[C::TN]) {
   constexpr uint32_t kOut = 0x80000000u;
-  const int so = unit * (C::kUnit / 2), sso = unit * (C::kUnit / 16);
+  const int so = unit * (C::kUnit / 2), sso = unit * (C::kUnit / C::SBLK);
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
 #pragma unroll
@@ -1231,7 +1241,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   const int L = xcd_remap(blockIdx.x, (int)(p.tiles_m * p.tiles_n) * S);
   const int tile = L / S, z = L % S;
   const int64_t m0 = (int64_t)(tile / tiles_n) * C::BM, n0 = (int64_t)(tile % tiles_n) * C::BN;
-  const int64_t ld = p.K / 2, lds = p.K / 16;
+  const int64_t ld = p.K / 2, lds = p.K / C::SBLK;
   const int rows_a = (int)min<int64_t>(C::BM, p.M - m0), rows_b = (int)min<int64_t>(C::BN, p.N - n0);
   const rsrc_t ra = make_rsrc(p.a + m0 * ld, (uint32_t)(rows_a * ld));
   const rsrc_t ras = make_rsrc(p.a_sf + m0 * lds, (uint32_t)(rows_a * lds));
@@ -1240,7 +1250,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r_in = lane & 15, g = lane >> 4;
   // code offsets: rows lane % 8 and 8 + lane % 8 of each 16-row block, bytes
-  // 16 (lane / 8) of the unit; scale word g of row r_in
+  // 16 (lane / 8) of the unit; scale word g (MX: g / 2) of row r_in
+  const int sw = C::kMx ? 4 * (g >> 1) : 4 * g;
   uint32_t va[C::TM][2], vas[C::TM], vb[C::TN][2], vbs[C::TN];
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
@@ -1250,7 +1261,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       va[tm][h] = r < rows_a ? (uint32_t)(r * ld + 16 * (lane >> 3)) : 0x80000000u;
     }
     const int r = tm * 16 + r_in;
-    vas[tm] = r < rows_a ? (uint32_t)(r * lds + 4 * g) : 0x80000000u;
+    vas[tm] = r < rows_a ? (uint32_t)(r * lds + sw) : 0x80000000u;
   }
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn) {
@@ -1260,7 +1271,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       vb[tn][h] = r < rows_b ? (uint32_t)(r * ld + 16 * (lane >> 3)) : 0x80000000u;
     }
     const int r = tn * 16 + r_in;
-    vbs[tn] = r < rows_b ? (uint32_t)(r * lds + 4 * g) : 0x80000000u;
+    vbs[tn] = r < rows_b ? (uint32_t)(r * lds + sw) : 0x80000000u;
   }
   // this work-group's K units [u_lo, u_hi): all of K, or split z of S
   const int nu_all = (int)(p.K / C::kUnit);
@@ -1290,6 +1301,31 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       for (int tm = 0; tm < C::TM; ++tm) kreg_exchange(R.aq[u][tm], lo8);
 #pragma unroll
       for (int tn = 0; tn < C::TN; ++tn) kreg_exchange(R.bq[u][tn], lo8);
+      if constexpr (C::kMx) {
+        typedef int v8i_t __attribute__((ext_vector_type(8)));
+        const int ssh = 16 * (g & 1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          v8i_t bv[C::TN];
+          int sb[C::TN];
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) {
+            const uint32_t* w = R.bq[u][tn] + 4 * c;
+            bv[tn] = v8i_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+            sb[tn] = (int)(R.bs[u][tn] >> (ssh + 8 * c));
+          }
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm) {
+            const uint32_t* w = R.aq[u][tm] + 4 * c;
+            const v8i_t av = v8i_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+            const int sa = (int)(R.as[u][tm] >> (ssh + 8 * c));
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn)
+              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[tn], acc[tm][tn], 4, 4, 0, sa, 0,
+                                                                             sb[tn]);
+          }
+        }
+      } else {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         h2_t asp[C::TM], bsp[C::TN];
@@ -1309,6 +1345,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
             for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<16>::run(af, bf[tn], acc[tm][tn]);
           }
         }
+      }
       }
       // the slot's reload stays after its last reads (old and new contents
       // share registers; no copies that would wait on the load)
@@ -1380,6 +1417,11 @@ typedef KCfg<16, 16, 4, 3, 4> KReg16x16;
 typedef KCfg<32, 16, 4, 3, 4> KReg32x16;
 typedef KCfg<32, 32, 4, 3, 2> KReg32x32;
 typedef KCfg<64, 32, 4, 2, 2> KReg64x32;
+// MXFP4 register-streamed tiles (scaled FP4 MFMA, no dequantisation)
+typedef KCfg<16, 16, 4, 3, 4, 1> MxReg16x16;
+typedef KCfg<32, 16, 4, 3, 4, 1> MxReg32x16;
+typedef KCfg<32, 32, 4, 3, 2, 1> MxReg32x32;
+typedef KCfg<64, 32, 4, 2, 2, 1> MxReg64x32;
 // large M: 256 K per stage (each row's codes one 128-byte line), 2 stages
 typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2> CfgTile256w8k256;  // 8 waves of 128x64
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2> CfgTile128k256;    // 4 waves of 64x64
@@ -1427,6 +1469,10 @@ static const PlanKind kMxKinds[] = {
     {"mx64x64_fp4mfma", 64, 64, 256, true, false, true},
     {"mx256x256w8_fp4mfma", 256, 256, 256, false, false, true},
     {"mx256x256w8s4_fp4mfma", 256, 256, 128, false, false, true},
+    {"mxreg16x16_fp4mfma", 16, 16, 256, true, true, true, MxReg16x16::KS},
+    {"mxreg32x16_fp4mfma", 32, 16, 256, true, true, true, MxReg32x16::KS},
+    {"mxreg32x32_fp4mfma", 32, 32, 256, true, true, true, MxReg32x32::KS},
+    {"mxreg64x32_fp4mfma", 64, 32, 256, true, true, true, MxReg64x32::KS},
 };
 static constexpr int kNumMxKinds = (int)(sizeof(kMxKinds) / sizeof(kMxKinds[0]));
 static constexpr int kNumKinds = (int)(sizeof(kKinds) / sizeof(kKinds[0]));
@@ -1458,6 +1504,11 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
       // work-group each) measured best; more splits cost more in the reduction
       // than they gain in occupancy
       s = (kK4Blocks + tiles / 2) / tiles;
+    } else if (k.mx) {
+      // MX LDS tiles: at most one work-group per CU (192 tiles of 64x64 at
+      // 1024 x 768 x 6144: 20.8 us unsplit against 25.4 us split in two)
+      s = tiles * 2 <= kCUs ? kCUs / tiles : 1;
+      if (s > nk / kMinStagesPerSplit) s = nk / kMinStagesPerSplit;
     } else {
       s = (kTargetBlocks + tiles - 1) / tiles;
       int64_t cap = kMaxPartialBytesPerTile / ((int64_t)k.bm * k.bn * 4);
@@ -1566,16 +1617,26 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// MXFP4 plan, from cold sweeps at K = 6144: 256x256 tiles of 8 waves while
+// MXFP4 plan, from cold sweeps at K = 6144: up to M = 512 the register tile
+// (the same rule as for NVFP4: the smallest of 16x16, 32x16, 32x32, 64x32
+// with at most one work-group per CU); else 256x256 tiles of 8 waves while
 // they fill the CUs, then 128x128 (two work-groups per CU) while those fill
 // them, else 64x64 with split-K up to about 1.5 work-groups per CU.
 // NVFP4_MX_PLAN=<kind>[,<splits>] forces one (tuning sweeps only).
 GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
-  int kind = 2, forced_splits = 0;
+  int kind = -1, forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (t256 >= kCUs) kind = 3;
-  else if (t128 >= kCUs) kind = 1;
+  if (M <= 512) {
+    for (int kk = 5; kk <= 8; ++kk) {  // register tiles 16x16, 32x16, 32x32, 64x32
+      const PlanKind& k = kMxKinds[kk];
+      if (((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) <= kCUs) {
+        kind = kk;
+        break;
+      }
+    }
+  }
+  if (kind < 0) kind = t256 >= kCUs ? 3 : (t128 >= kCUs ? 1 : 2);
   if (const char* env = getenv("NVFP4_MX_PLAN")) {
     int fk = -1, fs = 0;
     if (sscanf(env, "%d,%d", &fk, &fs) >= 1 && fk >= 0 && fk < kNumMxKinds) {
@@ -1604,6 +1665,10 @@ hipError_t launch_mx_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) 
     case 1: launch_one<CfgMx128, true>(pl, p, stream); break;
     case 3: launch_one<CfgMx256w8, false>(pl, p, stream); break;
     case 4: launch_one<CfgMx256w8s4, false>(pl, p, stream); break;
+    case 5: launch_kreg<MxReg16x16>(pl, p, stream); break;
+    case 6: launch_kreg<MxReg32x16>(pl, p, stream); break;
+    case 7: launch_kreg<MxReg32x32>(pl, p, stream); break;
+    case 8: launch_kreg<MxReg64x32>(pl, p, stream); break;
     default: launch_one<CfgMx64, true>(pl, p, stream); break;
   }
   return hipGetLastError();

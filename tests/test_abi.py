@@ -153,8 +153,14 @@ def test_mx_gemm_error_paths_and_queries():
     assert call(M=0, a=None) == 0                                   # empty: success before any check
     assert nv.nvfp4_mx_gemm_plan(16, 768, 100) == "none"
     assert nv.nvfp4_mx_gemm_plan(16384, 6144, 6144).startswith("mx256x256w8")
-    assert nv.nvfp4_mx_gemm_plan(16, 768, 6144).startswith("mx64x64")
-    need = nv.nvfp4_mx_gemm_workspace_size(16, 768, 6144)
-    assert need > 4096 and (need - 4096) % (12 * 64 * 64 * 4) == 0   # split-K partials of 12 tiles
+    assert nv.nvfp4_mx_gemm_plan(16, 768, 6144).startswith("mxreg16x16")
+    assert nv.nvfp4_mx_gemm_plan(512, 768, 6144).startswith("mxreg64x32")
+    assert nv.nvfp4_mx_gemm_plan(1024, 768, 6144).startswith("mx64x64")
+    # 48 register tiles of 16x16 split K in two; 64 LDS tiles of 64x64 (M = 1024,
+    # N = 256) split in four; 192 of them not at all
+    assert nv.nvfp4_mx_gemm_workspace_size(16, 768, 6144) == 4096 + 48 * 2 * 16 * 16 * 4
+    assert nv.nvfp4_mx_gemm_workspace_size(64, 768, 6144) == 0
+    assert nv.nvfp4_mx_gemm_workspace_size(1024, 256, 6144) == 4096 + 64 * 4 * 64 * 64 * 4
+    assert nv.nvfp4_mx_gemm_workspace_size(1024, 768, 6144) == 0
     assert call(M=16, N=768, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
     assert nv.nvfp4_mx_gemm_workspace_size(16384, 6144, 6144) == 0

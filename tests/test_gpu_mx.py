@@ -1,5 +1,5 @@
 """GPU parity of the MXFP4 GEMM (nvfp4_mx_gemm) with the MX oracle, through
-the C ABI: every MX plan forced on ragged shapes, the attention-projection
+the C ABI: every MX plan (LDS-staged and register tiles) forced on ragged shapes, the attention-projection
 sweep and sampled rows of the large shapes with seeded random codes and E8M0
 scales, determinism, and the no-op / error paths that need a device."""
 import numpy as np
@@ -55,7 +55,7 @@ def test_every_mx_plan_forced_on_ragged_shapes(monkeypatch):
         a, asf, b, bsf = _operands(M + N, M, N, K)
         at, asft, bt, bsft = dev(a), dev(asf), dev(b), dev(bsf)
         seen = set()
-        for kind in range(6):   # past the last kind the plan falls back to auto
+        for kind in range(10):   # past the last kind the plan falls back to auto
             for splits in (1, 3):
                 monkeypatch.setenv("NVFP4_MX_PLAN", f"{kind},{splits}")
                 plan = nv.nvfp4_mx_gemm_plan(M, N, K)
