@@ -138,8 +138,12 @@ size_t nvfp4_grouped_workspace_size(int64_t rows, int64_t N, int64_t K, int32_t 
  * 2048 chunks of 16 bytes: chunk c (0..7, K elements 256k + 32c ..) of row r
  * (0..255) is stored at chunk position
  * (((r / 32) * 2 + (r % 32) / 16) * 2 + c / 4) * 64 + (c % 4) * 16 + r % 16,
- * the order in which the kernel's lanes load them.  A scale block is 256 rows
- * of 16 bytes in row order.  All pointers 16-byte aligned.
+ * the order in which the kernel's lanes load them.  A scale block is 1024
+ * words of 4 bytes: word w (0..3, scale bytes 4w .. 4w+3 of the stage) of row
+ * r is stored at word position
+ * ((((r / 32) * 16 + r % 16) * 2 + w % 2) * 4 + ((r % 32) / 16) * 2 + w / 2,
+ * so that each lane's four words are one 16-byte chunk.  All pointers
+ * 16-byte aligned.
  * K % 512 == 0 (ERR_UNSUPPORTED otherwise).  Asynchronous on stream.
  *
  * nvfp4_grouped_gemm_packed: as nvfp4_grouped_gemm with b, b_sf replaced by

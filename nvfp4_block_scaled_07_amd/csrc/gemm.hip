@@ -953,9 +953,10 @@ struct GRegs {
 // Loads of stage kt into register slot u.  Always the same instructions (so
 // the compiler can count outstanding loads exactly); a dead stage (live ==
 // false, past the end of K) uses out-of-range offsets, which return zero
-// without a memory access.  With one scale word per 16-row block (WHOLE_LINES)
-// only the first sub-step's scale offset is loaded.
-template <class C, int D, bool WHOLE_LINES>
+// without a memory access.  Unpacked weights (whole-line loads) need one
+// scale word per 16-row block; packed weights hold a lane's four scale words
+// (both row blocks, both sub-steps) in one 16-byte chunk.
+template <class C, int D, bool PACKED>
 __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const rsrc_t& rb, const rsrc_t& rbs,
                                         const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
                                         uint32_t b_step, uint32_t bs_step, const rsrc_t& ra, const rsrc_t& ras,
@@ -967,9 +968,14 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
     for (int s = 0; s < C::kSub; ++s) {
       R.bq[u][tn][s] = __builtin_bit_cast(
           u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn][s] : kOut, kt * b_step, 0));
-      if (!WHOLE_LINES || s == 0)
-        R.bs[u][tn][s] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][s] : kOut, kt * bs_step, 0);
+      if (!PACKED && s == 0)
+        R.bs[u][tn][0] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][0] : kOut, kt * bs_step, 0);
     }
+  if constexpr (PACKED) {
+    const u4_t w = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbs, live ? vbs[0][0] : kOut,
+                                                                                  kt * bs_step, 0));
+    R.bs[u][0][0] = w[0]; R.bs[u][0][1] = w[1]; R.bs[u][1][0] = w[2]; R.bs[u][1][1] = w[3];
+  }
   typedef typename GRegs<C, D>::AQ AQ;
   if constexpr (GRegs<C, D>::kAP == 1)
     R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va : kOut, kt * C::RB, 0));
@@ -982,8 +988,9 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 
 // PACKED: B (codes and scales) in the stage-contiguous layout written by
 // k_pack_b (each stage of a 256-row slab is one block; rows past N are zero);
-// every load instruction reads 1 KB in lane order, and lane 16 g + r holds
-// chunks g and 4 + g of row r.  Unpacked `[E][N][K/2]` weights are read in
+// every code load instruction reads 1 KB in lane order, lane 16 g + r holds
+// chunks g and 4 + g of row r, and a wave's scale words for the stage are one
+// 512-byte run.  Unpacked `[E][N][K/2]` weights are read in
 // whole 128-byte lines as in the register K-group tile: sub-step s loads rows
 // 8 s + lane % 8 of each 16-row block, chunk lane / 8, and one DPP rotation
 // gives lane 16 g + r chunks 2 g and 2 g + 1 of row r, whose four scales are
@@ -995,6 +1002,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
   static_assert(C::BM * C::CH <= C::kThreads, "one A chunk per thread");
   static_assert(PACKED || (C::kSub == 2 && C::KG == 4), "whole-line loads pair the two sub-steps of a 256-K stage");
+  static_assert(!PACKED || (C::TN == 2 && C::kSub == 2 && C::MF == 16 && C::kWN == 32), "packed scale chunk layout");
   __shared__ __attribute__((aligned(16))) SmemGR<C> sm;
   const int tiles_n = (int)((p.N + C::BN - 1) / C::BN);
   const int L = xcd_remap(blockIdx.x, tiles_n * p.E);
@@ -1039,9 +1047,10 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
       if constexpr (PACKED) {
-        const int c = C::KG * s + g;
+        // rows past N are zero in the packed block; the scale chunk of lane
+        // 16 g + r_in is (wn * 16 + r_in) * 2 + g / 2
         vb[tn][s] = row < b_rows ? (uint32_t)(((wn * C::TN + tn) * C::kSub + s) * 64 + lane) * 16 : 0x80000000u;
-        vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * (c >> 1)) : 0x80000000u;
+        vbs[tn][s] = (uint32_t)(((wn * 16 + r_in) * 2 + (g >> 1)) * 16);
       } else {
         const int lrow = wn * C::kWN + tn * C::MF + 8 * s + (lane & 7);
         vb[tn][s] = lrow < b_rows ? (uint32_t)(lrow * b_ld + 16 * (lane >> 3)) : 0x80000000u;
@@ -1069,7 +1078,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     __syncthreads();  // the previous row chunk is done with both A tiles
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      gr_load<C, D, !PACKED>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
+      gr_load<C, D, PACKED>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
     for (int i0 = 0; i0 < n; i0 += D) {
@@ -1142,7 +1151,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
           __builtin_amdgcn_sched_barrier(0);
-          gr_load<C, D, !PACKED>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
+          gr_load<C, D, PACKED>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
         }
       }
     }
@@ -1721,14 +1730,27 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
 // block of 256 rows x 128 code bytes (and 256 x 16 scale bytes), rows past N
 // zero.  Inside a code block the 16-byte chunks are in the order the grouped
 // kernel's lanes load them (wave, column block, sub-step, lane), so each load
-// instruction reads 1 KB in one run; scale rows stay in row order.  One
-// 16-byte chunk per thread and step.
+// instruction reads 1 KB in one run; a scale block holds each lane's four
+// scale words in one 16-byte chunk (packed_sf_word).  One 16-byte source chunk
+// per thread and step.
 constexpr int kPackRows = CfgGroupedReg::BN, kPackK = CfgGroupedReg::BK;
+static_assert(CfgGroupedReg64::BN == kPackRows && CfgGroupedReg64::kWN == CfgGroupedReg::kWN &&
+                  CfgGroupedReg64::TN == CfgGroupedReg::TN && CfgGroupedReg64::BK == kPackK,
+              "both packed kernels share one layout");
 
 // position of chunk c (0..7) of row r (0..255) inside a packed code block
 __host__ __device__ constexpr int packed_chunk(int r, int c) {
   typedef CfgGroupedReg G;
   return (((r / G::kWN) * G::TN + (r % G::kWN) / G::MF) * G::kSub + c / G::KG) * 64 + (c % G::KG) * G::MF + r % G::MF;
+}
+
+// word position of scale word w (0..3: bytes 4 w .. 4 w + 3) of row r (0..255)
+// inside a packed scale block: the lane 16 g + r % 16 of wave r / 32 that
+// needs it reads words [row r0, s = 0], [r0, s = 1], [r0 + 16, s = 0],
+// [r0 + 16, s = 1] (r0 = 32 (r / 32) + r % 16, word 2 s + g / 2) as one chunk
+__host__ __device__ constexpr int packed_sf_word(int r, int w) {
+  typedef CfgGroupedReg G;
+  return (((r / G::kWN) * G::MF + r % G::MF) * 2 + w % 2) * 4 + ((r % G::kWN) / G::MF) * 2 + w / 2;
 }
 
 __global__ __launch_bounds__(256) void k_pack_b(const u4_t* __restrict__ b, const u4_t* __restrict__ b_sf, int64_t N,
@@ -1752,8 +1774,13 @@ __global__ __launch_bounds__(256) void k_pack_b(const u4_t* __restrict__ b, cons
     const int64_t e = slab / tiles, row = (slab % tiles) * kPackRows + r;
     u4_t v = {0u, 0u, 0u, 0u};
     if (row < N) v = code ? b[(e * N + row) * ld16 + kst * 8 + c] : b_sf[(e * N + row) * lds16 + kst];
-    if (code) pb[block * (kPackRows * 8) + packed_chunk(r, c)] = v;
-    else psf[qq] = v;
+    if (code) {
+      pb[block * (kPackRows * 8) + packed_chunk(r, c)] = v;
+    } else {
+      uint32_t* sw = (uint32_t*)(psf + block * kPackRows);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sw[packed_sf_word(r, w)] = v[w];
+    }
   }
 }
 
