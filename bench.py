@@ -275,13 +275,17 @@ def grouped_inputs(torch, nv, synth, quantise, dev):
     T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
     tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
     rows = int(off[-1])
-    qa_tok, sfa_tok, gsa = quantise(synth.token_activations(T, K))
+    x32 = synth.token_activations(T, K)
+    qa_tok, sfa_tok, gsa = quantise(x32)
     tok_t = torch.from_numpy(tok).to(dev)
     qa, sfa = qa_tok[tok_t].contiguous(), sfa_tok[tok_t].contiguous()
+    # the same tokens as bf16 activations, for the fused-quantisation call
+    x_bf16 = torch.from_numpy(x32).to(dev).to(torch.bfloat16)
     b = torch.from_numpy(synth.random_codes(g["seed_expert_base"], E * N, K)).to(dev)
     bsf = torch.from_numpy(synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, 0x20, 0x38)).to(dev)
     active = int((np.diff(off) > 0).sum())
-    return dict(rows=rows, N=N, K=K, E=E, qa=qa, sfa=sfa, b=b, bsf=bsf, off=torch.from_numpy(off).to(dev),
+    return dict(rows=rows, N=N, K=K, E=E, T=T, qa=qa, sfa=sfa, b=b, bsf=bsf, off=torch.from_numpy(off).to(dev),
+                x_bf16=x_bf16, tok=tok_t.to(torch.int32), gsa=gsa,
                 alpha=torch.full((E,), 1.0, dtype=torch.float32, device=dev) / gsa,
                 d=torch.empty((rows, N), dtype=torch.int16, device=dev), active=active,
                 rows_per_expert_max=int(np.diff(off).max()),
@@ -481,6 +485,7 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
     # the same call on weights packed once into the stage-contiguous layout
     # (packing is a one-time weight transform, outside the timed region)
     pb, psf = nv.grouped_pack(b, bsf, N, K, E)
+    T, x_bf16, tok_i32, gsa = gi["T"], gi["x_bf16"], gi["tok"], gi["gsa"]
     del b, bsf, gi
     torch.cuda.empty_cache()
     us_p = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_packed(qa, sfa, pb, psf, off_t, alpha, d, rows, N, K,
@@ -489,7 +494,29 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
         us=round(us_p, 2), gbps=round(by / us_p / 1e3, 1), frac_hbm=round(by / us_p / 1e3 / PEAK_HBM_GBPS, 4),
         tflops=round(fl / us_p / 1e6, 2),
         traffic=read_traffic_record(GROUPED_TRAFFIC_RECORD, grouped_call_name(rows, N, K, E)))
-    del pb, psf, qa, sfa, d
+    # the MoE step from bf16 token activations: gather + quantise fused into
+    # the GEMM's A load, against the unfused sequence (quantise kernel on the
+    # tokens, row gather, grouped GEMM) on the same packed weights
+    us_f = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_packed_fused(
+        x_bf16, tok_i32, gsa, pb, psf, off_t, alpha, d, rows, T, N, K, E), 10)
+    x32 = x_bf16.float()
+    q_tok = torch.empty((T, K // 2), dtype=torch.uint8, device=dev)
+    sf_tok = torch.empty((T, K // 16), dtype=torch.uint8, device=dev)
+    tok64 = tok_i32.long()
+
+    def unfused(i):
+        nv.nvfp4_quantize(x32, T, K, gsa, q_tok, sf_tok)
+        torch.index_select(q_tok, 0, tok64, out=qa)
+        torch.index_select(sf_tok, 0, tok64, out=sfa)
+        nv.nvfp4_grouped_gemm_packed(qa, sfa, pb, psf, off_t, alpha, d, rows, N, K, E)
+    us_u = timed(torch, stream, unfused, 10)
+    # weights, bf16 tokens, row tokens, bf16 out, offsets, alphas
+    by_f = by - rows * K * 9 // 16 + T * K * 2 + 4 * rows
+    res["grouped_moe_512tok_256exp_top8"]["fused_quant_packed"] = dict(
+        note="nvfp4_grouped_gemm_packed_fused: bf16 tokens gathered and quantised inside the GEMM",
+        us=round(us_f, 2), gbps=round(by_f / us_f / 1e3, 1), frac_hbm=round(by_f / us_f / 1e3 / PEAK_HBM_GBPS, 4),
+        algorithmic_bytes=by_f, unfused_pipeline_us=round(us_u, 2))
+    del pb, psf, qa, sfa, d, x32, q_tok, sf_tok
     torch.cuda.empty_cache()
 
     # grouped calls with the same rows in every expert, weights >= 512 MB

@@ -158,6 +158,41 @@ nvfp4_status nvfp4_grouped_gemm_packed(const uint8_t* a, const uint8_t* a_sf, co
                                        int32_t* status, void* stream);
 
 /*
+ * Grouped GEMM with the activation quantisation fused into the A load: the
+ * step before the GEMM in an MoE layer (token gather and NVFP4 quantisation
+ * of the activations), done by the GEMM kernel itself instead of a quantise
+ * kernel and a gather.  The pages benchmark the expert GEMM on already
+ * quantised operands ("When a Benchmark Crashes: The Elusive FP4 GEMM
+ * Comparison on Blackwell SM120", section "Why This Message Was Written");
+ * the quantisation rules are those of nvfp4_quantize below.
+ *
+ *   A[i][:] = NVFP4(x[row_token[i]][:], *a_global_scale)   (x[i] if row_token is NULL)
+ *   D = nvfp4_grouped_gemm(A, B, offsets, alpha)
+ *
+ * x: bf16 [T][K] activations (device, 16-byte aligned); bf16 values are
+ * exact fp32 values, so the result equals nvfp4_quantize on their fp32
+ * copy, a row gather and nvfp4_grouped_gemm, bit for bit.  row_token: int32
+ * [rows] device, token of each expert-sorted row, or NULL (then rows <= T).
+ * Tokens outside [0, T) read as zero rows.  a_global_scale: device fp32
+ * encode scale shared by all rows (a static activation scale; NULL = 1.0).
+ * b, b_sf: [E][N][K/2] and [E][N][K/16] (nvfp4_grouped_gemm_fused) or the
+ * buffers of nvfp4_grouped_pack_b (nvfp4_grouped_gemm_packed_fused).
+ * offsets, alpha, d, status: as nvfp4_grouped_gemm; in addition, when the
+ * offsets are valid, *status = -(1 + i) for the first row i whose token lies
+ * outside [0, T).  K % 512 == 0 and T * K * 2 < 2^31 (ERR_UNSUPPORTED
+ * otherwise); no workspace.  Asynchronous on stream.
+ */
+nvfp4_status nvfp4_grouped_gemm_fused(const uint16_t* x, const int32_t* row_token, const float* a_global_scale,
+                                      const uint8_t* b, const uint8_t* b_sf, const int32_t* offsets,
+                                      const float* alpha, uint16_t* d, int64_t rows, int64_t T, int64_t N,
+                                      int64_t K, int32_t E, int32_t* status, void* stream);
+nvfp4_status nvfp4_grouped_gemm_packed_fused(const uint16_t* x, const int32_t* row_token,
+                                             const float* a_global_scale, const uint8_t* packed,
+                                             const uint8_t* packed_sf, const int32_t* offsets, const float* alpha,
+                                             uint16_t* d, int64_t rows, int64_t T, int64_t N, int64_t K, int32_t E,
+                                             int32_t* status, void* stream);
+
+/*
  * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
  * The pages never quantise (their test used random bytes); this follows the
  * block_size 16 and e4m3fn scale format of the pages above with these steps,

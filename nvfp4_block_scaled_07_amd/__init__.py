@@ -35,6 +35,10 @@ SIGNATURES = {
     "nvfp4_grouped_pack_b": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "nvfp4_grouped_gemm_packed": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp,
                                                  _vp]),
+    "nvfp4_grouped_gemm_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                _i32, _vp, _vp]),
+    "nvfp4_grouped_gemm_packed_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                                       _i64, _i32, _vp, _vp]),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_global_scale": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_alpha_from_scales": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
@@ -199,6 +203,27 @@ def nvfp4_grouped_gemm_packed(a, a_sf, packed, packed_sf, offsets, alpha, d, row
     st = lib().nvfp4_grouped_gemm_packed(_ptr(a), _ptr(a_sf), _ptr(packed), _ptr(packed_sf), _ptr(offsets),
                                          _ptr(alpha), _ptr(d), rows, N, K, E, _ptr(status), _stream(stream))
     _check(st, "nvfp4_grouped_gemm_packed")
+    return d
+
+
+def nvfp4_grouped_gemm_fused(x, row_token, a_global_scale, b, b_sf, offsets, alpha, d, rows: int, T: int, N: int,
+                             K: int, E: int, status=None, stream=None):
+    """Grouped GEMM quantising bf16 activations x [T][K] on load: A row i is
+    x[row_token[i]] (x[i] when row_token is None); b, b_sf as nvfp4_grouped_gemm."""
+    st = lib().nvfp4_grouped_gemm_fused(_ptr(x), _ptr(row_token), _ptr(a_global_scale), _ptr(b), _ptr(b_sf),
+                                        _ptr(offsets), _ptr(alpha), _ptr(d), rows, T, N, K, E, _ptr(status),
+                                        _stream(stream))
+    _check(st, "nvfp4_grouped_gemm_fused")
+    return d
+
+
+def nvfp4_grouped_gemm_packed_fused(x, row_token, a_global_scale, packed, packed_sf, offsets, alpha, d, rows: int,
+                                    T: int, N: int, K: int, E: int, status=None, stream=None):
+    """nvfp4_grouped_gemm_fused on weights packed by nvfp4_grouped_pack_b."""
+    st = lib().nvfp4_grouped_gemm_packed_fused(_ptr(x), _ptr(row_token), _ptr(a_global_scale), _ptr(packed),
+                                               _ptr(packed_sf), _ptr(offsets), _ptr(alpha), _ptr(d), rows, T, N, K,
+                                               E, _ptr(status), _stream(stream))
+    _check(st, "nvfp4_grouped_gemm_packed_fused")
     return d
 
 

@@ -173,7 +173,7 @@ size_t nvfp4_grouped_packed_size(int64_t N, int64_t K, int32_t E, size_t* sf_byt
 }
 
 namespace {
-nvfp4_status check_packed_shape(int64_t N, int64_t K, int32_t E) {
+static nvfp4_status check_packed_shape(int64_t N, int64_t K, int32_t E) {
   if (N < 0 || E < 0) return fail(NVFP4_ERR_SHAPE, "N = %lld, E = %d must be >= 0", (long long)N, E);
   nvfp4_status s = check_k(K);
   if (s != NVFP4_OK) return s;
@@ -219,6 +219,59 @@ nvfp4_status nvfp4_grouped_gemm_packed(const uint8_t* a, const uint8_t* a_sf, co
   nvfp4::GroupedLaunch p{a, a_sf, packed, packed_sf, offsets, alpha, d, rows, N, K, E};
   return hip_status(nvfp4::launch_grouped_packed(p, status, (hipStream_t)stream, true),
                     "nvfp4_grouped_gemm_packed launch");
+}
+
+namespace {
+static nvfp4_status grouped_fused(const uint16_t* x, const int32_t* row_token, const float* a_gs, const uint8_t* b,
+                                  const uint8_t* b_sf, const int32_t* offsets, const float* alpha, uint16_t* d,
+                                  int64_t rows, int64_t T, int64_t N, int64_t K, int32_t E, int32_t* status,
+                                  void* stream, bool packed, const char* fn) {
+  if (rows < 0 || T < 0 || N < 0 || E < 0)
+    return fail(NVFP4_ERR_SHAPE, "rows = %lld, T = %lld, N = %lld, E = %d must be >= 0", (long long)rows,
+                (long long)T, (long long)N, E);
+  nvfp4_status s = check_k(K);
+  if (s != NVFP4_OK) return s;
+  if (K % 512) return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: the fused grouped GEMM needs K %% 512 == 0", (long long)K);
+  if (T > 0 && T * K * 2 >= (int64_t(1) << 31))
+    return fail(NVFP4_ERR_UNSUPPORTED, "T * K * 2 = %lld bytes of activations: at most 2^31 - 1 supported",
+                (long long)(T * K * 2));
+  if (!row_token && rows > T)
+    return fail(NVFP4_ERR_SHAPE, "rows = %lld > T = %lld with row_token NULL (row i reads token i)", (long long)rows,
+                (long long)T);
+  if (N > (1ll << 30) || rows > (1ll << 30) || E > 65535)
+    return fail(NVFP4_ERR_UNSUPPORTED, "rows or N above 2^30 (or E > 65535) are not supported");
+  if (!offsets && E > 0) return fail(NVFP4_ERR_NULL, "offsets must be non-NULL");
+  if (!aligned(offsets, 4) || !aligned(status, 4) || !aligned(row_token, 4))
+    return fail(NVFP4_ERR_ALIGN, "offsets, row_token and status must be 4-byte aligned");
+  nvfp4::GroupedLaunch p{nullptr, nullptr, b, b_sf, offsets, alpha, d, rows, N, K, E, x, row_token, a_gs, T};
+  if (E == 0 || N == 0 || rows == 0)
+    return hip_status(nvfp4::launch_grouped_fused(p, packed, status, (hipStream_t)stream, false), fn);
+  if (!x || !b || !b_sf || !d)
+    return fail(NVFP4_ERR_NULL, "x, b, b_sf and d must be non-NULL (row_token, a_global_scale, alpha and status "
+                                "may be NULL)");
+  if (!aligned(x, 16) || !aligned(b, 16) || !aligned(b_sf, 16))
+    return fail(NVFP4_ERR_ALIGN, "x, b and b_sf must be 16-byte aligned");
+  if (!aligned(d, 4) || !aligned(alpha, 4) || !aligned(a_gs, 4))
+    return fail(NVFP4_ERR_ALIGN, "d, alpha and a_global_scale must be 4-byte aligned");
+  return hip_status(nvfp4::launch_grouped_fused(p, packed, status, (hipStream_t)stream, true), fn);
+}
+}  // namespace
+
+nvfp4_status nvfp4_grouped_gemm_fused(const uint16_t* x, const int32_t* row_token, const float* a_global_scale,
+                                      const uint8_t* b, const uint8_t* b_sf, const int32_t* offsets,
+                                      const float* alpha, uint16_t* d, int64_t rows, int64_t T, int64_t N,
+                                      int64_t K, int32_t E, int32_t* status, void* stream) {
+  return grouped_fused(x, row_token, a_global_scale, b, b_sf, offsets, alpha, d, rows, T, N, K, E, status, stream,
+                       false, "nvfp4_grouped_gemm_fused launch");
+}
+
+nvfp4_status nvfp4_grouped_gemm_packed_fused(const uint16_t* x, const int32_t* row_token,
+                                             const float* a_global_scale, const uint8_t* packed,
+                                             const uint8_t* packed_sf, const int32_t* offsets, const float* alpha,
+                                             uint16_t* d, int64_t rows, int64_t T, int64_t N, int64_t K, int32_t E,
+                                             int32_t* status, void* stream) {
+  return grouped_fused(x, row_token, a_global_scale, packed, packed_sf, offsets, alpha, d, rows, T, N, K, E, status,
+                       stream, true, "nvfp4_grouped_gemm_packed_fused launch");
 }
 
 nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K, const float* global_scale, uint8_t* q,

@@ -35,6 +35,7 @@
 //    deterministic.
 //  * Work-group order is remapped so that work-groups sharing operand rows
 //    run on the same XCD (its own 4 MB L2).
+#include <limits.h>
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -948,6 +949,10 @@ struct GRegs {
   uint32_t bs[D][C::TN][C::kSub];
   AQ aq[D];
   uint32_t as[D];
+  // fused quantisation: kAX 16-byte chunks of bf16 activations per lane and
+  // stage, one per 8-element half block (whole-line loads: 32 lanes per row)
+  static constexpr int kAX = C::BM * C::BK * 2 / 16 / C::kThreads;
+  u4_t ax[D][kAX];
 };
 
 // Loads of stage kt into register slot u.  Always the same instructions (so
@@ -956,11 +961,11 @@ struct GRegs {
 // without a memory access.  Unpacked weights (whole-line loads) need one
 // scale word per 16-row block; packed weights hold a lane's four scale words
 // (both row blocks, both sub-steps) in one 16-byte chunk.
-template <class C, int D, bool PACKED>
+template <class C, int D, bool PACKED, bool FUSED>
 __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const rsrc_t& rb, const rsrc_t& rbs,
                                         const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
                                         uint32_t b_step, uint32_t bs_step, const rsrc_t& ra, const rsrc_t& ras,
-                                        uint32_t va, uint32_t vas) {
+                                        uint32_t va, uint32_t vas, const uint32_t (&vax)[GRegs<C, D>::kAX]) {
   constexpr uint32_t kOut = 0x80000000u;
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn)
@@ -977,13 +982,21 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
     R.bs[u][0][0] = w[0]; R.bs[u][0][1] = w[1]; R.bs[u][1][0] = w[2]; R.bs[u][1][1] = w[3];
   }
   typedef typename GRegs<C, D>::AQ AQ;
-  if constexpr (GRegs<C, D>::kAP == 1)
-    R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va : kOut, kt * C::RB, 0));
-  else if constexpr (GRegs<C, D>::kAP == 2)
-    R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b64(ra, live ? va : kOut, kt * C::RB, 0));
-  else
-    R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b32(ra, live ? va : kOut, kt * C::RB, 0));
-  R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * C::SB, 0);
+  if constexpr (FUSED) {
+    // bf16 activations, 512 bytes per row and stage
+#pragma unroll
+    for (int i = 0; i < GRegs<C, D>::kAX; ++i)
+      R.ax[u][i] = __builtin_bit_cast(
+          u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? vax[i] : kOut, kt * C::BK * 2, 0));
+  } else {
+    if constexpr (GRegs<C, D>::kAP == 1)
+      R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va : kOut, kt * C::RB, 0));
+    else if constexpr (GRegs<C, D>::kAP == 2)
+      R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b64(ra, live ? va : kOut, kt * C::RB, 0));
+    else
+      R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b32(ra, live ? va : kOut, kt * C::RB, 0));
+    R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * C::SB, 0);
+  }
 }
 
 // PACKED: B (codes and scales) in the stage-contiguous layout written by
@@ -995,7 +1008,18 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 // 8 s + lane % 8 of each 16-row block, chunk lane / 8, and one DPP rotation
 // gives lane 16 g + r chunks 2 g and 2 g + 1 of row r, whose four scales are
 // one word.
-template <class C, int D, bool PACKED>
+//
+// FUSED: A is not stored quantised.  Wave w loads rows w * BM/8 .. of the
+// stage from the bf16 activations (row row_token[i] of x for the expert's row
+// i) in whole lines, two rows per instruction: lane l reads 16 bytes
+// (elements 8 (l % 32) .. + 7) of row 2 j + l / 32 of its rows, so the lane
+// pairs (l, l ^ 1) hold the two halves of one 16-element block.  Each lane
+// takes the block's amax over its pair (one DPP swap), quantises its half
+// with the rules of the quantise kernel (quantize_half_block16) and writes
+// the dequantised f16 values to the A tile, so the tile, and therefore D, is
+// bit for bit what the quantise kernel, a row gather and the unfused kernel
+// produce.  Tokens outside [0, T) read as zero rows.
+template <class C, int D, bool PACKED, bool FUSED = false>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_grouped_reg(
     GroupedLaunch p) {
   static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
@@ -1003,6 +1027,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   static_assert(C::BM * C::CH <= C::kThreads, "one A chunk per thread");
   static_assert(PACKED || (C::kSub == 2 && C::KG == 4), "whole-line loads pair the two sub-steps of a 256-K stage");
   static_assert(!PACKED || (C::TN == 2 && C::kSub == 2 && C::MF == 16 && C::kWN == 32), "packed scale chunk layout");
+  static_assert(!FUSED || (C::kWaves * 2 * GRegs<C, D>::kAX == C::BM && C::BK == 256),
+                "fused quantisation: each wave loads whole rows, two per instruction");
   __shared__ __attribute__((aligned(16))) SmemGR<C> sm;
   const int tiles_n = (int)((p.N + C::BN - 1) / C::BN);
   const int L = xcd_remap(blockIdx.x, tiles_n * p.E);
@@ -1012,6 +1038,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   if (lo < 0 || hi <= lo || hi > p.rows) return;  // empty or invalid expert
   const int64_t ld = p.K / 2, lds = p.K / 16;
   const float alpha = p.alpha ? p.alpha[e] : 1.0f;
+  const float gs_a = FUSED && p.a_gs ? *p.a_gs : 1.0f;
   const int b_rows = (int)min<int64_t>(C::BN, p.N - n0);
   const int n = (int)(p.K / C::BK);
   const uint8_t *bt, *bst;
@@ -1065,20 +1092,39 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   for (int64_t mc = lo; mc < hi; mc += C::BM) {
     const int rows_c = (int)min<int64_t>(C::BM, hi - mc);
     const int tm_active = (rows_c + C::MF - 1) / C::MF;
-    const rsrc_t ra = make_rsrc(p.a + mc * ld, (uint32_t)(rows_c * ld));
-    const rsrc_t ras = make_rsrc(p.a_sf + mc * lds, (uint32_t)(rows_c * lds));
     // every row block is computed (the kernel waits on HBM, not on MFMA), so
     // the loop has no per-block branches; rows past the expert load as zero
     // and their outputs are never stored
-    const uint32_t va = ar < rows_c ? (uint32_t)(ar * ld + ac * 16 + ah * (16 / RT::kAP)) : 0x80000000u;
-    const uint32_t vas = ar < rows_c ? (uint32_t)(ar * lds + 4 * (ac >> 1)) : 0x80000000u;
+    rsrc_t ra, ras;
+    uint32_t va, vas, vax[RT::kAX];
+    if constexpr (FUSED) {
+      // the whole activation tensor (T * K * 2 < 2^31 bytes, checked by the
+      // host), addressed through each row's token
+      ra = make_rsrc(p.x, (uint32_t)(p.T * p.K * 2));
+      ras = ra;
+#pragma unroll
+      for (int i = 0; i < RT::kAX; ++i) {
+        const int r = wave * 2 * RT::kAX + 2 * i + (lane >> 5);
+        int64_t tok = -1;
+        if (r < rows_c) tok = p.row_token ? (int64_t)p.row_token[mc + r] : mc + r;
+        vax[i] = tok >= 0 && tok < p.T ? (uint32_t)(tok * p.K * 2 + (lane & 31) * 16) : 0x80000000u;
+      }
+      va = vas = 0x80000000u;
+    } else {
+      ra = make_rsrc(p.a + mc * ld, (uint32_t)(rows_c * ld));
+      ras = make_rsrc(p.a_sf + mc * lds, (uint32_t)(rows_c * lds));
+      va = ar < rows_c ? (uint32_t)(ar * ld + ac * 16 + ah * (16 / RT::kAP)) : 0x80000000u;
+      vas = ar < rows_c ? (uint32_t)(ar * lds + 4 * (ac >> 1)) : 0x80000000u;
+#pragma unroll
+      for (int i = 0; i < RT::kAX; ++i) vax[i] = 0x80000000u;
+    }
     typename C::Acc acc[C::TM][C::TN];
     zero_acc<C>(acc);
     GRegs<C, D> R;
     __syncthreads();  // the previous row chunk is done with both A tiles
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      gr_load<C, D, PACKED>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
+      gr_load<C, D, PACKED, FUSED>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
     for (int i0 = 0; i0 < n; i0 += D) {
@@ -1087,7 +1133,20 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
         const int st = i0 + u;  // < n: the launcher picks this kernel only when D divides n
         {
           uint16_t* af = sm.af[u & 1];
-          {
+          if constexpr (FUSED) {
+            // this lane's half blocks: quantise, then write the dequantised
+            // values (8-value group lane % 32 of the row)
+#pragma unroll
+            for (int i = 0; i < RT::kAX; ++i) {
+              const int r = wave * 2 * RT::kAX + 2 * i + (lane >> 5);
+              f4_t lo, hi;
+              bf16x8_to_f32(R.ax[u][i], lo, hi);
+              uint32_t w;
+              const uint32_t code = quantize_half_block16(lo, hi, gs_a, w);
+              const _Float16 sh = (_Float16)e4m3_value_pos(code);  // exact
+              *(h8_t*)(af + r * C::BK + (((lane & 31) ^ (r & 15)) << 3)) = dequant8(w, h2_t{sh, sh});
+            }
+          } else {
             const h2_t sp = e4m3x2_to_h2(R.as[u] >> (16 * (ac & 1)));
 #pragma unroll
             for (int tt = 0; tt < 4 / RT::kAP; ++tt) {
@@ -1151,7 +1210,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
           __builtin_amdgcn_sched_barrier(0);
-          gr_load<C, D, PACKED>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas);
+          gr_load<C, D, PACKED, FUSED>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va,
+                                       vas, vax);
         }
       }
     }
@@ -1445,6 +1505,7 @@ static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row
 typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass
 typedef Cfg<32, 256, 1, 8, 16, 256, 2> CfgGroupedReg;    // MoE experts, B streamed through registers
 typedef Cfg<64, 256, 1, 8, 16, 256, 2, 0, 1, 2> CfgGroupedReg64;  // the same with 64-row passes over each expert
+typedef Cfg<32, 256, 1, 8, 16, 256, 2, 0, 1, 4> CfgGroupedRegF;  // 32-row passes quantising A on load: 2 WGs per CU
 
 struct PlanKind {
   const char* name;
@@ -1823,6 +1884,55 @@ hipError_t launch_grouped_packed(GroupedLaunch p, int32_t* status, hipStream_t s
   else
     hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, true>), dim3(tiles_n * (unsigned)p.E),
                        dim3(CfgGroupedReg::kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Token check of the fused grouped GEMM: when the offsets were valid
+// (status 0), status = -(1 + i) for the first row i whose token lies outside
+// [0, T).  Runs after k_check_offsets on the same stream.
+__global__ __launch_bounds__(256) void k_check_tokens(const int32_t* __restrict__ tok, int64_t rows, int64_t T,
+                                                      int32_t* status) {
+  __shared__ int first;
+  if (threadIdx.x == 0) first = INT_MAX;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < rows; i += blockDim.x) {
+    const int32_t t = tok[i];
+    if (t < 0 || t >= T) atomicMin(&first, (int)i);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && first != INT_MAX && *status == 0) *status = -(first + 1);
+}
+
+hipError_t launch_grouped_fused(GroupedLaunch p, bool packed, int32_t* status, hipStream_t stream, bool compute) {
+  if (status) {
+    hipLaunchKernelGGL(k_check_offsets, dim3(1), dim3(64), 0, stream, p.offsets, p.E, p.rows, status);
+    if (p.row_token && p.rows > 0)
+      hipLaunchKernelGGL(k_check_tokens, dim3(1), dim3(256), 0, stream, p.row_token, p.rows, p.T, status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (!compute) return hipSuccess;
+  // the register kernels only (the host requires K % 512 == 0); row passes of
+  // 32 or 64 rows chosen as for the unfused calls
+  const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
+  int gk = tall_experts(p) ? 3 : 2;
+  if (const char* env = getenv("NVFP4_GPLAN")) gk = atoi(env) == 3 ? 3 : 2;
+  const dim3 grid(tiles_n * (unsigned)p.E);
+  if (packed) {
+    if (gk == 3)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, true, true>), grid, dim3(CfgGroupedReg64::kThreads), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedRegF, 2, true, true>), grid, dim3(CfgGroupedRegF::kThreads), 0,
+                         stream, p);
+  } else {
+    if (gk == 3)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false, true>), grid, dim3(CfgGroupedReg64::kThreads), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedRegF, 2, false, true>), grid, dim3(CfgGroupedRegF::kThreads), 0,
+                         stream, p);
+  }
   return hipGetLastError();
 }
 

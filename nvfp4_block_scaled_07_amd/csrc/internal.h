@@ -30,6 +30,13 @@ struct GroupedLaunch {
   uint16_t* d;
   int64_t rows, N, K;
   int E;
+  // Activations quantised on load (the fused variant; a and a_sf unused):
+  // bf16 x[T][K], A row i = x[row_token[i]] (x[i] when row_token is NULL),
+  // quantised with the encode scale *a_gs (1.0 when NULL).
+  const uint16_t* x;
+  const int32_t* row_token;
+  const float* a_gs;
+  int64_t T;
 };
 
 struct GemmPlan {
@@ -49,6 +56,9 @@ hipError_t launch_mx_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream
 hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
 // Grouped GEMM on weights pre-packed by launch_pack_b (K % 512 == 0).
 hipError_t launch_grouped_packed(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute);
+// Grouped GEMM quantising its bf16 activations on load (K % 512 == 0), on
+// [E][N][K/2] weights or (packed) on weights written by launch_pack_b.
+hipError_t launch_grouped_fused(GroupedLaunch p, bool packed, int32_t* status, hipStream_t stream, bool compute);
 size_t packed_b_bytes(int64_t N, int64_t K, int32_t E, size_t* sf_bytes);
 hipError_t launch_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64_t K, int32_t E, uint8_t* pb,
                          uint8_t* psf, hipStream_t stream);

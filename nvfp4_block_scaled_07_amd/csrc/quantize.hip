@@ -19,37 +19,6 @@
 
 namespace nvfp4 {
 
-// fp32 t (finite, >= 0) -> e4m3fn code, round to nearest even, saturating.
-__device__ __forceinline__ uint32_t e4m3_encode_pos(float t) {
-  t = fminf(t, 448.0f);
-  if (t < 0.015625f) {
-    // subnormal range: grid 2^-9; a result of 8 is code 0x08 = 2^-6
-    return (uint32_t)__builtin_rintf(t * 512.0f);
-  }
-  uint32_t u = __float_as_uint(t);
-  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the mantissa to 3 bits, ties to even
-  return (u >> 20) - 960u;           // rebias exponent 127 -> 7 (120 * 8 = 960)
-}
-
-// e4m3fn code in [0x00, 0x7E] -> its fp32 value (exact).
-__device__ __forceinline__ float e4m3_value_pos(uint32_t code) {
-  const int e = (int)(code >> 3), m = (int)(code & 7u);
-  return e ? __builtin_ldexpf((float)(8 + m), e - 10) : __builtin_ldexpf((float)m, -9);
-}
-
-// Codes of 8 consecutive scaled elements, 2 per byte (element 2j in the low
-// nibble of byte j).  The hardware f32 -> e2m1 conversion (scale 1.0: no
-// extra scaling) rounds to nearest even, saturates at +-6 and keeps the sign
-// of values that round to zero.
-__device__ __forceinline__ uint32_t e2m1x8(f4_t lo, f4_t hi, float r) {
-  uint32_t w = 0u;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo[0] * r, lo[1] * r, 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo[2] * r, lo[3] * r, 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hi[0] * r, hi[1] * r, 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hi[2] * r, hi[3] * r, 1.0f, 3);
-  return w;
-}
-
 // One thread per 16-element block (4 loads of 16 bytes, 8 code bytes and one
 // scale byte out); the block's scale is computed once.  Each thread handles
 // kQB blocks, one grid width apart, with all their loads issued first.
@@ -71,16 +40,10 @@ __global__ __launch_bounds__(256) void k_quantize(const f4_t* __restrict__ x, in
 #pragma unroll
     for (int j = 0; j < kQB; ++j) {
       const int64_t b = b0 + j * stride;
-      float a = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[j][c][0]), fabsf(v[j][c][1])), fmaxf(fabsf(v[j][c][2]), fabsf(v[j][c][3]))));
-      const float t = (a / 6.0f) * gs;
-      const uint32_t code = e4m3_encode_pos(t);
-      const float sv = e4m3_value_pos(code);
-      const float r = sv == 0.0f ? 0.0f : gs / sv;
+      uint32_t w[2];
+      const uint32_t code = quantize_block16(v[j], gs, w);
       if (b < nb) {
-        q[b] = u2_t{e2m1x8(v[j][0], v[j][1], r), e2m1x8(v[j][2], v[j][3], r)};
+        q[b] = u2_t{w[0], w[1]};
         sf[b] = (uint8_t)code;
       }
     }

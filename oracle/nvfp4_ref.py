@@ -268,6 +268,38 @@ def grouped_gemm(a, a_sf, b, b_sf, offsets, alpha, d_init) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Fused activation quantisation: the step before the grouped GEMM in an MoE
+# layer (tokens routed to experts are gathered and quantised, then multiplied
+# by each expert's weights; P3 "Why This Message Was Written": 256 experts, 8
+# active per token).  Nothing new is computed: the gather is a row copy and
+# the quantiser and grouped GEMM are the functions above.
+# ---------------------------------------------------------------------------
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact: bf16 is the top half of fp32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def gather_rows(x: np.ndarray, row_token, rows: int) -> np.ndarray:
+    """Row i of the result is x[row_token[i]] (x[i] when row_token is None).
+    READING: a token outside [0, T) gives a zero row."""
+    T = x.shape[0]
+    tok = np.arange(rows) if row_token is None else np.asarray(row_token, dtype=np.int64)[:rows]
+    out = np.zeros((rows,) + x.shape[1:], dtype=x.dtype)
+    ok = (tok >= 0) & (tok < T)
+    out[ok] = x[tok[ok]]
+    return out
+
+
+def grouped_gemm_fused(x_bits, row_token, gs, b, b_sf, offsets, alpha, d_init, rows: int) -> np.ndarray:
+    """D = grouped_gemm(quantize(gather(bf16 x), gs), B, offsets, alpha):
+    the grouped GEMM whose A rows are the routed tokens' activations
+    (bf16 ``[T][K]``), quantised with one encode scale gs for all rows."""
+    a32 = gather_rows(bf16_bits_to_f32(x_bits), row_token, rows)
+    a, a_sf = quantize(a32, np.float32(gs))
+    return grouped_gemm(a, a_sf, b, b_sf, offsets, alpha, d_init)
+
+
+# ---------------------------------------------------------------------------
 # Exact integer mode (an independent check of the fp64 path).
 # ---------------------------------------------------------------------------
 def _int_tables():

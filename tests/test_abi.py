@@ -164,3 +164,30 @@ def test_mx_gemm_error_paths_and_queries():
     assert nv.nvfp4_mx_gemm_workspace_size(1024, 768, 6144) == 0
     assert call(M=16, N=768, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
     assert nv.nvfp4_mx_gemm_workspace_size(16384, 6144, 6144) == 0
+
+
+def _fused(packed=False, x=FAKE, tok=FAKE, gs=None, b=FAKE, bsf=FAKE, off=FAKE, alpha=None, d=FAKE, rows=64,
+           T=32, N=256, K=512, E=4, st=None):
+    fn = nv.lib().nvfp4_grouped_gemm_packed_fused if packed else nv.lib().nvfp4_grouped_gemm_fused
+    return fn(x, tok, gs, b, bsf, off, alpha, d, rows, T, N, K, E, st, None)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_fused_grouped_error_paths(packed):
+    assert _fused(packed, K=256) == 4 and "512" in nv.nvfp4_last_error()
+    assert _fused(packed, K=40) == 2
+    assert _fused(packed, rows=-1) == 2
+    assert _fused(packed, T=-1) == 2
+    assert _fused(packed, T=1 << 18, K=4096) == 4 and "2^31" in nv.nvfp4_last_error()
+    assert _fused(packed, tok=None, rows=64, T=32) == 2 and "row_token" in nv.nvfp4_last_error()
+    assert _fused(packed, off=None) == 1
+    assert _fused(packed, x=None) == 1
+    assert _fused(packed, b=None) == 1
+    assert _fused(packed, d=None) == 1
+    assert _fused(packed, x=FAKE + 8) == 3
+    assert _fused(packed, tok=FAKE + 2) == 3
+    assert _fused(packed, gs=FAKE + 2) == 3
+    assert _fused(packed, st=FAKE + 2) == 3
+    # nothing to multiply and no status word: accepted without a launch
+    assert _fused(packed, rows=0, x=None, d=None) == 0
+    assert _fused(packed, E=0, off=None, x=None) == 0

@@ -1,0 +1,159 @@
+"""GPU parity of the grouped GEMM that quantises its bf16 activations on load
+(nvfp4_grouped_gemm_fused / nvfp4_grouped_gemm_packed_fused), through the C ABI:
+against the oracle at the GEMM tolerance, and bit for bit against the unfused
+path (the quantise kernel, a row gather and the grouped GEMM on the GPU)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_07_amd as nv
+import synth
+from oracle import nvfp4_ref as o
+from tests.gpu_util import bits, check_gemm, dev, gpu_quantize, host, say, scalar
+
+pytestmark = pytest.mark.gpu
+SENTINEL = 0x7FC1
+
+
+def _bf16(x32: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of fp32 values, round to nearest even (torch's cast)."""
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+class _plan:
+    """NVFP4_GPLAN=2 (32-row passes) or 3 (64-row passes) for one call."""
+
+    def __init__(self, gk):
+        self.gk = gk
+
+    def __enter__(self):
+        self.old = os.environ.get("NVFP4_GPLAN")
+        if self.gk is not None:
+            os.environ["NVFP4_GPLAN"] = str(self.gk)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("NVFP4_GPLAN", None)
+        else:
+            os.environ["NVFP4_GPLAN"] = self.old
+
+
+def _fused(x_t, tok_t, gs_t, b_t, bsf_t, off_t, alpha_t, rows, T, N, K, E, packed):
+    d = torch.full((max(rows, 1), max(N, 1)), SENTINEL, dtype=torch.int16, device="cuda")
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    fn = nv.nvfp4_grouped_gemm_packed_fused if packed else nv.nvfp4_grouped_gemm_fused
+    fn(x_t, tok_t, gs_t, b_t, bsf_t, off_t, alpha_t, d, rows, T, N, K, E, st)
+    return d, st
+
+
+def _unfused(x32_t, tok, gs_t, b_t, bsf_t, off_t, alpha_t, rows, N, K, E, packed):
+    """Quantise kernel on the fp32 copy, row gather (zero rows for invalid
+    tokens), then the grouped GEMM."""
+    q_t, sf_t = gpu_quantize(x32_t, gs_t)
+    T = x32_t.shape[0]
+    q_t = torch.cat([q_t, torch.zeros_like(q_t[:1])])
+    sf_t = torch.cat([sf_t, torch.zeros_like(sf_t[:1])])
+    idx = np.where((tok >= 0) & (tok < T), tok, T).astype(np.int64)
+    idx_t = torch.from_numpy(idx).cuda()
+    qa_t, sfa_t = q_t[idx_t].contiguous(), sf_t[idx_t].contiguous()
+    d = torch.full((max(rows, 1), max(N, 1)), SENTINEL, dtype=torch.int16, device="cuda")
+    if packed:
+        nv.nvfp4_grouped_gemm_packed(qa_t, sfa_t, b_t, bsf_t, off_t, alpha_t, d, rows, N, K, E)
+    else:
+        nv.nvfp4_grouped_gemm(qa_t, sfa_t, b_t, bsf_t, off_t, alpha_t, d, rows, N, K, E, None)
+    return d
+
+
+def _problem(seed=0, T=100, E=6, N=300, K=1024, counts=(0, 1, 33, 70, 17, 64)):
+    rng = np.random.default_rng(seed)
+    x32 = (rng.standard_normal((T, K)) * 2.0).astype(np.float32)
+    x32[3, :16] = 0.0                                  # an all-zero block
+    x32[5, 16:32] *= 1e-30                             # a block whose scale underflows to 0
+    xb = _bf16(x32)
+    xq = o.bf16_bits_to_f32(xb)                        # the values the kernel sees
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(off[-1])
+    tok = rng.integers(0, T, rows).astype(np.int32)
+    tok[2] = tok[1]                                    # a repeated token
+    b = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    bsf = rng.integers(0x28, 0x40, size=(E, N, K // 16), dtype=np.uint8)
+    alpha = np.linspace(0.5, 2.0, E).astype(np.float32)
+    gs = np.float32(2688.0) / np.float32(np.abs(xq).max())
+    return xb, xq, tok, off, rows, b, bsf, alpha, gs
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("gk", [2, 3])
+def test_fused_ragged_against_oracle_and_unfused(packed, gk):
+    xb, xq, tok, off, rows, b, bsf, alpha, gs = _problem()
+    T, K = xq.shape
+    E, N = b.shape[:2]
+    tok = tok.copy()
+    tok[40] = T + 5                                    # an invalid token: zero row, status -(1 + 40)
+    say("fused ragged", "packed" if packed else "plain", "gplan", gk, "rows", rows)
+    b_t, bsf_t = dev(b), dev(bsf)
+    if packed:
+        b_t, bsf_t = nv.grouped_pack(b_t, bsf_t, N, K, E)
+    x_t = dev(xb.view(np.int16))
+    gs_t, off_t, alpha_t, tok_t = scalar(gs), dev(off), dev(alpha), dev(tok)
+    with _plan(gk):
+        d, st = _fused(x_t, tok_t, gs_t, b_t, bsf_t, off_t, alpha_t, rows, T, N, K, E, packed)
+        du = _unfused(dev(xq), tok, gs_t, b_t, bsf_t, off_t, alpha_t, rows, N, K, E, packed)
+    assert int(host(st)[0]) == -(1 + 40)
+    got = bits(d)
+    np.testing.assert_array_equal(got, bits(du))
+    qa, sfa = o.quantize(o.gather_rows(xq, tok, rows), gs)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(got[lo:hi], qa[lo:hi], sfa[lo:hi], b[e], bsf[e], alpha[e], f"expert {e}")
+    ref = o.grouped_gemm_fused(xb, tok, gs, b, bsf, off, alpha, np.full((rows, N), SENTINEL, np.uint16), rows)
+    assert (got[40] == ref[40]).all() and (ref[40] == 0).all()
+
+
+def test_fused_identity_rows_and_null_scale():
+    xb, xq, _, off, rows, b, bsf, alpha, _ = _problem(seed=4, T=200, counts=(10, 0, 40, 66, 5, 79))
+    T, K = xq.shape
+    E, N = b.shape[:2]
+    say("fused identity rows", rows)
+    d, st = _fused(dev(xb.view(np.int16)), None, None, dev(b), dev(bsf), dev(off), None, rows, T, N, K, E, False)
+    assert int(host(st)[0]) == 0
+    got = bits(d)
+    qa, sfa = o.quantize(xq[:rows], np.float32(1.0))
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(got[lo:hi], qa[lo:hi], sfa[lo:hi], b[e], bsf[e], None, f"expert {e}")
+
+
+def test_fused_moe_workload_512_tokens():
+    g = synth.GROUPED
+    T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
+    tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
+    rows = int(off[-1])
+    xb = _bf16(synth.token_activations(T, K))
+    xq = o.bf16_bits_to_f32(xb)
+    gs = o.global_encode_scale(xq)
+    say("fused moe: expert weights")
+    b = synth.random_codes(g["seed_expert_base"], E * N, K).reshape(E, N, K // 2)
+    bsf = synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, lo=0x20, hi=0x38).reshape(E, N, K // 16)
+    alpha = np.random.default_rng(77).uniform(0.5, 2.0, E).astype(np.float32) / np.float32(gs)
+    pb, psf = nv.grouped_pack(dev(b), dev(bsf), N, K, E)
+    gs_t, off_t, alpha_t = scalar(gs), dev(off), dev(alpha)
+    say("fused moe: grouped gemm rows", rows)
+    d, st = _fused(dev(xb.view(np.int16)), dev(tok.astype(np.int32)), gs_t, pb, psf, off_t, alpha_t,
+                   rows, T, N, K, E, True)
+    du = _unfused(dev(xq), tok, gs_t, pb, psf, off_t, alpha_t, rows, N, K, E, True)
+    assert int(host(st)[0]) == 0
+    got = bits(d)
+    np.testing.assert_array_equal(got, bits(du))
+    qa, sfa = o.quantize(xq, gs)
+    experts = np.unique(np.concatenate([np.random.default_rng(6).choice(E, 12, replace=False),
+                                        [0, E - 1, int(np.argmax(np.diff(off)))]]))
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            rt = tok[lo:hi]
+            check_gemm(got[lo:hi], qa[rt], sfa[rt], b[e], bsf[e], alpha[e], f"expert {e}")
