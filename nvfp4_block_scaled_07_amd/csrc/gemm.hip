@@ -967,6 +967,14 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
                                         uint32_t b_step, uint32_t bs_step, const rsrc_t& ra, const rsrc_t& ras,
                                         uint32_t va, uint32_t vas, const uint32_t (&vax)[GRegs<C, D>::kAX]) {
   constexpr uint32_t kOut = 0x80000000u;
+  if constexpr (FUSED) {
+    // bf16 activations (512 bytes per row and stage), issued before the
+    // slot's weights so that waiting for them leaves the weights in flight
+#pragma unroll
+    for (int i = 0; i < GRegs<C, D>::kAX; ++i)
+      R.ax[u][i] = __builtin_bit_cast(
+          u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? vax[i] : kOut, kt * C::BK * 2, 0));
+  }
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
@@ -982,13 +990,7 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
     R.bs[u][0][0] = w[0]; R.bs[u][0][1] = w[1]; R.bs[u][1][0] = w[2]; R.bs[u][1][1] = w[3];
   }
   typedef typename GRegs<C, D>::AQ AQ;
-  if constexpr (FUSED) {
-    // bf16 activations, 512 bytes per row and stage
-#pragma unroll
-    for (int i = 0; i < GRegs<C, D>::kAX; ++i)
-      R.ax[u][i] = __builtin_bit_cast(
-          u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? vax[i] : kOut, kt * C::BK * 2, 0));
-  } else {
+  if constexpr (!FUSED) {
     if constexpr (GRegs<C, D>::kAP == 1)
       R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b128(ra, live ? va : kOut, kt * C::RB, 0));
     else if constexpr (GRegs<C, D>::kAP == 2)
@@ -1019,6 +1021,24 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 // the dequantised f16 values to the A tile, so the tile, and therefore D, is
 // bit for bit what the quantise kernel, a row gather and the unfused kernel
 // produce.  Tokens outside [0, T) read as zero rows.
+// Fused quantisation of one stage's activations (register slot ax) into the
+// f16 A tile af: each lane quantises its half blocks and writes their
+// dequantised values as 8-value group lane % 32 of its rows.
+template <class C, int D>
+__device__ __forceinline__ void gr_fused_a(const u4_t (&ax)[GRegs<C, D>::kAX], uint16_t* af, float gs, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int i = 0; i < GRegs<C, D>::kAX; ++i) {
+    const int r = wave * 2 * GRegs<C, D>::kAX + 2 * i + (lane >> 5);
+    f4_t lo, hi;
+    bf16x8_to_f32(ax[i], lo, hi);
+    uint32_t w;
+    const uint32_t code = quantize_half_block16(lo, hi, gs, w);
+    const _Float16 sh = (_Float16)e4m3_value_pos(code);  // exact
+    *(h8_t*)(af + r * C::BK + (((lane & 31) ^ (r & 15)) << 3)) = dequant8(w, h2_t{sh, sh});
+  }
+}
+
 template <class C, int D, bool PACKED, bool FUSED = false>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_grouped_reg(
     GroupedLaunch p) {
@@ -1127,26 +1147,18 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       gr_load<C, D, PACKED, FUSED>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
+    // fused: the A tile of stage s + 1 is written during stage s, after the
+    // barrier that ends every read of that buffer (stage s - 1), so the
+    // quantisation overlaps the other waves' MFMAs instead of holding every
+    // wave at the barrier; stage 0's is written here
+    if constexpr (FUSED) gr_fused_a<C, D>(R.ax[0], sm.af[0], gs_a, wave, lane);
     for (int i0 = 0; i0 < n; i0 += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         const int st = i0 + u;  // < n: the launcher picks this kernel only when D divides n
         {
           uint16_t* af = sm.af[u & 1];
-          if constexpr (FUSED) {
-            // this lane's half blocks: quantise, then write the dequantised
-            // values (8-value group lane % 32 of the row)
-#pragma unroll
-            for (int i = 0; i < RT::kAX; ++i) {
-              const int r = wave * 2 * RT::kAX + 2 * i + (lane >> 5);
-              f4_t lo, hi;
-              bf16x8_to_f32(R.ax[u][i], lo, hi);
-              uint32_t w;
-              const uint32_t code = quantize_half_block16(lo, hi, gs_a, w);
-              const _Float16 sh = (_Float16)e4m3_value_pos(code);  // exact
-              *(h8_t*)(af + r * C::BK + (((lane & 31) ^ (r & 15)) << 3)) = dequant8(w, h2_t{sh, sh});
-            }
-          } else {
+          if constexpr (!FUSED) {
             const h2_t sp = e4m3x2_to_h2(R.as[u] >> (16 * (ac & 1)));
 #pragma unroll
             for (int tt = 0; tt < 4 / RT::kAP; ++tt) {
@@ -1206,6 +1218,10 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
                 }
               }
             }
+          }
+          if constexpr (FUSED) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + 1 < n) gr_fused_a<C, D>(R.ax[(u + 1) % D], sm.af[(u + 1) & 1], gs_a, wave, lane);
           }
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
