@@ -519,6 +519,12 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
     del pb, psf, qa, sfa, d, x32, q_tok, sf_tok
     torch.cuda.empty_cache()
 
+    # one MoE layer's experts (nvfp4_moe_ffn): 512 tokens, top-8 of 256
+    # experts, H = 6144, I = 2048; gate/up grouped GEMM with the activation
+    # gather and quantisation fused, SwiGLU + NVFP4, down grouped GEMM, combine
+    res["moe_ffn_512tok_256exp_top8"] = moe_ffn_workload(nv, torch, dev, stream, synth)
+    torch.cuda.empty_cache()
+
     # grouped calls with the same rows in every expert, weights >= 512 MB
     uni = []
     for u in synth.GROUPED_UNIFORM:
@@ -611,6 +617,50 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
     res["quantize_16384x6144"] = dict(us=round(us, 2), gbps=round(by / us / 1e3, 1),
                                       frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4))
     return res
+
+
+def moe_ffn_workload(nv, torch, dev, stream, synth):
+    g = synth.GROUPED
+    T, E, H, k = g["tokens"], g["experts"], g["k"], g["top_k"]
+    I = g["n"]
+    tok, off = synth.routing(g["seed_router"], T, E, k)
+    rows = int(off[-1])
+    tr = synth.token_rows(tok, T, k)
+    tw = synth.routing_weights(g["seed_router"] + 1, T, k)
+    x32 = torch.from_numpy(synth.token_activations(T, H)).to(dev)
+    x = x32.to(torch.bfloat16)
+    gs_x = torch.empty(1, dtype=torch.float32, device=dev)
+    nv.nvfp4_global_scale(x32, x32.numel(), gs_x)
+    del x32
+
+    def packed(seed, N, K):
+        b = torch.from_numpy(synth.random_codes(seed, E * N, K)).to(dev)
+        bsf = torch.from_numpy(synth.random_scale_bytes(seed + 1, E * N, K, 0x20, 0x38)).to(dev)
+        pb, psf = nv.grouped_pack(b, bsf, N, K, E)
+        del b, bsf
+        torch.cuda.empty_cache()
+        return pb, psf
+    pgu, pgusf = packed(g["seed_expert_base"] + 100, 2 * I, H)
+    pd, pdsf = packed(g["seed_expert_base"] + 200, H, I)
+    a_gu = torch.full((E,), 1e-4, dtype=torch.float32, device=dev)
+    a_d = torch.full((E,), 1e-3, dtype=torch.float32, device=dev)
+    gs_h = torch.ones(1, dtype=torch.float32, device=dev)
+    tok_t = torch.from_numpy(tok.astype(np.int32)).to(dev)
+    off_t = torch.from_numpy(off).to(dev)
+    tr_t, tw_t = torch.from_numpy(tr).to(dev), torch.from_numpy(tw).to(dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(nv.nvfp4_moe_ffn_workspace_size(T, H, I, k), dtype=torch.uint8, device=dev)
+    us = timed(torch, stream, lambda i: nv.nvfp4_moe_ffn(x, gs_x, tok_t, off_t, pgu, pgusf, a_gu, gs_h, pd, pdsf,
+                                                         a_d, tr_t, tw_t, out, T, H, I, E, k, ws), 10)
+    active = int((np.diff(off) > 0).sum())
+    # expert weights, bf16 tokens in and out, routing indices and weights
+    by = active * 3 * I * H * 9 // 16 + 2 * T * H * 2 + rows * 4 + T * k * 8 + 4 * (E + 1) + 8 * E
+    fl = 2.0 * rows * 3 * I * H
+    del pgu, pgusf, pd, pdsf, ws
+    return dict(note="nvfp4_moe_ffn: fused gather+quantise gate/up grouped GEMM, SwiGLU+NVFP4, down grouped GEMM, "
+                     "combine; packed expert weights", T=T, H=H, I=I, E=E, top_k=k, us=round(us, 2),
+                gbps=round(by / us / 1e3, 1), frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4),
+                tflops=round(fl / us / 1e6, 2), algorithmic_bytes=by)
 
 
 def cpu_baseline(seconds):

@@ -193,6 +193,57 @@ nvfp4_status nvfp4_grouped_gemm_packed_fused(const uint16_t* x, const int32_t* r
                                              int32_t* status, void* stream);
 
 /*
+ * The MoE expert FFN over the grouped GEMM.  The pages run each MoE layer's
+ * experts through a fused MoE kernel (cutlass_moe) with 256 experts, 8 active
+ * per token, hidden size H = 6144 and expert intermediate size I = 2048
+ * ("When a Benchmark Crashes: The Elusive FP4 GEMM Comparison on Blackwell
+ * SM120", sections "Why This Message Was Written" and "The Thinking Process
+ * Visible in Reasoning Parts").  The activation is not named on the pages;
+ * it is read as SwiGLU: h = silu(gate) * up, silu(g) = g / (1 + exp(-g)),
+ * with gate and up the first and second I columns of the gate/up output.
+ *
+ * nvfp4_swiglu_quantize: gu bf16 [rows][2I] -> h in fp32 -> NVFP4 with the
+ * quantiser of nvfp4_quantize and the device encode scale gs (NULL = 1.0):
+ * q uint8 [rows][I/2], sf uint8 [rows][I/16].  I % 16 == 0; gu, q 16-byte
+ * aligned.
+ *
+ * nvfp4_moe_combine: out bf16 [T][H] row t = sum over j < top_k, in j
+ * order, of weight[t][j] * down[rows_of[t][j]] (bf16 [rows][H]), in fp32,
+ * rounded once to bf16; an index outside [0, rows) adds nothing.  H % 8 == 0;
+ * down, out 16-byte aligned.
+ *
+ * nvfp4_moe_ffn: one MoE layer's experts for T tokens routed top_k of E:
+ *   gu   = nvfp4_grouped_gemm_packed_fused(x, row_token, gs_x, w_gu)  [rows][2I]
+ *   h    = nvfp4_swiglu_quantize(gu, gs_h)                            [rows][I] NVFP4
+ *   down = nvfp4_grouped_gemm_packed(h, w_d)                          [rows][H]
+ *   out  = nvfp4_moe_combine(down, token_rows, token_weight)          [T][H]
+ * with rows = T * top_k sorted by expert (offsets [E+1], row_token [rows]:
+ * the token of each row) and token_rows [T][top_k] the inverse map (the row
+ * of each of a token's experts); token_weight [T][top_k] fp32 routing
+ * weights; token_rows must name rows that the offsets cover (rows outside
+ * every expert range hold unspecified values).  x bf16 [T][H]; w_gu, w_gu_sf:
+ * expert weights [E][2I][H/2] packed
+ * by nvfp4_grouped_pack_b (N = 2I, K = H); w_d, w_d_sf: [E][H][I/2] packed
+ * (N = H, K = I); alpha_gu, alpha_d: device fp32 [E] (NULL = 1.0); gs_x, gs_h:
+ * device encode scales (NULL = 1.0).  The intermediates live in the
+ * caller's workspace (nvfp4_moe_ffn_workspace_size bytes, 256-byte
+ * aligned).  H % 512 == 0 and I % 512 == 0 (ERR_UNSUPPORTED otherwise),
+ * T * H * 2 < 2^31.  status: as nvfp4_grouped_gemm_fused (offsets, then
+ * tokens).  Asynchronous on stream.
+ */
+nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gu, int64_t rows, int64_t I, const float* gs, uint8_t* q,
+                                   uint8_t* sf, void* stream);
+nvfp4_status nvfp4_moe_combine(const uint16_t* down, const int32_t* rows_of, const float* weight, uint16_t* out,
+                               int64_t T, int64_t H, int32_t top_k, int64_t rows, void* stream);
+size_t nvfp4_moe_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int32_t top_k);
+nvfp4_status nvfp4_moe_ffn(const uint16_t* x, const float* gs_x, const int32_t* row_token, const int32_t* offsets,
+                           const uint8_t* w_gu, const uint8_t* w_gu_sf, const float* alpha_gu, const float* gs_h,
+                           const uint8_t* w_d, const uint8_t* w_d_sf, const float* alpha_d,
+                           const int32_t* token_rows, const float* token_weight, uint16_t* out, int64_t T,
+                           int64_t H, int64_t I, int32_t E, int32_t top_k, void* workspace,
+                           size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
  * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
  * The pages never quantise (their test used random bytes); this follows the
  * block_size 16 and e4m3fn scale format of the pages above with these steps,

@@ -39,6 +39,11 @@ SIGNATURES = {
                                                 _i32, _vp, _vp]),
     "nvfp4_grouped_gemm_packed_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                                        _i64, _i32, _vp, _vp]),
+    "nvfp4_swiglu_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp]),
+    "nvfp4_moe_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "nvfp4_moe_ffn": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                     _i64, _i64, _i32, _i32, _vp, _sz, _vp, _vp]),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_global_scale": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_alpha_from_scales": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
@@ -225,6 +230,38 @@ def nvfp4_grouped_gemm_packed_fused(x, row_token, a_global_scale, packed, packed
                                                E, _ptr(status), _stream(stream))
     _check(st, "nvfp4_grouped_gemm_packed_fused")
     return d
+
+
+def nvfp4_swiglu_quantize(gu, rows: int, I: int, gs, q, sf, stream=None):
+    """h = silu(gate) * up of bf16 gu [rows][2I], quantised to NVFP4 (q, sf)."""
+    st = lib().nvfp4_swiglu_quantize(_ptr(gu), rows, I, _ptr(gs), _ptr(q), _ptr(sf), _stream(stream))
+    _check(st, "nvfp4_swiglu_quantize")
+    return q, sf
+
+
+def nvfp4_moe_combine(down, rows_of, weight, out, T: int, H: int, top_k: int, rows: int, stream=None):
+    st = lib().nvfp4_moe_combine(_ptr(down), _ptr(rows_of), _ptr(weight), _ptr(out), T, H, top_k, rows,
+                                 _stream(stream))
+    _check(st, "nvfp4_moe_combine")
+    return out
+
+
+def nvfp4_moe_ffn_workspace_size(T: int, H: int, I: int, top_k: int) -> int:
+    return int(lib().nvfp4_moe_ffn_workspace_size(T, H, I, top_k))
+
+
+def nvfp4_moe_ffn(x, gs_x, row_token, offsets, w_gu, w_gu_sf, alpha_gu, gs_h, w_d, w_d_sf, alpha_d, token_rows,
+                  token_weight, out, T: int, H: int, I: int, E: int, top_k: int, workspace, status=None,
+                  stream=None):
+    """One MoE layer's experts: fused gate/up grouped GEMM, SwiGLU + NVFP4,
+    down grouped GEMM, weighted combine (weights packed by nvfp4_grouped_pack_b)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().nvfp4_moe_ffn(_ptr(x), _ptr(gs_x), _ptr(row_token), _ptr(offsets), _ptr(w_gu), _ptr(w_gu_sf),
+                             _ptr(alpha_gu), _ptr(gs_h), _ptr(w_d), _ptr(w_d_sf), _ptr(alpha_d), _ptr(token_rows),
+                             _ptr(token_weight), _ptr(out), T, H, I, E, top_k, _ptr(workspace), ws_bytes,
+                             _ptr(status), _stream(stream))
+    _check(st, "nvfp4_moe_ffn")
+    return out
 
 
 def nvfp4_quantize(x, R: int, K: int, global_scale, q, sf, stream=None):

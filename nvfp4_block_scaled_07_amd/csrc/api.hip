@@ -274,6 +274,114 @@ nvfp4_status nvfp4_grouped_gemm_packed_fused(const uint16_t* x, const int32_t* r
                        stream, true, "nvfp4_grouped_gemm_packed_fused launch");
 }
 
+nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gu, int64_t rows, int64_t I, const float* gs, uint8_t* q,
+                                   uint8_t* sf, void* stream) {
+  if (rows < 0 || I < 0) return fail(NVFP4_ERR_SHAPE, "rows = %lld, I = %lld must be >= 0", (long long)rows, (long long)I);
+  if (I % 16) return fail(NVFP4_ERR_SHAPE, "I = %lld is not a multiple of the block size 16", (long long)I);
+  if (rows == 0 || I == 0) return ok();
+  if (!gu || !q || !sf) return fail(NVFP4_ERR_NULL, "gu, q and sf must be non-NULL (gs may be NULL)");
+  if (!aligned(gu, 16) || !aligned(q, 16) || !aligned(gs, 4))
+    return fail(NVFP4_ERR_ALIGN, "gu and q must be 16-byte aligned, gs 4-byte aligned");
+  return hip_status(nvfp4::launch_swiglu_quantize(gu, rows, I, gs, q, sf, (hipStream_t)stream),
+                    "nvfp4_swiglu_quantize launch");
+}
+
+nvfp4_status nvfp4_moe_combine(const uint16_t* down, const int32_t* rows_of, const float* weight, uint16_t* out,
+                               int64_t T, int64_t H, int32_t top_k, int64_t rows, void* stream) {
+  if (T < 0 || H < 0 || top_k < 0 || rows < 0)
+    return fail(NVFP4_ERR_SHAPE, "T, H, top_k and rows must be >= 0");
+  if (H % 8) return fail(NVFP4_ERR_SHAPE, "H = %lld must be a multiple of 8", (long long)H);
+  if (T == 0 || H == 0) return ok();
+  if (!out || (top_k > 0 && (!down || !rows_of || !weight)))
+    return fail(NVFP4_ERR_NULL, "down, rows_of, weight and out must be non-NULL");
+  if (!aligned(down, 16) || !aligned(out, 16) || !aligned(rows_of, 4) || !aligned(weight, 4))
+    return fail(NVFP4_ERR_ALIGN, "down and out must be 16-byte aligned, rows_of and weight 4-byte aligned");
+  return hip_status(nvfp4::launch_moe_combine(down, rows_of, weight, out, T, H, top_k, rows, (hipStream_t)stream),
+                    "nvfp4_moe_combine launch");
+}
+
+}  // extern "C"
+
+namespace {
+// nvfp4_moe_ffn workspace: gate/up output bf16 [rows][2I], h codes
+// [rows][I/2], h scales [rows][I/16], down output bf16 [rows][H], each
+// segment starting on a 256-byte boundary.
+struct FfnWs {
+  size_t gu, hq, hsf, down, total;
+};
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+FfnWs ffn_ws(int64_t T, int64_t H, int64_t I, int32_t top_k) {
+  const size_t rows = (size_t)T * (size_t)top_k;
+  FfnWs w;
+  w.gu = 0;
+  w.hq = w.gu + up256(rows * (size_t)I * 4);
+  w.hsf = w.hq + up256(rows * (size_t)I / 2);
+  w.down = w.hsf + up256(rows * (size_t)I / 16);
+  w.total = w.down + up256(rows * (size_t)H * 2);
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_moe_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int32_t top_k) {
+  if (T < 0 || H < 0 || I < 0 || top_k < 0) return 0;
+  return ffn_ws(T, H, I, top_k).total;
+}
+
+nvfp4_status nvfp4_moe_ffn(const uint16_t* x, const float* gs_x, const int32_t* row_token, const int32_t* offsets,
+                           const uint8_t* w_gu, const uint8_t* w_gu_sf, const float* alpha_gu, const float* gs_h,
+                           const uint8_t* w_d, const uint8_t* w_d_sf, const float* alpha_d,
+                           const int32_t* token_rows, const float* token_weight, uint16_t* out, int64_t T,
+                           int64_t H, int64_t I, int32_t E, int32_t top_k, void* workspace,
+                           size_t workspace_bytes, int32_t* status, void* stream) {
+  if (T < 0 || H < 0 || I < 0 || E < 0 || top_k < 0)
+    return fail(NVFP4_ERR_SHAPE, "T, H, I, E and top_k must be >= 0");
+  if (H % 512 || I % 512 || H == 0 || I == 0)
+    return fail(NVFP4_ERR_UNSUPPORTED, "H = %lld, I = %lld: the MoE FFN needs both positive multiples of 512",
+                (long long)H, (long long)I);
+  if (H > (int64_t(1) << 22) || I > (int64_t(1) << 22))
+    return fail(NVFP4_ERR_UNSUPPORTED, "H and I must be <= 4194304");
+  if (T * H * 2 >= (int64_t(1) << 31))
+    return fail(NVFP4_ERR_UNSUPPORTED, "T * H * 2 = %lld bytes of activations: at most 2^31 - 1 supported",
+                (long long)(T * H * 2));
+  if (E > 65535 || (int64_t)T * top_k > (1ll << 30)) return fail(NVFP4_ERR_UNSUPPORTED, "E or T * top_k too large");
+  const int64_t rows = T * (int64_t)top_k;
+  if (T == 0) return ok();
+  if (top_k > 0 && E == 0) return fail(NVFP4_ERR_SHAPE, "top_k = %d routed rows need E >= 1 experts", top_k);
+  if (!x || !row_token || !offsets || !w_gu || !w_gu_sf || !w_d || !w_d_sf || !token_rows || !token_weight || !out)
+    return fail(NVFP4_ERR_NULL, "x, row_token, offsets, weights, token_rows, token_weight and out must be non-NULL "
+                                "(gs_x, gs_h, alphas and status may be NULL)");
+  if (!aligned(x, 16) || !aligned(w_gu, 16) || !aligned(w_gu_sf, 16) || !aligned(w_d, 16) || !aligned(w_d_sf, 16) ||
+      !aligned(out, 16) || !aligned(workspace, 256))
+    return fail(NVFP4_ERR_ALIGN, "x, weights and out must be 16-byte aligned, the workspace 256-byte aligned");
+  if (!aligned(row_token, 4) || !aligned(offsets, 4) || !aligned(token_rows, 4) || !aligned(token_weight, 4) ||
+      !aligned(alpha_gu, 4) || !aligned(alpha_d, 4) || !aligned(gs_x, 4) || !aligned(gs_h, 4) || !aligned(status, 4))
+    return fail(NVFP4_ERR_ALIGN, "index, weight, scale and status arrays must be 4-byte aligned");
+  const FfnWs w = ffn_ws(T, H, I, top_k);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, w.total);
+  uint8_t* ws = (uint8_t*)workspace;
+  uint16_t* gu = (uint16_t*)(ws + w.gu);
+  uint8_t* hq = ws + w.hq;
+  uint8_t* hsf = ws + w.hsf;
+  uint16_t* down = (uint16_t*)(ws + w.down);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (rows > 0 && E > 0) {
+    nvfp4::GroupedLaunch p1{nullptr, nullptr, w_gu, w_gu_sf, offsets, alpha_gu, gu, rows, 2 * I, H, E,
+                            x, row_token, gs_x, T};
+    e = nvfp4::launch_grouped_fused(p1, true, status, st, true);
+    if (e == hipSuccess) e = nvfp4::launch_swiglu_quantize(gu, rows, I, gs_h, hq, hsf, st);
+    if (e == hipSuccess) {
+      nvfp4::GroupedLaunch p2{hq, hsf, w_d, w_d_sf, offsets, alpha_d, down, rows, H, I, E};
+      e = nvfp4::launch_grouped_packed(p2, nullptr, st, true);
+    }
+  }
+  if (e == hipSuccess) e = nvfp4::launch_moe_combine(down, token_rows, token_weight, out, T, H, top_k, rows, st);
+  return hip_status(e, "nvfp4_moe_ffn launch");
+}
+
 nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K, const float* global_scale, uint8_t* q,
                             uint8_t* sf, void* stream) {
   if (R < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "R = %lld, K = %lld must be >= 0", (long long)R, (long long)K);

@@ -65,6 +65,15 @@ hipError_t launch_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64
 size_t grouped_workspace(int64_t rows, int64_t N, int64_t K, int32_t E);
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);
 
+// MoE expert FFN pieces (moe.hip): SwiGLU of a [rows][2I] bf16 gate/up
+// output quantised to NVFP4 ([rows][I/2] codes, [rows][I/16] scales), and
+// the weighted combine of each token's top_k expert rows of a [rows][H] bf16
+// output into [T][H] bf16.
+hipError_t launch_swiglu_quantize(const uint16_t* gu, int64_t rows, int64_t I, const float* gs, uint8_t* q,
+                                  uint8_t* sf, hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t* down, const int32_t* rows_of, const float* wt, uint16_t* out,
+                              int64_t T, int64_t H, int32_t top_k, int64_t rows, hipStream_t stream);
+
 hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs, uint8_t* q, uint8_t* sf,
                            hipStream_t stream);
 hipError_t launch_global_scale(const float* x, int64_t n, float* gs, hipStream_t stream);

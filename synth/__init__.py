@@ -108,6 +108,19 @@ def routing(seed: int, tokens: int, experts: int, top_k: int):
     return token_of_row, offsets
 
 
+def token_rows(token_of_row: np.ndarray, tokens: int, top_k: int) -> np.ndarray:
+    """Inverse of the routing's row order: int32[tokens][top_k], the rows of
+    each token in ascending row order."""
+    order = np.argsort(token_of_row, kind="stable")
+    return order.reshape(tokens, top_k).astype(np.int32)
+
+
+def routing_weights(seed: int, tokens: int, top_k: int) -> np.ndarray:
+    """Seeded positive combine weights float32[tokens][top_k] summing to about 1."""
+    w = np.random.default_rng(seed).uniform(0.05, 1.0, size=(tokens, top_k))
+    return (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
 def random_codes(seed: int, rows: int, k: int) -> np.ndarray:
     """Uniform random packed bytes uint8[rows][k/2] (every e2m1 code pair)."""
     rng = np.random.default_rng(seed)
