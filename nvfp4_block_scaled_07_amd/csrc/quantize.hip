@@ -7,8 +7,10 @@
 // GEMM Kernels on Blackwell SM120", section "Assumptions and Their
 // Consequences") with float8_e4m3fn block scales and two 4-bit codes per byte
 // ("When a Benchmark Crashes: The Elusive FP4 GEMM Comparison on Blackwell
-// SM120", section "Input Knowledge Required", item 3).  The arithmetic below
-// is fp32 with round-to-nearest-even, in this order, per 16-element block:
+// SM120", section "Input Knowledge Required", item 3).  The arithmetic
+// (quantize_block16 in device.h, shared with the kernels that quantise on
+// load) is fp32 with round-to-nearest-even, in this order, per 16-element
+// block:
 //   t = (amax / 6) * gs;  sf = e4m3 RNE, saturating at 448
 //   r = gs / E4M3(sf) (correctly rounded; 0 when the scale is 0)
 //   code = e2m1 RNE of x * r, saturating at 6, sign bit kept
