@@ -231,6 +231,16 @@ nvfp4_status nvfp4_grouped_gemm_packed_fused(const uint16_t* x, const int32_t* r
  * T * H * 2 < 2^31.  status: as nvfp4_grouped_gemm_fused (offsets, then
  * tokens).  Asynchronous on stream.
  */
+/*
+ * nvfp4_quantize_rows_bf16: the gather and quantisation of the fused grouped
+ * GEMM as a separate step: row i of q uint8 [rows][K/2], sf uint8
+ * [rows][K/16] is the NVFP4 quantisation (the rules of nvfp4_quantize, encode
+ * scale *gs, NULL = 1.0) of bf16 row row_token[i] of x [T][K] (row i when
+ * row_token is NULL, then rows <= T); tokens outside [0, T) give zero rows.
+ * K % 16 == 0; x, q 16-byte aligned.  Asynchronous on stream.
+ */
+nvfp4_status nvfp4_quantize_rows_bf16(const uint16_t* x, const int32_t* row_token, const float* gs, uint8_t* q,
+                                      uint8_t* sf, int64_t rows, int64_t T, int64_t K, void* stream);
 nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gu, int64_t rows, int64_t I, const float* gs, uint8_t* q,
                                    uint8_t* sf, void* stream);
 nvfp4_status nvfp4_moe_combine(const uint16_t* down, const int32_t* rows_of, const float* weight, uint16_t* out,

@@ -39,6 +39,7 @@ SIGNATURES = {
                                                 _i32, _vp, _vp]),
     "nvfp4_grouped_gemm_packed_fused": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                                        _i64, _i32, _vp, _vp]),
+    "nvfp4_quantize_rows_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "nvfp4_swiglu_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp]),
     "nvfp4_moe_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
@@ -230,6 +231,14 @@ def nvfp4_grouped_gemm_packed_fused(x, row_token, a_global_scale, packed, packed
                                                E, _ptr(status), _stream(stream))
     _check(st, "nvfp4_grouped_gemm_packed_fused")
     return d
+
+
+def nvfp4_quantize_rows_bf16(x, row_token, gs, q, sf, rows: int, T: int, K: int, stream=None):
+    """NVFP4 of bf16 rows x[row_token[i]] (x[i] when row_token is None)."""
+    st = lib().nvfp4_quantize_rows_bf16(_ptr(x), _ptr(row_token), _ptr(gs), _ptr(q), _ptr(sf), rows, T, K,
+                                        _stream(stream))
+    _check(st, "nvfp4_quantize_rows_bf16")
+    return q, sf
 
 
 def nvfp4_swiglu_quantize(gu, rows: int, I: int, gs, q, sf, stream=None):

@@ -3,6 +3,7 @@
 // call touches no device memory.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/nvfp4.h"
 #include "internal.h"
@@ -274,6 +275,20 @@ nvfp4_status nvfp4_grouped_gemm_packed_fused(const uint16_t* x, const int32_t* r
                        stream, true, "nvfp4_grouped_gemm_packed_fused launch");
 }
 
+nvfp4_status nvfp4_quantize_rows_bf16(const uint16_t* x, const int32_t* row_token, const float* gs, uint8_t* q,
+                                      uint8_t* sf, int64_t rows, int64_t T, int64_t K, void* stream) {
+  if (rows < 0 || T < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "rows, T and K must be >= 0");
+  if (K % 16) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of the block size 16", (long long)K);
+  if (!row_token && rows > T)
+    return fail(NVFP4_ERR_SHAPE, "rows = %lld > T = %lld with row_token NULL", (long long)rows, (long long)T);
+  if (rows == 0 || K == 0) return ok();
+  if ((!x && T > 0) || !q || !sf) return fail(NVFP4_ERR_NULL, "x, q and sf must be non-NULL");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(row_token, 4) || !aligned(gs, 4))
+    return fail(NVFP4_ERR_ALIGN, "x and q must be 16-byte aligned, row_token and gs 4-byte aligned");
+  return hip_status(nvfp4::launch_quantize_rows_bf16(x, row_token, rows, T, K, gs, q, sf, (hipStream_t)stream),
+                    "nvfp4_quantize_rows_bf16 launch");
+}
+
 nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gu, int64_t rows, int64_t I, const float* gs, uint8_t* q,
                                    uint8_t* sf, void* stream) {
   if (rows < 0 || I < 0) return fail(NVFP4_ERR_SHAPE, "rows = %lld, I = %lld must be >= 0", (long long)rows, (long long)I);
@@ -307,7 +322,7 @@ namespace {
 // [rows][I/2], h scales [rows][I/16], down output bf16 [rows][H], each
 // segment starting on a 256-byte boundary.
 struct FfnWs {
-  size_t gu, hq, hsf, down, total;
+  size_t gu, hq, hsf, down, aq, asf, total;
 };
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 FfnWs ffn_ws(int64_t T, int64_t H, int64_t I, int32_t top_k) {
@@ -317,7 +332,9 @@ FfnWs ffn_ws(int64_t T, int64_t H, int64_t I, int32_t top_k) {
   w.hq = w.gu + up256(rows * (size_t)I * 4);
   w.hsf = w.hq + up256(rows * (size_t)I / 2);
   w.down = w.hsf + up256(rows * (size_t)I / 16);
-  w.total = w.down + up256(rows * (size_t)H * 2);
+  w.aq = w.down + up256(rows * (size_t)H * 2);
+  w.asf = w.aq + up256(rows * (size_t)H / 2);
+  w.total = w.asf + up256(rows * (size_t)H / 16);
   return w;
 }
 }  // namespace
@@ -369,9 +386,28 @@ nvfp4_status nvfp4_moe_ffn(const uint16_t* x, const float* gs_x, const int32_t* 
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (rows > 0 && E > 0) {
-    nvfp4::GroupedLaunch p1{nullptr, nullptr, w_gu, w_gu_sf, offsets, alpha_gu, gu, rows, 2 * I, H, E,
-                            x, row_token, gs_x, T};
-    e = nvfp4::launch_grouped_fused(p1, true, status, st, true);
+    // gate/up: the tokens gathered and quantised once into the workspace,
+    // then the packed grouped GEMM (measured faster here than quantising on
+    // load, which every one of an expert's 2I / 256 column tiles repeats);
+    // NVFP4_FFN_FUSED=1 selects the fused kernel (tuning only)
+    const char* env = getenv("NVFP4_FFN_FUSED");
+    const bool fused = env && atoi(env) == 1;
+    if (fused) {
+      nvfp4::GroupedLaunch p1{nullptr, nullptr, w_gu, w_gu_sf, offsets, alpha_gu, gu, rows, 2 * I, H, E,
+                              x, row_token, gs_x, T};
+      e = nvfp4::launch_grouped_fused(p1, true, status, st, true);
+    } else {
+      uint8_t* aq = ws + w.aq;
+      uint8_t* asf = ws + w.asf;
+      nvfp4::GroupedLaunch pc{nullptr, nullptr, nullptr, nullptr, offsets, nullptr, nullptr, rows, 2 * I, H, E,
+                              x, row_token, gs_x, T};
+      e = nvfp4::launch_grouped_fused(pc, true, status, st, false);  // offsets and tokens into status
+      if (e == hipSuccess) e = nvfp4::launch_quantize_rows_bf16(x, row_token, rows, T, H, gs_x, aq, asf, st);
+      if (e == hipSuccess) {
+        nvfp4::GroupedLaunch p1{aq, asf, w_gu, w_gu_sf, offsets, alpha_gu, gu, rows, 2 * I, H, E};
+        e = nvfp4::launch_grouped_packed(p1, nullptr, st, true);
+      }
+    }
     if (e == hipSuccess) e = nvfp4::launch_swiglu_quantize(gu, rows, I, gs_h, hq, hsf, st);
     if (e == hipSuccess) {
       nvfp4::GroupedLaunch p2{hq, hsf, w_d, w_d_sf, offsets, alpha_d, down, rows, H, I, E};

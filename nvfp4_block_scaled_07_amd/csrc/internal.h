@@ -76,6 +76,9 @@ hipError_t launch_moe_combine(const uint16_t* down, const int32_t* rows_of, cons
 
 hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs, uint8_t* q, uint8_t* sf,
                            hipStream_t stream);
+// bf16 rows x[row_token[i]] (x[i] if row_token is NULL) -> NVFP4 [rows][K/2], [rows][K/16].
+hipError_t launch_quantize_rows_bf16(const uint16_t* x, const int32_t* row_token, int64_t rows, int64_t T,
+                                    int64_t K, const float* gs, uint8_t* q, uint8_t* sf, hipStream_t stream);
 hipError_t launch_global_scale(const float* x, int64_t n, float* gs, hipStream_t stream);
 hipError_t launch_alpha(const float* gs_a, const float* gs_b, float* alpha, int32_t count, hipStream_t stream);
 

@@ -52,6 +52,34 @@ __global__ __launch_bounds__(256) void k_quantize(const f4_t* __restrict__ x, in
   }
 }
 
+// Rows gathered from bf16 activations and quantised: row i of (q, sf) is
+// the quantisation of x[row_token[i]] (x[i] when row_token is NULL; a token
+// outside [0, T) gives a zero row).  One thread per 16-element block; bf16
+// values are exact fp32 values, so the codes are those k_quantize gives the
+// fp32 copy of the gathered rows.
+__global__ __launch_bounds__(256) void k_quantize_rows_bf16(const u4_t* __restrict__ x, const int32_t* __restrict__ tok,
+                                                            int64_t rows, int64_t T, int64_t K,
+                                                            const float* __restrict__ gs_p, u2_t* __restrict__ q,
+                                                            uint8_t* __restrict__ sf) {
+  const int64_t kb = K / 16;
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= rows * kb) return;
+  const float gs = gs_p ? *gs_p : 1.0f;
+  const int64_t i = b / kb, j = b % kb;
+  const int64_t t = tok ? (int64_t)tok[i] : i;
+  f4_t v[4] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f},
+               f4_t{0.f, 0.f, 0.f, 0.f}};
+  if (t >= 0 && t < T) {
+    const u4_t* src = x + t * (K / 8) + 2 * j;
+    bf16x8_to_f32(src[0], v[0], v[1]);
+    bf16x8_to_f32(src[1], v[2], v[3]);
+  }
+  uint32_t w[2];
+  const uint32_t code = quantize_block16(v, gs, w);
+  q[b] = u2_t{w[0], w[1]};
+  sf[b] = (uint8_t)code;
+}
+
 __global__ void k_zero_word(uint32_t* w) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *w = 0u;
 }
@@ -109,6 +137,15 @@ hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, (const f4_t*)x, nb, gs, (u2_t*)q,
                      sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_bf16(const uint16_t* x, const int32_t* row_token, int64_t rows, int64_t T,
+                                    int64_t K, const float* gs, uint8_t* q, uint8_t* sf, hipStream_t stream) {
+  const int64_t nb = rows * (K / 16);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_rows_bf16, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream,
+                     (const u4_t*)x, row_token, rows, T, K, gs, (u2_t*)q, sf);
   return hipGetLastError();
 }
 

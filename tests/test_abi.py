@@ -191,3 +191,31 @@ def test_fused_grouped_error_paths(packed):
     # nothing to multiply and no status word: accepted without a launch
     assert _fused(packed, rows=0, x=None, d=None) == 0
     assert _fused(packed, E=0, off=None, x=None) == 0
+
+
+def test_moe_ffn_and_pieces_error_paths():
+    L = nv.lib()
+    assert L.nvfp4_quantize_rows_bf16(FAKE, FAKE, None, FAKE, FAKE, 8, 4, 40, None) == 2
+    assert L.nvfp4_quantize_rows_bf16(FAKE, None, None, FAKE, FAKE, 8, 4, 64, None) == 2
+    assert L.nvfp4_quantize_rows_bf16(FAKE + 8, FAKE, None, FAKE, FAKE, 8, 4, 64, None) == 3
+    assert L.nvfp4_quantize_rows_bf16(FAKE, FAKE, None, None, FAKE, 8, 4, 64, None) == 1
+    assert L.nvfp4_swiglu_quantize(FAKE, 4, 40, None, FAKE, FAKE, None) == 2
+    assert L.nvfp4_swiglu_quantize(None, 4, 64, None, FAKE, FAKE, None) == 1
+    assert L.nvfp4_swiglu_quantize(FAKE + 4, 4, 64, None, FAKE, FAKE, None) == 3
+    assert L.nvfp4_moe_combine(FAKE, FAKE, FAKE, FAKE, 4, 12, 2, 8, None) == 2
+    assert L.nvfp4_moe_combine(FAKE, None, FAKE, FAKE, 4, 16, 2, 8, None) == 1
+    assert L.nvfp4_moe_combine(FAKE + 8, FAKE, FAKE, FAKE, 4, 16, 2, 8, None) == 3
+    need = L.nvfp4_moe_ffn_workspace_size(4, 512, 512, 2)
+    assert need > 0
+
+    def ffn(H=512, I=512, E=2, k=2, ws=FAKE, wsb=None, x=FAKE, T=4):
+        return L.nvfp4_moe_ffn(x, None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                               T, H, I, E, k, ws, need if wsb is None else wsb, None, None)
+    assert ffn(H=256) == 4 and "512" in nv.nvfp4_last_error()
+    assert ffn(I=768) == 4
+    assert ffn(E=0) == 2
+    assert ffn(x=None) == 1
+    assert ffn(ws=FAKE + 16) == 3
+    assert ffn(wsb=need - 1) == 5
+    assert ffn(ws=None) == 5
+    assert ffn(T=0, x=None) == 0

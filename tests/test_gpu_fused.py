@@ -157,3 +157,23 @@ def test_fused_moe_workload_512_tokens():
         if hi > lo:
             rt = tok[lo:hi]
             check_gemm(got[lo:hi], qa[rt], sfa[rt], b[e], bsf[e], alpha[e], f"expert {e}")
+
+
+def test_quantize_rows_bf16_bitwise():
+    xb, xq, tok, off, rows, b, bsf, alpha, gs = _problem(seed=8)
+    T, K = xq.shape
+    tok = tok.copy()
+    tok[7] = -2
+    tok[9] = T
+    say("quantize rows bf16", rows, T, K)
+    q = torch.empty((rows, K // 2), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((rows, K // 16), dtype=torch.uint8, device="cuda")
+    nv.nvfp4_quantize_rows_bf16(dev(xb.view(np.int16)), dev(tok), scalar(gs), q, sf, rows, T, K)
+    rq, rsf = o.quantize(o.gather_rows(xq, tok, rows), gs)
+    np.testing.assert_array_equal(host(q), rq)
+    np.testing.assert_array_equal(host(sf), rsf)
+    # identity rows, NULL scale
+    nv.nvfp4_quantize_rows_bf16(dev(xb.view(np.int16)), None, None, q[:T], sf[:T], T, T, K)
+    rq, rsf = o.quantize(xq, np.float32(1.0))
+    np.testing.assert_array_equal(host(q)[:T], rq)
+    np.testing.assert_array_equal(host(sf)[:T], rsf)
