@@ -57,6 +57,9 @@ def main():
     ap.add_argument("--profile-mx", type=int, default=0, metavar="M",
                     help="for profiler runs: the MXFP4 GEMM M x 6144 x 6144 (graph of 10 calls, replayed 6 times); "
                          "prints its time")
+    ap.add_argument("--profile-moe", action="store_true",
+                    help="run only the MoE expert FFN layer (512 tokens, top-8 of 256 experts) as the bench times "
+                         "it, for a profiler")
     ap.add_argument("--graph", action="store_true",
                     help="with --profile-call: time the call as the headline does (graphs of 64 calls over "
                          "the rotating sets, replayed 8 times) instead of 8 eager calls")
@@ -125,6 +128,9 @@ def main():
         return
     if args.profile_mx:
         profile_mx(torch, nv, synth, stream, args.profile_mx)
+        return
+    if args.profile_moe:
+        print(json.dumps(moe_ffn_workload(nv, torch, dev, stream, synth)), flush=True)
         return
 
     # ---------------- headline: attention-projection sweep -----------------
