@@ -663,8 +663,8 @@ def moe_ffn_workload(nv, torch, dev, stream, synth):
     by = active * 3 * I * H * 9 // 16 + 2 * T * H * 2 + rows * 4 + T * k * 8 + 4 * (E + 1) + 8 * E
     fl = 2.0 * rows * 3 * I * H
     del pgu, pgusf, pd, pdsf, ws
-    return dict(note="nvfp4_moe_ffn: fused gather+quantise gate/up grouped GEMM, SwiGLU+NVFP4, down grouped GEMM, "
-                     "combine; packed expert weights", T=T, H=H, I=I, E=E, top_k=k, us=round(us, 2),
+    return dict(note="nvfp4_moe_ffn: gather+quantise of the routed tokens, gate/up grouped GEMM, SwiGLU+NVFP4, "
+                     "down grouped GEMM, combine; packed expert weights", T=T, H=H, I=I, E=E, top_k=k, us=round(us, 2),
                 gbps=round(by / us / 1e3, 1), frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4),
                 tflops=round(fl / us / 1e6, 2), algorithmic_bytes=by)
 

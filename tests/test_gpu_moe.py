@@ -169,3 +169,40 @@ def test_moe_ffn_pages_shape_sampled_tokens():
         fr = _frob(out[t], ref[i])
         say("token", t, "relative Frobenius error", fr)
         assert fr <= 1e-2
+
+
+def test_moe_ffn_graph_replays_match_eager():
+    # the whole layer (status word included) captured in one HIP graph; each
+    # replay, with eager work and synchronisation in between, equals the eager run
+    T, H, I, E, k = 48, 1024, 512, 6, 2
+    P = _ffn_problem(T, H, I, E, k, seed=500)
+    t = {n: dev(v) for n, v in P.items() if isinstance(v, np.ndarray) and n not in ("w_gu", "w_gu_sf", "w_d", "w_d_sf", "x")}
+    x = dev(P["x"].view(np.int16))
+    pgu, pgusf = nv.grouped_pack(dev(P["w_gu"]), dev(P["w_gu_sf"]), 2 * I, H, E)
+    pd, pdsf = nv.grouped_pack(dev(P["w_d"]), dev(P["w_d_sf"]), H, I, E)
+    gs_x, gs_h = scalar(P["gs_x"]), scalar(P["gs_h"])
+    ws = torch.empty(nv.nvfp4_moe_ffn_workspace_size(T, H, I, k), dtype=torch.uint8, device="cuda")
+    out = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+
+    def run():
+        nv.nvfp4_moe_ffn(x, gs_x, t["tok"], t["off"], pgu, pgusf, t["a_gu"], gs_h, pd, pdsf, t["a_d"], t["tr"],
+                         t["tw"], out, T, H, I, E, k, ws, st)
+    say("ffn graph eager")
+    run()
+    eager = bits(out).copy()
+    assert int(host(st)[0]) == 0
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        out.fill_(0)
+        ws.fill_(0xFF)
+        st.fill_(-7)
+        torch.cuda.synchronize()
+        say("ffn graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(out), eager)
+        assert int(host(st)[0]) == 0
