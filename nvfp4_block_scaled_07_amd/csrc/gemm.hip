@@ -1021,6 +1021,78 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 // the dequantised f16 values to the A tile, so the tile, and therefore D, is
 // bit for bit what the quantise kernel, a row gather and the unfused kernel
 // produce.  Tokens outside [0, T) read as zero rows.
+// The stage's A codes of register slot u (this thread's part ah of chunk ac
+// of row ar) dequantised into the f16 A tile af.
+template <class C, int D>
+__device__ __forceinline__ void gr_dequant_a(const GRegs<C, D>& R, int u, uint16_t* af, int ar, int ac, int ah) {
+  typedef GRegs<C, D> RT;
+  const h2_t sp = e4m3x2_to_h2(R.as[u] >> (16 * (ac & 1)));
+#pragma unroll
+  for (int tt = 0; tt < 4 / RT::kAP; ++tt) {
+    const int t = ah * (4 / RT::kAP) + tt;  // 8-value group of the chunk
+    const h8_t o = dequant8(R.aq[u][tt], scale_pair(sp, t >> 1));
+    *(h8_t*)(af + ar * C::BK + (((4 * ac + t) ^ (ar & 15)) << 3)) = o;
+  }
+}
+
+// One stage of the grouped register kernels after the A tile is in LDS:
+// the B fragments of register slot u (whole-line loads are first put into
+// MFMA layout by the DPP exchange) dequantised and multiplied with the f16 A
+// tile af.
+template <class C, int D, bool PACKED>
+__device__ __forceinline__ void gr_compute(GRegs<C, D>& R, int u, const uint16_t* af,
+                                           typename C::Acc (&acc)[C::TM][C::TN], int r_in, int g, bool lo8) {
+  if constexpr (!PACKED) {
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      uint32_t w[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { w[j] = R.bq[u][tn][0][j]; w[4 + j] = R.bq[u][tn][1][j]; }
+      kreg_exchange(w, lo8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { R.bq[u][tn][0][j] = w[j]; R.bq[u][tn][1][j] = w[4 + j]; }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < C::kSub; ++s) {
+    const int c = PACKED ? C::KG * s + g : 2 * g + s;
+    h2_t bsp[C::TN];
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn)
+      bsp[tn] = PACKED ? e4m3x2_to_h2(R.bs[u][tn][s] >> (16 * (c & 1))) : e4m3x2_to_h2(R.bs[u][tn][0] >> (16 * s));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (C::TM <= 2) {
+        h8_t a[C::TM];
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) {
+          const int row = tm * C::MF + r_in;
+          a[tm] = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
+        }
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+          const h8_t bf = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm) acc[tm][tn] = Mfma<C::MF>::run(a[tm], bf, acc[tm][tn]);
+        }
+      } else {
+        // taller tiles: dequantise the B fragments first, then stream
+        // one A fragment at a time (fewer live registers)
+        h8_t bf[C::TN];
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) bf[tn] = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) {
+          const int row = tm * C::MF + r_in;
+          const h8_t a = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<C::MF>::run(a, bf[tn], acc[tm][tn]);
+        }
+      }
+    }
+  }
+}
+
 // Fused quantisation of one stage's activations (register slot ax) into the
 // f16 A tile af: each lane quantises its half blocks and writes their
 // dequantised values as 8-value group lane % 32 of its rows.
@@ -1158,67 +1230,11 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
         const int st = i0 + u;  // < n: the launcher picks this kernel only when D divides n
         {
           uint16_t* af = sm.af[u & 1];
-          if constexpr (!FUSED) {
-            const h2_t sp = e4m3x2_to_h2(R.as[u] >> (16 * (ac & 1)));
-#pragma unroll
-            for (int tt = 0; tt < 4 / RT::kAP; ++tt) {
-              const int t = ah * (4 / RT::kAP) + tt;  // 8-value group of the chunk
-              const h8_t o = dequant8(R.aq[u][tt], scale_pair(sp, t >> 1));
-              *(h8_t*)(af + ar * C::BK + (((4 * ac + t) ^ (ar & 15)) << 3)) = o;
-            }
-          }
+          if constexpr (!FUSED) gr_dequant_a<C, D>(R, u, af, ar, ac, ah);
           // LDS-only barrier: a __syncthreads() fence would also wait for the
           // prefetched loads (loads and stores share one counter)
           lds_barrier();
-          if constexpr (!PACKED) {
-#pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn) {
-              uint32_t w[8];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) { w[j] = R.bq[u][tn][0][j]; w[4 + j] = R.bq[u][tn][1][j]; }
-              kreg_exchange(w, lo8);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) { R.bq[u][tn][0][j] = w[j]; R.bq[u][tn][1][j] = w[4 + j]; }
-            }
-          }
-#pragma unroll
-          for (int s = 0; s < C::kSub; ++s) {
-            const int c = PACKED ? C::KG * s + g : 2 * g + s;
-            h2_t bsp[C::TN];
-#pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn)
-              bsp[tn] = PACKED ? e4m3x2_to_h2(R.bs[u][tn][s] >> (16 * (c & 1))) : e4m3x2_to_h2(R.bs[u][tn][0] >> (16 * s));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              if constexpr (C::TM <= 2) {
-                h8_t a[C::TM];
-#pragma unroll
-                for (int tm = 0; tm < C::TM; ++tm) {
-                  const int row = tm * C::MF + r_in;
-                  a[tm] = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
-                }
-#pragma unroll
-                for (int tn = 0; tn < C::TN; ++tn) {
-                  const h8_t bf = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
-#pragma unroll
-                  for (int tm = 0; tm < C::TM; ++tm) acc[tm][tn] = Mfma<C::MF>::run(a[tm], bf, acc[tm][tn]);
-                }
-              } else {
-                // taller tiles: dequantise the B fragments first, then stream
-                // one A fragment at a time (fewer live registers)
-                h8_t bf[C::TN];
-#pragma unroll
-                for (int tn = 0; tn < C::TN; ++tn) bf[tn] = dequant8(R.bq[u][tn][s][t], scale_pair(bsp[tn], t >> 1));
-#pragma unroll
-                for (int tm = 0; tm < C::TM; ++tm) {
-                  const int row = tm * C::MF + r_in;
-                  const h8_t a = *(const h8_t*)(af + row * C::BK + (((4 * c + t) ^ (row & 15)) << 3));
-#pragma unroll
-                  for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = Mfma<C::MF>::run(a, bf[tn], acc[tm][tn]);
-                }
-              }
-            }
-          }
+          gr_compute<C, D, PACKED>(R, u, af, acc, r_in, g, lo8);
           if constexpr (FUSED) {
             __builtin_amdgcn_sched_barrier(0);
             if (st + 1 < n) gr_fused_a<C, D>(R.ax[(u + 1) % D], sm.af[(u + 1) & 1], gs_a, wave, lane);
