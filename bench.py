@@ -179,9 +179,13 @@ def main():
         reps = min(len(sets), 64)
         g = capture(torch, lambda: [call(w, sets[i], alpha, outs, wss, m) for i in range(reps)])
         t_us = replay_us(torch, stream, g, reps)
+        del g
+        # the same calls on one buffer set (operands L2 / Infinity Cache resident)
+        g = capture(torch, lambda: [call(w, sets[0], alpha, outs, wss, m) for _ in range(reps)])
+        t_warm = replay_us(torch, stream, g, reps)
         fl = 2.0 * m * N * K
         by = algo_bytes(m, N, K)
-        shapes.append(dict(M=m, N=N, K=K, plan=nv.nvfp4_gemm_plan(m, N, K), us=round(t_us, 3),
+        shapes.append(dict(M=m, N=N, K=K, plan=nv.nvfp4_gemm_plan(m, N, K), us=round(t_us, 3), us_warm=round(t_warm, 3),
                            tflops=round(fl / t_us / 1e6, 2), gbps=round(by / t_us / 1e3, 1),
                            frac_f16_mfma=round(fl / t_us / 1e6 / PEAK_F16_TFLOPS, 4),
                            frac_fp4_peak=round(fl / t_us / 1e6 / PEAK_FP4_TFLOPS, 4),
@@ -203,6 +207,11 @@ def main():
                         frac=round(dom["gbps"] / PEAK_HBM_GBPS, 4), traffic=traffic,
                         kernel_call=f"{call_name} ({dom['plan']})", algorithmic_bytes=by,
                         algorithmic_flops=fl)
+    # launch floor: a graph of 64 one-element fills (the smallest kernel)
+    tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+    g = capture(torch, lambda: [tiny.fill_(float(i)) for i in range(64)])
+    launch_floor = replay_us(torch, stream, g, 64)
+    del g, tiny
     del multi, single
     del sets, outs, wss
     torch.cuda.empty_cache()
@@ -214,7 +223,9 @@ def main():
                config=dict(workload=f"{name}: nvfp4_gemm M in {ms} x N={N} x K={K}, bf16 out, "
                                     f"rotating HBM-resident buffer sets (cold cache)",
                            M=ms, N=N, K=K, block_size=16),
-               roofline=roofline, shapes=shapes)
+               roofline=roofline, shapes=shapes,
+               launch_floor_us=dict(us=round(launch_floor, 3),
+                                    note="per kernel in a graph of 64 one-element fills: the floor under every call"))
 
     if not args.no_extra:
         out["other_workloads"] = other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)

@@ -219,3 +219,19 @@ def test_moe_ffn_and_pieces_error_paths():
     assert ffn(wsb=need - 1) == 5
     assert ffn(ws=None) == 5
     assert ffn(T=0, x=None) == 0
+
+
+def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
+    # the binding has no CPU path: without the built library every entry point
+    # fails at load, and no module of the package imports the oracle
+    monkeypatch.setattr(nv, "_lib", None)
+    monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        nv.lib()
+    with pytest.raises(ImportError):
+        nv.nvfp4_gemm_plan(16, 768, 6144)
+    pkg = os.path.join(ROOT, "nvfp4_block_scaled_07_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            src = open(os.path.join(pkg, f)).read()
+            assert "oracle" not in src.replace("no CPU or PyTorch fallback", ""), f
