@@ -177,3 +177,22 @@ def test_quantize_rows_bf16_bitwise():
     rq, rsf = o.quantize(xq, np.float32(1.0))
     np.testing.assert_array_equal(host(q)[:T], rq)
     np.testing.assert_array_equal(host(sf)[:T], rsf)
+
+
+def test_fused_degenerate_calls_report_status():
+    # no rows: only the offsets are checked (status 0, nothing written); an
+    # invalid range reports its expert; no experts: nothing to do
+    K, N, T = 512, 256, 4
+    x = torch.zeros((T, K), dtype=torch.int16, device="cuda")
+    b = torch.zeros((2, N, K // 2), dtype=torch.uint8, device="cuda")
+    bsf = torch.zeros((2, N, K // 16), dtype=torch.uint8, device="cuda")
+    d = torch.full((3, N), SENTINEL, dtype=torch.int16, device="cuda")  # 3 rows: the second call writes them
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    say("fused degenerate")
+    nv.nvfp4_grouped_gemm_fused(x, None, None, b, bsf, dev(np.array([0, 0, 0], np.int32)), None, d, 0, T, N, K, 2, st)
+    assert int(host(st)[0]) == 0 and (bits(d) == SENTINEL).all()
+    nv.nvfp4_grouped_gemm_fused(x, None, None, b, bsf, dev(np.array([0, 3, 2], np.int32)), None, d, 3, T, N, K, 2, st)
+    assert int(host(st)[0]) == 2
+    assert (bits(d) == 0).all()  # expert 0's rows of zero activations; expert 1 skipped
+    nv.nvfp4_grouped_gemm_fused(x, None, None, b, bsf, None, None, d, 3, T, N, K, 0, None)
+    torch.cuda.synchronize()

@@ -206,3 +206,15 @@ def test_moe_ffn_graph_replays_match_eager():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(out), eager)
         assert int(host(st)[0]) == 0
+
+
+def test_moe_ffn_single_token_and_empty_experts():
+    # one token routed to 2 of 5 experts: three experts have no rows
+    T, H, I, E, k = 1, 512, 512, 5, 2
+    P = _ffn_problem(T, H, I, E, k, seed=600)
+    assert (np.diff(P["off"]) == 0).sum() == 3
+    say("moe ffn single token")
+    out, _ = _run_ffn(P, T, H, I, E, k)
+    ref, _ = m.moe_ffn(P["x"], P["gs_x"], P["tok"], P["off"], P["w_gu"], P["w_gu_sf"], P["a_gu"], P["gs_h"],
+                       P["w_d"], P["w_d_sf"], P["a_d"], P["tr"], P["tw"], I)
+    assert _frob(out, ref) <= 1e-2
