@@ -133,8 +133,9 @@ size_t nvfp4_grouped_workspace_size(int64_t rows, int64_t N, int64_t K, int32_t 
  * (the nvfp4_grouped_gemm layout) -> packed, packed_sf (caller-allocated,
  * sizes from nvfp4_grouped_packed_size).  Layout, per expert e, slab
  * t = 0 .. ceil(N/256)-1 and stage k = 0 .. K/256-1: block
- * (e * ceil(N/256) + t) * (K/256) + k holds rows t*256 .. t*256+255 of expert
- * e and K elements 256k .. 256k+255 (rows past N are zero).  A code block is
+ * k * (E * ceil(N/256)) + e * ceil(N/256) + t (stage-major, so the work-groups
+ * running at one time read neighbouring blocks) holds rows t*256 .. t*256+255
+ * of expert e and K elements 256k .. 256k+255 (rows past N are zero).  A code block is
  * 2048 chunks of 16 bytes: chunk c (0..7, K elements 256k + 32c ..) of row r
  * (0..255) is stored at chunk position
  * (((r / 32) * 2 + (r % 32) / 16) * 2 + c / 4) * 64 + (c % 4) * 16 + r % 16,

@@ -961,12 +961,30 @@ struct GRegs {
 // without a memory access.  Unpacked weights (whole-line loads) need one
 // scale word per 16-row block; packed weights hold a lane's four scale words
 // (both row blocks, both sub-steps) in one 16-byte chunk.
+// Packed weights: stage kt of a slab is the block at base + kt * stride
+// (codes) and sbase + kt * sstride (scales); the buffer resource of each
+// stage is formed from the 64-bit address, so no 32-bit offset limits the
+// size of the packed tensor.
+struct PackedStream {
+  const uint8_t* base;
+  const uint8_t* sbase;
+  int64_t stride, sstride;
+};
+
 template <class C, int D, bool PACKED, bool FUSED>
-__device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const rsrc_t& rb, const rsrc_t& rbs,
+__device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const PackedStream& ps,
+                                        const rsrc_t& rb, const rsrc_t& rbs,
                                         const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
                                         uint32_t b_step, uint32_t bs_step, const rsrc_t& ra, const rsrc_t& ras,
                                         uint32_t va, uint32_t vas, const uint32_t (&vax)[GRegs<C, D>::kAX]) {
   constexpr uint32_t kOut = 0x80000000u;
+  rsrc_t rbk = rb, rbsk = rbs;
+  uint32_t bo = kt * b_step, bso = kt * bs_step;
+  if constexpr (PACKED) {
+    rbk = make_rsrc(ps.base + (int64_t)kt * ps.stride, C::BN * C::RB);
+    rbsk = make_rsrc(ps.sbase + (int64_t)kt * ps.sstride, C::BN * C::SB);
+    bo = bso = 0;
+  }
   if constexpr (FUSED) {
     // bf16 activations (512 bytes per row and stage), issued before the
     // slot's weights so that waiting for them leaves the weights in flight
@@ -980,13 +998,13 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
       R.bq[u][tn][s] = __builtin_bit_cast(
-          u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, live ? vb[tn][s] : kOut, kt * b_step, 0));
+          u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbk, live ? vb[tn][s] : kOut, bo, 0));
       if (!PACKED && s == 0)
-        R.bs[u][tn][0] = __builtin_amdgcn_raw_buffer_load_b32(rbs, live ? vbs[tn][0] : kOut, kt * bs_step, 0);
+        R.bs[u][tn][0] = __builtin_amdgcn_raw_buffer_load_b32(rbsk, live ? vbs[tn][0] : kOut, bso, 0);
     }
   if constexpr (PACKED) {
-    const u4_t w = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbs, live ? vbs[0][0] : kOut,
-                                                                                  kt * bs_step, 0));
+    const u4_t w = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbsk, live ? vbs[0][0] : kOut,
+                                                                                  bso, 0));
     R.bs[u][0][0] = w[0]; R.bs[u][0][1] = w[1]; R.bs[u][1][0] = w[2]; R.bs[u][1][1] = w[3];
   }
   typedef typename GRegs<C, D>::AQ AQ;
@@ -1001,8 +1019,9 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
   }
 }
 
-// PACKED: B (codes and scales) in the stage-contiguous layout written by
-// k_pack_b (each stage of a 256-row slab is one block; rows past N are zero);
+// PACKED: B (codes and scales) in the layout written by k_pack_b (each
+// stage of a 256-row slab is one block, blocks in stage-major order; rows
+// past N are zero);
 // every code load instruction reads 1 KB in lane order, lane 16 g + r holds
 // chunks g and 4 + g of row r, and a wave's scale words for the stage are one
 // 512-byte run.  Unpacked `[E][N][K/2]` weights are read in
@@ -1135,14 +1154,19 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   const int n = (int)(p.K / C::BK);
   const uint8_t *bt, *bst;
   uint32_t b_bytes, bs_bytes, b_step, bs_step, b_ld, bs_ld;
+  PackedStream ps{nullptr, nullptr, 0, 0};
   if constexpr (PACKED) {
-    const int64_t slab = (int64_t)e * tiles_n + L % tiles_n;
-    b_step = C::BN * C::RB;
-    bs_step = C::BN * C::SB;
-    bt = p.b + slab * n * b_step;
-    bst = p.b_sf + slab * n * bs_step;
-    b_bytes = (uint32_t)(n * b_step);
-    bs_bytes = (uint32_t)(n * bs_step);
+    // stage-major blocks: stage kt of slab s at (kt * slabs + s) * block
+    const int64_t slab = (int64_t)e * tiles_n + L % tiles_n, slabs = (int64_t)p.E * tiles_n;
+    ps.base = p.b + slab * (C::BN * C::RB);
+    ps.sbase = p.b_sf + slab * (C::BN * C::SB);
+    ps.stride = slabs * (C::BN * C::RB);
+    ps.sstride = slabs * (C::BN * C::SB);
+    b_step = bs_step = 0;
+    bt = ps.base;
+    bst = ps.sbase;
+    b_bytes = C::BN * C::RB;
+    bs_bytes = C::BN * C::SB;
     b_ld = C::RB;
     bs_ld = C::SB;
   } else {
@@ -1216,7 +1240,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     __syncthreads();  // the previous row chunk is done with both A tiles
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      gr_load<C, D, PACKED, FUSED>(R, u, u, true, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
+      gr_load<C, D, PACKED, FUSED>(R, u, u, true, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
     // fused: the A tile of stage s + 1 is written during stage s, after the
@@ -1242,8 +1266,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
           __builtin_amdgcn_sched_barrier(0);
-          gr_load<C, D, PACKED, FUSED>(R, u, st + D, st + D < n, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va,
-                                       vas, vax);
+          gr_load<C, D, PACKED, FUSED>(R, u, st + D, st + D < n, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras,
+                                       va, vas, vax);
         }
       }
     }
@@ -1821,7 +1845,9 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
 // Weight pre-pack for the grouped GEMM: [E][N][K/2] codes and [E][N][K/16]
 // scales -> per (expert, 256-row slab, 256-element K stage) one contiguous
 // block of 256 rows x 128 code bytes (and 256 x 16 scale bytes), rows past N
-// zero.  Inside a code block the 16-byte chunks are in the order the grouped
+// zero, blocks ordered by stage, then expert, then slab: the work-groups on
+// the chip at one time walk neighbouring blocks, which streams faster from
+// HBM than each reading its own slab's run.  Inside a code block the 16-byte chunks are in the order the grouped
 // kernel's lanes load them (wave, column block, sub-step, lane), so each load
 // instruction reads 1 KB in one run; a scale block holds each lane's four
 // scale words in one 16-byte chunk (packed_sf_word).  One 16-byte source chunk
@@ -1862,15 +1888,16 @@ __global__ __launch_bounds__(256) void k_pack_b(const u4_t* __restrict__ b, cons
     const int c = code ? (int)(qq % 8) : 0;
     const int64_t blk = code ? qq / 8 : qq;          // (slab, stage, row)
     const int r = (int)(blk % kPackRows);
-    const int64_t block = blk / kPackRows;           // slab * nst + stage
+    const int64_t block = blk / kPackRows;           // source order: slab * nst + stage
     const int64_t kst = block % nst, slab = block / nst;
     const int64_t e = slab / tiles, row = (slab % tiles) * kPackRows + r;
+    const int64_t dst = kst * ((int64_t)E * tiles) + slab;  // stage-major: stage, then (expert, slab)
     u4_t v = {0u, 0u, 0u, 0u};
     if (row < N) v = code ? b[(e * N + row) * ld16 + kst * 8 + c] : b_sf[(e * N + row) * lds16 + kst];
     if (code) {
-      pb[block * (kPackRows * 8) + packed_chunk(r, c)] = v;
+      pb[dst * (kPackRows * 8) + packed_chunk(r, c)] = v;
     } else {
-      uint32_t* sw = (uint32_t*)(psf + block * kPackRows);
+      uint32_t* sw = (uint32_t*)(psf + dst * kPackRows);
 #pragma unroll
       for (int w = 0; w < 4; ++w) sw[packed_sf_word(r, w)] = v[w];
     }

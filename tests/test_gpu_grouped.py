@@ -153,7 +153,8 @@ def _np_pack(b, bsf, N, K, E):
     pos = (((r // 32) * 2 + (r % 32) // 16) * 2 + c // 4) * 64 + (c % 4) * 16 + r % 16
     out = np.zeros((E, T, n, 2048, 16), np.uint8)
     out[:, :, :, pos.reshape(-1), :] = blocks.reshape(E, T, n, 2048, 16)
-    pb = out.reshape(-1)
+    # blocks in stage-major order: stage, then expert, then slab
+    pb = np.ascontiguousarray(out.transpose(2, 0, 1, 3, 4)).reshape(-1)
     # scale block: word w (bytes 4w .. 4w+3) of row r goes to word position
     # ((((r // 32) * 16 + r % 16) * 2 + w % 2) * 4 + ((r % 32) // 16) * 2 + w // 2
     words = np.ascontiguousarray(sp.reshape(E, T, 256, n, 16).transpose(0, 1, 3, 2, 4)).view(np.uint32)
@@ -162,7 +163,7 @@ def _np_pack(b, bsf, N, K, E):
     wpos = (((r // 32) * 16 + r % 16) * 2 + w % 2) * 4 + ((r % 32) // 16) * 2 + w // 2
     sf = np.zeros((E, T, n, 1024), np.uint32)
     sf[:, :, :, wpos.reshape(-1)] = words.reshape(E, T, n, 1024)
-    psf = sf.view(np.uint8).reshape(-1)
+    psf = np.ascontiguousarray(sf.transpose(2, 0, 1, 3)).view(np.uint8).reshape(-1)
     return pb, psf
 
 
