@@ -443,10 +443,16 @@ def capture(torch, fn):
     return g
 
 
-def replay_us(torch, stream, g, calls, repeats=5):
-    """Median over `repeats` replays of the per-call time (us) of a graph holding `calls` calls."""
-    g.replay()
-    torch.cuda.synchronize()
+def replay_us(torch, stream, g, calls, repeats=5, warm_s=0.05):
+    """Median over `repeats` replays of the per-call time (us) of a graph holding `calls` calls,
+    after untimed replays for at least `warm_s` seconds (at least 3): the clocks ramp up under
+    sustained load, and the inputs of several workloads are built on the host just before."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < warm_s:
+        g.replay()
+        torch.cuda.synchronize()
+        n += 1
     ts = []
     for _ in range(repeats):
         e0 = torch.cuda.Event(enable_timing=True)
