@@ -218,3 +218,18 @@ def test_moe_ffn_single_token_and_empty_experts():
     ref, _ = m.moe_ffn(P["x"], P["gs_x"], P["tok"], P["off"], P["w_gu"], P["w_gu_sf"], P["a_gu"], P["gs_h"],
                        P["w_d"], P["w_d_sf"], P["a_d"], P["tr"], P["tw"], I)
     assert _frob(out, ref) <= 1e-2
+
+
+def test_moe_ffn_tall_experts():
+    # 128 tokens, top-2 of 4 experts: about 64 rows per expert, so both
+    # grouped GEMMs take their 64-row passes
+    T, H, I, E, k = 128, 512, 1024, 4, 2
+    P = _ffn_problem(T, H, I, E, k, seed=700)
+    assert T * k > 40 * E
+    say("moe ffn tall experts", np.diff(P["off"]))
+    out, _ = _run_ffn(P, T, H, I, E, k)
+    ref, _ = m.moe_ffn(P["x"], P["gs_x"], P["tok"], P["off"], P["w_gu"], P["w_gu_sf"], P["a_gu"], P["gs_h"],
+                       P["w_d"], P["w_d_sf"], P["a_d"], P["tr"], P["tw"], I)
+    fr = _frob(out, ref)
+    say("ffn relative Frobenius error", fr)
+    assert fr <= 1e-2
