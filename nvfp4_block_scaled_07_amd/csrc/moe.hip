@@ -53,7 +53,11 @@ __global__ __launch_bounds__(256) void k_swiglu_quantize(const u4_t* __restrict_
 // out[t][c .. c + 7] = bf16( sum_j w[t][j] * down[rows_of[t][j]][c .. c + 7] ),
 // summed in fp32 in j order (one multiply and one add per term, each rounded
 // once); a row index outside [0, rows) contributes nothing.  One thread per
-// 8 output columns of one token.
+// 8 output columns of one token.  The token's rows are taken kCB at a time:
+// all their indices, then all their row loads, are issued before the sums,
+// so a thread waits for two memory round trips per kCB rows, not two per row.
+constexpr int kCB = 8;
+
 __global__ __launch_bounds__(256) void k_moe_combine(const u4_t* __restrict__ down, const int32_t* __restrict__ rows_of,
                                                      const float* __restrict__ wt, u4_t* __restrict__ out, int64_t T,
                                                      int64_t H, int32_t top_k, int64_t rows) {
@@ -64,16 +68,32 @@ __global__ __launch_bounds__(256) void k_moe_combine(const u4_t* __restrict__ do
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int j = 0; j < top_k; ++j) {
-    const int32_t r = rows_of[t * top_k + j];
-    if (r < 0 || r >= rows) continue;
-    const float wj = wt[t * top_k + j];
-    f4_t lo, hi;
-    bf16x8_to_f32(down[(int64_t)r * (H / 8) + c8], lo, hi);
+  for (int j0 = 0; j0 < top_k; j0 += kCB) {
+    int32_t r[kCB];
+    float w[kCB];
+    bool ok[kCB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += wj * lo[e];
-      acc[4 + e] += wj * hi[e];
+    for (int j = 0; j < kCB; ++j) {
+      const bool in = j0 + j < top_k;
+      r[j] = in ? rows_of[t * top_k + j0 + j] : -1;
+      w[j] = in ? wt[t * top_k + j0 + j] : 0.0f;
+    }
+    u4_t v[kCB];
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) {
+      ok[j] = r[j] >= 0 && r[j] < rows;
+      v[j] = ok[j] ? down[(int64_t)r[j] * (H / 8) + c8] : u4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) {
+      if (!ok[j]) continue;
+      f4_t lo, hi;
+      bf16x8_to_f32(v[j], lo, hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w[j] * lo[e];
+        acc[4 + e] += w[j] * hi[e];
+      }
     }
   }
   out[i] = u4_t{f32x2_to_bf16x2_bits(acc[0], acc[1]), f32x2_to_bf16x2_bits(acc[2], acc[3]),
