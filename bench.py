@@ -76,7 +76,7 @@ def main():
         write_traffic_record(*args.traffic, args.requests, "grouped" if args.profile_grouped else args.profile_call)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+        print(json.dumps({"error": "the benchmark runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not implemented", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 

@@ -56,7 +56,7 @@ typedef enum {
   NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
   NVFP4_ERR_SHAPE = 2,       /* negative size, K % 16 != 0, offsets/E invalid */
   NVFP4_ERR_ALIGN = 3,       /* a base pointer is not aligned as documented */
-  NVFP4_ERR_UNSUPPORTED = 4, /* valid NVFP4 call outside this build's shapes (K % 256 != 0, K > 2^22) */
+  NVFP4_ERR_UNSUPPORTED = 4, /* valid NVFP4 call outside the library's supported shapes (K % 256 != 0, K > 2^22) */
   NVFP4_ERR_WORKSPACE = 5,   /* workspace missing or smaller than *_workspace_size() */
   NVFP4_ERR_HIP = 6          /* a HIP runtime call or launch failed */
 } nvfp4_status;

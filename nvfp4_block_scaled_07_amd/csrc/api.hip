@@ -38,11 +38,11 @@ nvfp4_status check_k(int64_t K) {
   if (K % 16 != 0)
     return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of the block size 16", (long long)K);
   if (K % 256 != 0)
-    return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: this build needs K %% 256 == 0", (long long)K);
+    return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: the library needs K %% 256 == 0", (long long)K);
   if (K == 0) return fail(NVFP4_ERR_UNSUPPORTED, "K = 0 is not supported");
   // buffer offsets inside one 256-row operand tile stay below 2^31
   if (K > (int64_t(1) << 22))
-    return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: this build needs K <= 4194304", (long long)K);
+    return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: the library needs K <= 4194304", (long long)K);
   return NVFP4_OK;
 }
 
