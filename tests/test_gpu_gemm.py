@@ -283,3 +283,36 @@ def test_register_tiles_split_k_forced(monkeypatch, M, N, K):
             check_gemm(bits(d), a, asf, b, bsf, np.float32(0.5), f"{key} splits {splits}")
     monkeypatch.delenv("NVFP4_PLAN")
     assert len(seen) >= (4 if K == 256 else 11)
+
+
+def test_maximum_k_every_plan_kind(monkeypatch):
+    # K = 2^22, the largest supported K: a row of codes is 2 MB, so a 256-row
+    # operand tile spans 512 MB of 32-bit buffer offsets.  Every plan kind
+    # (split-K forced to 3 where it applies) on a ragged 17 x 24 output,
+    # against one oracle evaluation.
+    M, N, K = 17, 24, 1 << 22
+    a, b = synth.random_codes(131, M, K), synth.random_codes(132, N, K)
+    asf = synth.random_scale_bytes(133, M, K, lo=0x30, hi=0x40)
+    bsf = synth.random_scale_bytes(134, N, K, lo=0x30, hi=0x40)
+    alpha = np.float32(2.0 ** -6)
+    say("max K oracle")
+    s = o.gemm_fp64(a, asf, b, bsf) * np.float64(alpha)
+    ref = o.bf16_rne(s)
+    tol = o.gemm_tolerance(a, asf, b, bsf, alpha, ref)
+    want = o.bf16_to_f64(ref)
+    at, asft, bt, bsft = dev(a), dev(asf), dev(b), dev(bsf)
+    seen = set()
+    for kind in range(24):
+        for splits in (1, 3):
+            monkeypatch.setenv("NVFP4_PLAN", f"{kind},{splits}")
+            key = (nv.nvfp4_gemm_plan(M, N, K), nv.nvfp4_gemm_workspace_size(M, N, K))
+            if key in seen:
+                continue
+            seen.add(key)
+            say("max K plan", kind, splits, key)
+            d = gpu_gemm(at, asft, bt, bsft, scalar(alpha), M, N, K, d_fill=0x7FC1)
+            got = o.bf16_to_f64(bits(d))
+            assert (np.abs(got - want) <= tol).all(), f"{key}: outside tolerance"
+            assert np.linalg.norm(got - s) / np.linalg.norm(s) <= 1e-2, key
+    monkeypatch.delenv("NVFP4_PLAN")
+    assert len(seen) >= 10
