@@ -196,3 +196,38 @@ def test_fused_degenerate_calls_report_status():
     assert (bits(d) == 0).all()  # expert 0's rows of zero activations; expert 1 skipped
     nv.nvfp4_grouped_gemm_fused(x, None, None, b, bsf, None, None, d, 3, T, N, K, 0, None)
     torch.cuda.synchronize()
+
+
+def test_grouped_paths_at_maximum_k():
+    # K = 2^22 on the plain, packed and fused-packed grouped kernels: 2 experts
+    # of 20 rows (one 256-row slab each, mostly padding), 3 + 5 routed rows
+    E, N, K, T = 2, 20, 1 << 22, 6
+    rng = np.random.default_rng(141)
+    x32 = rng.standard_normal((T, K)).astype(np.float32)
+    xb = _bf16(x32)
+    xq = o.bf16_bits_to_f32(xb)
+    gs = o.global_encode_scale(xq)
+    tok = np.array([5, 0, 2, 2, 1, 4, 3, 0], dtype=np.int32)
+    off = np.array([0, 3, 8], dtype=np.int32)
+    rows = 8
+    b = synth.random_codes(142, E * N, K).reshape(E, N, K // 2)
+    bsf = synth.random_scale_bytes(143, E * N, K, lo=0x30, hi=0x40).reshape(E, N, K // 16)
+    alpha = np.array([2.0 ** -10, 2.0 ** -9], np.float32)
+    qa, sfa = o.quantize(o.gather_rows(xq, tok, rows), gs)
+    b_t, bsf_t, off_t, alpha_t = dev(b), dev(bsf), dev(off), dev(alpha)
+    say("max K grouped: plain")
+    d = torch.full((rows, N), SENTINEL, dtype=torch.int16, device="cuda")
+    nv.nvfp4_grouped_gemm(dev(qa), dev(sfa), b_t, bsf_t, off_t, alpha_t, d, rows, N, K, E, None)
+    got_plain = bits(d)
+    say("max K grouped: packed and fused")
+    pb, psf = nv.grouped_pack(b_t, bsf_t, N, K, E)
+    del b_t, bsf_t
+    d2 = torch.full((rows, N), SENTINEL, dtype=torch.int16, device="cuda")
+    nv.nvfp4_grouped_gemm_packed(dev(qa), dev(sfa), pb, psf, off_t, alpha_t, d2, rows, N, K, E)
+    d3, st = _fused(dev(xb.view(np.int16)), dev(tok), scalar(gs), pb, psf, off_t, alpha_t, rows, T, N, K, E, True)
+    assert int(host(st)[0]) == 0
+    np.testing.assert_array_equal(bits(d2), got_plain)
+    np.testing.assert_array_equal(bits(d3), got_plain)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        check_gemm(got_plain[lo:hi], qa[lo:hi], sfa[lo:hi], b[e], bsf[e], alpha[e], f"max K expert {e}")
