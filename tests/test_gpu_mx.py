@@ -99,3 +99,31 @@ def test_zero_sized_and_bad_k():
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.nvfp4_mx_gemm(x, x, x, x, None, d, 4, 8, 48)
     assert e.value.status == 2
+
+
+def test_every_mx_plan_at_maximum_k(monkeypatch):
+    # K = 2^22 (2 MB code rows, 128 KB scale rows) on every MX plan, with and
+    # without split-K, against one oracle evaluation
+    M, N, K = 17, 24, 1 << 22
+    a, asf, b, bsf = _operands(7300, M, N, K)
+    alpha = np.float32(2.0 ** -8)
+    say("mx max K oracle")
+    s = mx.gemm_fp64(a, asf, b, bsf) * np.float64(alpha)
+    ref = o.bf16_rne(s)
+    tol = mx.gemm_tolerance(a, asf, b, bsf, alpha, ref)
+    want = o.bf16_to_f64(ref)
+    at, asft, bt, bsft = dev(a), dev(asf), dev(b), dev(bsf)
+    seen = set()
+    for kind in range(10):
+        for splits in (1, 3):
+            monkeypatch.setenv("NVFP4_MX_PLAN", f"{kind},{splits}")
+            key = (nv.nvfp4_mx_gemm_plan(M, N, K), nv.nvfp4_mx_gemm_workspace_size(M, N, K))
+            if key in seen:
+                continue
+            seen.add(key)
+            say("mx max K plan", kind, splits, key)
+            got = o.bf16_to_f64(bits(_mx_gemm(at, asft, bt, bsft, scalar(alpha), M, N, K)))
+            assert (np.abs(got - want) <= tol).all(), f"{key}: outside tolerance"
+            assert np.linalg.norm(got - s) / np.linalg.norm(s) <= 1e-2, key
+    monkeypatch.delenv("NVFP4_MX_PLAN")
+    assert len(seen) >= 8
