@@ -57,6 +57,10 @@ def main():
     ap.add_argument("--profile-mx", type=int, default=0, metavar="M",
                     help="for profiler runs: the MXFP4 GEMM M x 6144 x 6144 (graph of 10 calls, replayed 6 times); "
                          "prints its time")
+    ap.add_argument("--profile-quantize", action="store_true",
+                    help="run only the quantiser workload (16384 x 6144 fp32) as the bench times it, for a profiler")
+    ap.add_argument("--profile-fused", action="store_true",
+                    help="run only the fused-quantisation grouped call (512 tokens, packed weights), for a profiler")
     ap.add_argument("--profile-moe", action="store_true",
                     help="run only the MoE expert FFN layer (512 tokens, top-8 of 256 experts) as the bench times "
                          "it, for a profiler")
@@ -128,6 +132,14 @@ def main():
         return
     if args.profile_mx:
         profile_mx(torch, nv, synth, stream, args.profile_mx)
+        return
+    if args.profile_quantize:
+        us, by = quantize_workload(nv, torch, dev, stream, synth)
+        print(json.dumps({"call": "nvfp4_quantize 16384 x 6144", "us_per_call": round(us, 2),
+                          "gbps": round(by / us / 1e3, 1)}), flush=True)
+        return
+    if args.profile_fused:
+        print(json.dumps(fused_grouped_workload(nv, torch, dev, stream, synth, quantise)), flush=True)
         return
     if args.profile_moe:
         print(json.dumps(moe_ffn_workload(nv, torch, dev, stream, synth)), flush=True)
@@ -631,15 +643,35 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
                                              "dequantised; context only", shapes=ref)
 
     # quantiser (prologue): 16384 x 6144 fp32 -> NVFP4
+    us, by = quantize_workload(nv, torch, dev, stream, synth)
+    res["quantize_16384x6144"] = dict(us=round(us, 2), gbps=round(by / us / 1e3, 1),
+                                      frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4))
+    return res
+
+
+def quantize_workload(nv, torch, dev, stream, synth):
+    """nvfp4_quantize on 16384 x 6144 fp32 activations (gs = 1), timed as a
+    graph of 10 calls; returns (us per call, bytes moved per call)."""
     x = torch.from_numpy(synth.normal_f32(4001, (16384, 6144))).to(dev)
     q = torch.empty((16384, 3072), dtype=torch.uint8, device=dev)
     sf = torch.empty((16384, 384), dtype=torch.uint8, device=dev)
     gs = torch.ones(1, dtype=torch.float32, device=dev)
     us = timed(torch, stream, lambda i: nv.nvfp4_quantize(x, 16384, 6144, gs, q, sf), 10)
-    by = 16384 * 6144 * (4 + 0.5 + 1 / 16)
-    res["quantize_16384x6144"] = dict(us=round(us, 2), gbps=round(by / us / 1e3, 1),
-                                      frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4))
-    return res
+    return us, 16384 * 6144 * (4 + 0.5 + 1 / 16)
+
+
+def fused_grouped_workload(nv, torch, dev, stream, synth, quantise):
+    """The 512-token grouped call from bf16 token activations with the gather
+    and quantisation fused into the A load (packed weights), timed as a graph
+    of 10 calls."""
+    gi = grouped_inputs(torch, nv, synth, quantise, dev)
+    rows, N, K, E, T = gi["rows"], gi["N"], gi["K"], gi["E"], gi["T"]
+    pb, psf = nv.grouped_pack(gi["b"], gi["bsf"], N, K, E)
+    del gi["b"], gi["bsf"]
+    torch.cuda.empty_cache()
+    us = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_packed_fused(
+        gi["x_bf16"], gi["tok"], gi["gsa"], pb, psf, gi["off"], gi["alpha"], gi["d"], rows, T, N, K, E), 10)
+    return dict(call=f"nvfp4_grouped_gemm_packed_fused rows={rows} T={T} N={N} K={K} E={E}", us_per_call=round(us, 2))
 
 
 def moe_ffn_workload(nv, torch, dev, stream, synth):
