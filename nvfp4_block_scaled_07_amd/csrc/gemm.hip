@@ -33,6 +33,12 @@
 //    (device-scope counter) sums the partials in split order, applies alpha
 //    and stores bf16, then resets the counter.  One launch, bitwise
 //    deterministic.
+//  * Register streaming: small-M tiles (k_gemm_kreg) and the grouped MoE
+//    kernels (k_grouped_reg) load operands straight into VGPRs in whole
+//    128-byte lines per row, two or three 256-element K units ahead, and put
+//    them into MFMA layout with one DPP exchange; there the number of reads
+//    a CU keeps in flight, not LDS, bounds the rate.  Expert weights can be
+//    packed once (k_pack_b) into the grouped kernel's lane order.
 //  * Work-group order is remapped so that work-groups sharing operand rows
 //    run on the same XCD (its own 4 MB L2).
 #include <limits.h>
