@@ -255,6 +255,26 @@ nvfp4_status nvfp4_moe_ffn(const uint16_t* x, const float* gs_x, const int32_t* 
                            size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
+ * Scale-layout interop.  The pages only name the switch between scale
+ * layouts ("The Art of Reading the Manual: Debugging FP4 GEMM Kernels on
+ * Blackwell SM120", section "The Message": use_8x4_sf_layout=False); this
+ * library takes linear [rows][K/16] scales.  These calls convert to and from
+ * the 128 x 4 tiled layout of the CUTLASS NVFP4 path (read as: the scale
+ * matrix, zero-padded to a multiple of 128 rows and 4 columns, stored as
+ * 512-byte tiles of 128 rows x 4 columns in row-major tile order, the scale
+ * of row r and column c of a tile at byte (r % 32) * 16 + ((r % 128) / 32) * 4
+ * + c % 4), for example once at weight-load time.
+ *
+ * nvfp4_scales_128x4_size: bytes of the tiled layout for rows x K (K % 16 ==
+ * 0; 0 for invalid sizes).  nvfp4_scales_to_128x4: sf uint8 [rows][K/16] ->
+ * tiled (padding written as zero).  nvfp4_scales_from_128x4: tiled -> sf.
+ * Device pointers, no alignment requirement; asynchronous on stream.
+ */
+size_t nvfp4_scales_128x4_size(int64_t rows, int64_t K);
+nvfp4_status nvfp4_scales_to_128x4(const uint8_t* sf, uint8_t* tiled, int64_t rows, int64_t K, void* stream);
+nvfp4_status nvfp4_scales_from_128x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, void* stream);
+
+/*
  * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
  * The pages never quantise (their test used random bytes); this follows the
  * block_size 16 and e4m3fn scale format of the pages above with these steps,

@@ -45,6 +45,9 @@ SIGNATURES = {
     "nvfp4_moe_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "nvfp4_moe_ffn": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                      _i64, _i64, _i32, _i32, _vp, _sz, _vp, _vp]),
+    "nvfp4_scales_128x4_size": (_sz, [_i64, _i64]),
+    "nvfp4_scales_to_128x4": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "nvfp4_scales_from_128x4": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_global_scale": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_alpha_from_scales": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
@@ -271,6 +274,23 @@ def nvfp4_moe_ffn(x, gs_x, row_token, offsets, w_gu, w_gu_sf, alpha_gu, gs_h, w_
                              _ptr(status), _stream(stream))
     _check(st, "nvfp4_moe_ffn")
     return out
+
+
+def nvfp4_scales_128x4_size(rows: int, K: int) -> int:
+    return int(lib().nvfp4_scales_128x4_size(rows, K))
+
+
+def nvfp4_scales_to_128x4(sf, tiled, rows: int, K: int, stream=None):
+    """Linear [rows][K/16] scales -> the 128 x 4 tiled layout."""
+    _check(lib().nvfp4_scales_to_128x4(_ptr(sf), _ptr(tiled), rows, K, _stream(stream)), "nvfp4_scales_to_128x4")
+    return tiled
+
+
+def nvfp4_scales_from_128x4(tiled, sf, rows: int, K: int, stream=None):
+    """The 128 x 4 tiled layout -> linear [rows][K/16] scales."""
+    _check(lib().nvfp4_scales_from_128x4(_ptr(tiled), _ptr(sf), rows, K, _stream(stream)),
+           "nvfp4_scales_from_128x4")
+    return sf
 
 
 def nvfp4_quantize(x, R: int, K: int, global_scale, q, sf, stream=None):

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnvfp4_gfx950.so")
-SOURCES = ["api.hip", "gemm.hip", "moe.hip", "quantize.hip"]
+SOURCES = ["api.hip", "gemm.hip", "layout.hip", "moe.hip", "quantize.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -418,6 +418,27 @@ nvfp4_status nvfp4_moe_ffn(const uint16_t* x, const float* gs_x, const int32_t* 
   return hip_status(e, "nvfp4_moe_ffn launch");
 }
 
+size_t nvfp4_scales_128x4_size(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0 || K % 16) return 0;
+  return nvfp4::tiled128x4_bytes(rows, K);
+}
+
+nvfp4_status nvfp4_scales_to_128x4(const uint8_t* sf, uint8_t* tiled, int64_t rows, int64_t K, void* stream) {
+  if (rows < 0 || K < 0 || K % 16) return fail(NVFP4_ERR_SHAPE, "rows >= 0 and K >= 0 with K %% 16 == 0 required");
+  if (rows == 0 || K == 0) return ok();
+  if (!sf || !tiled) return fail(NVFP4_ERR_NULL, "sf and tiled must be non-NULL");
+  return hip_status(nvfp4::launch_scales_to_128x4(sf, tiled, rows, K, (hipStream_t)stream),
+                    "nvfp4_scales_to_128x4 launch");
+}
+
+nvfp4_status nvfp4_scales_from_128x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, void* stream) {
+  if (rows < 0 || K < 0 || K % 16) return fail(NVFP4_ERR_SHAPE, "rows >= 0 and K >= 0 with K %% 16 == 0 required");
+  if (rows == 0 || K == 0) return ok();
+  if (!sf || !tiled) return fail(NVFP4_ERR_NULL, "sf and tiled must be non-NULL");
+  return hip_status(nvfp4::launch_scales_from_128x4(tiled, sf, rows, K, (hipStream_t)stream),
+                    "nvfp4_scales_from_128x4 launch");
+}
+
 nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K, const float* global_scale, uint8_t* q,
                             uint8_t* sf, void* stream) {
   if (R < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "R = %lld, K = %lld must be >= 0", (long long)R, (long long)K);

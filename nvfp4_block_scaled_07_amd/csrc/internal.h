@@ -74,6 +74,11 @@ hipError_t launch_swiglu_quantize(const uint16_t* gu, int64_t rows, int64_t I, c
 hipError_t launch_moe_combine(const uint16_t* down, const int32_t* rows_of, const float* wt, uint16_t* out,
                               int64_t T, int64_t H, int32_t top_k, int64_t rows, hipStream_t stream);
 
+// Scale layout interop (layout.hip): linear [rows][K/16] <-> 128 x 4 tiles.
+size_t tiled128x4_bytes(int64_t rows, int64_t K);
+hipError_t launch_scales_to_128x4(const uint8_t* sf, uint8_t* tiled, int64_t rows, int64_t K, hipStream_t stream);
+hipError_t launch_scales_from_128x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, hipStream_t stream);
+
 hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs, uint8_t* q, uint8_t* sf,
                            hipStream_t stream);
 // bf16 rows x[row_token[i]] (x[i] if row_token is NULL) -> NVFP4 [rows][K/2], [rows][K/16].

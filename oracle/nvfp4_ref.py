@@ -300,6 +300,41 @@ def grouped_gemm_fused(x_bits, row_token, gs, b, b_sf, offsets, alpha, d_init, r
 
 
 # ---------------------------------------------------------------------------
+# Interop: the 128 x 4 tiled scale layout.  The pages only name the switch
+# between scale layouts (P2 "The Message": use_8x4_sf_layout=False) and never
+# describe one.  READING: the tiled layout used by the CUTLASS NVFP4 path:
+# the [rows][K/16] scale matrix, padded with zeros to a multiple of 128 rows
+# and 4 columns, is stored as 512-byte tiles of 128 rows x 4 columns, tiles
+# in row-major order; inside a tile, the scale of row r and column c sits at
+# byte (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4.
+# ---------------------------------------------------------------------------
+def tiled128x4_size(rows: int, K: int) -> int:
+    return (-(-rows // 128) * 128) * (-(-(K // 16) // 4) * 4)
+
+
+def scales_to_128x4(sf: np.ndarray) -> np.ndarray:
+    """Linear ``uint8[rows][K/16]`` -> the 128 x 4 tiled byte sequence."""
+    rows, cols = sf.shape
+    tr, tc = -(-rows // 128), -(-cols // 4)
+    out = np.zeros(tr * tc * 512, dtype=np.uint8)
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    pos = ((r // 128) * tc + c // 4) * 512 + (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
+    out[pos] = sf
+    return out
+
+
+def scales_from_128x4(tiled: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """The 128 x 4 tiled byte sequence -> linear ``uint8[rows][K/16]``."""
+    cols = K // 16
+    tc = -(-cols // 4)
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    pos = ((r // 128) * tc + c // 4) * 512 + (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
+    return np.asarray(tiled, dtype=np.uint8)[pos]
+
+
+# ---------------------------------------------------------------------------
 # Exact integer mode (an independent check of the fp64 path).
 # ---------------------------------------------------------------------------
 def _int_tables():

@@ -235,3 +235,15 @@ def test_missing_library_raises_and_nothing_falls_back(monkeypatch, tmp_path):
         if f.endswith(".py"):
             src = open(os.path.join(pkg, f)).read()
             assert "oracle" not in src.replace("no CPU or PyTorch fallback", ""), f
+
+
+def test_scale_layout_error_paths_and_sizes():
+    L = nv.lib()
+    assert L.nvfp4_scales_128x4_size(130, 80) == 256 * 8
+    assert L.nvfp4_scales_128x4_size(1, 16) == 512
+    assert L.nvfp4_scales_128x4_size(4, 40) == 0
+    assert L.nvfp4_scales_to_128x4(FAKE, FAKE, 4, 40, None) == 2
+    assert L.nvfp4_scales_to_128x4(None, FAKE, 4, 64, None) == 1
+    assert L.nvfp4_scales_from_128x4(FAKE, None, 4, 64, None) == 1
+    assert L.nvfp4_scales_from_128x4(FAKE, FAKE, -1, 64, None) == 2
+    assert L.nvfp4_scales_to_128x4(None, None, 0, 64, None) == 0
