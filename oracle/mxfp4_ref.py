@@ -102,9 +102,4 @@ def gemm_tolerance(a, a_sf, b, b_sf, alpha, d_ref_bits) -> np.ndarray:
     """Per-element bound: 2 bf16 ulps of the reference plus the probabilistic
     fp32 summation error 8 |alpha| sqrt(K) 2**-24 ||(xA xB)_k||_2, the same
     form as the NVFP4 bound (the hardware accumulates in fp32)."""
-    xa = dequant(a, a_sf)
-    xb = dequant(b, b_sf)
-    K = xa.shape[1]
-    l2 = np.sqrt((xa * xa) @ (xb * xb).T)
-    floor = 8.0 * abs(float(np.float32(alpha))) * math.sqrt(K) * 2.0 ** -24 * l2
-    return 2.0 * nv.bf16_ulp(d_ref_bits) + floor
+    return nv.tolerance_dequantized(dequant(a, a_sf), dequant(b, b_sf), alpha, d_ref_bits)

@@ -41,9 +41,11 @@ Storage conventions:
   bits 4-7 of byte j.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.  One
-function is "parity unpinned": :func:`page_smoke_magnitudes` has no inputs the
-pages print, so only the bf16-representability of the printed numbers is
-checked.
+part is "parity unpinned": the 128 x 4 tiled scale layout
+(:func:`scales_to_128x4`, :func:`scales_from_128x4`) and the 8 x 4 one
+(:func:`scales_to_8x4`, :func:`scales_from_8x4`) are readings of layouts the
+pages only name; their tests check the index formulas against independent
+restatements, which catches slips but not a wrong reading.
 """
 from __future__ import annotations
 
@@ -334,6 +336,36 @@ def scales_from_128x4(tiled: np.ndarray, rows: int, K: int) -> np.ndarray:
     return np.asarray(tiled, dtype=np.uint8)[pos]
 
 
+# The 8 x 4 layout: the other swizzled layout that the ``use_8x4_sf_layout``
+# switch of P2 "The Message" names (the pages describe neither).  READING:
+# the scale matrix, padded with zeros to a multiple of 8 rows and 4 columns,
+# is stored as 32-byte tiles of 8 rows x 4 columns, tiles in row-major order;
+# inside a tile, the scale of row r and column c sits at byte
+# (r % 8) * 4 + c % 4.  Parity unpinned (a reading, as for the 128 x 4 one).
+def tiled8x4_size(rows: int, K: int) -> int:
+    return (-(-rows // 8) * 8) * (-(-(K // 16) // 4) * 4)
+
+
+def _pos_8x4(rows: int, cols: int) -> np.ndarray:
+    tc = -(-cols // 4)
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    return ((r // 8) * tc + c // 4) * 32 + (r % 8) * 4 + c % 4
+
+
+def scales_to_8x4(sf: np.ndarray) -> np.ndarray:
+    """Linear ``uint8[rows][K/16]`` -> the 8 x 4 tiled byte sequence."""
+    rows, cols = sf.shape
+    out = np.zeros(tiled8x4_size(rows, 16 * cols), dtype=np.uint8)
+    out[_pos_8x4(rows, cols)] = sf
+    return out
+
+
+def scales_from_8x4(tiled: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """The 8 x 4 tiled byte sequence -> linear ``uint8[rows][K/16]``."""
+    return np.asarray(tiled, dtype=np.uint8)[_pos_8x4(rows, K // 16)]
+
+
 # ---------------------------------------------------------------------------
 # Exact integer mode (an independent check of the fp64 path).
 # ---------------------------------------------------------------------------
@@ -379,17 +411,13 @@ def gemm_tolerance(a, a_sf, b, b_sf, alpha, d_ref_bits) -> np.ndarray:
     the target plus the probabilistic fp32 summation error (Higham-Mary,
     sqrt(K) u times the 2-norm of the terms), which no fp32 accumulator can
     avoid where the sum cancels."""
-    xa = dequant(a, a_sf)
-    xb = dequant(b, b_sf)
+    return tolerance_dequantized(dequant(a, a_sf), dequant(b, b_sf), alpha, d_ref_bits)
+
+
+def tolerance_dequantized(xa, xb, alpha, d_ref_bits) -> np.ndarray:
+    """The bound of :func:`gemm_tolerance` from the dequantised operands
+    ``xa [M][K]``, ``xb [N][K]`` (fp64)."""
     K = xa.shape[1]
     l2 = np.sqrt((xa * xa) @ (xb * xb).T)
     floor = 8.0 * abs(float(np.float32(alpha))) * math.sqrt(K) * 2.0 ** -24 * l2
     return 2.0 * bf16_ulp(d_ref_bits) + floor
-
-
-def page_smoke_magnitudes() -> tuple:
-    """The only numbers the pages print for the kernel's output (P1 "The
-    Results: A Correction": abs_max 18743296, abs_mean 626688 for M=128,
-    N=256, K=256 with random scales).  Parity unpinned: the inputs are not
-    printed; a test only checks both numbers are exact bf16 values."""
-    return 18743296.0, 626688.0
