@@ -1,18 +1,21 @@
 """Benchmark of the gfx950 NVFP4 block-scaled GEMM.
 
-One step = one pass of the attention-projection sweep of the pages (M in
-{16, 32, 64, 128, 256, 512, 1024} x N = 768 x K = 6144, bf16 out): seven
-``nvfp4_gemm`` calls on inputs already quantised and resident in HBM.  Each
-step uses the next of several rotating buffer sets (together more than twice
-the 256 MB Infinity Cache), so weights stream from HBM as in a real decode
-pass over many layers.  ``value`` is the step's total TFLOPS (2*M*N*K summed
-over the sweep / step time).
+One step = one pass over the pages' single-GEMM workloads across the metric's
+range M = 16..8192: the attention projections (M in {16, 32, 64, 128, 256,
+512, 1024} x N = 768 x K = 6144), the MoE expert shapes (M in {16, 32, 64,
+256, 1024} x N = 2048 x K = 6144) and the compute-bound shapes (M in {4096,
+8192} x N = 6144 x K = 6144): fourteen ``nvfp4_gemm`` calls on inputs already
+quantised and resident in HBM.  Each call of a step reads the next of several
+rotating buffer sets of its workload (each workload's sets together more than
+twice the 256 MB Infinity Cache), so operands stream from HBM as in a real
+pass over many layers.  ``value`` is the step's TFLOPS (2*M*N*K summed over
+the fourteen calls / step time).
 
 Printed as one JSON line, with per-shape results, the roofline of the
 dominant call (timed with HIP events on the stream it runs on), the other
-workloads of the pages (MoE expert sweep, large compute-bound shapes, the
-grouped 256-expert MoE GEMM, the quantiser), and the CPU oracle timed on a
-bounded sample of the same sweep.
+workloads of the pages (M = 16384, the grouped 256-expert MoE GEMM, the MoE
+expert FFN, MXFP4, the vendor bf16 GEMM at every shape, the quantiser), and
+the CPU oracle timed on one or more passes of the same step.
 """
 from __future__ import annotations
 
@@ -29,11 +32,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "NVFP4 GEMM TFLOPS & % roofline (MFMA peak or HBM GB/s), M=16..8192"
-PEAK_F16_TFLOPS = 2500.0      # dense f16 MFMA, MI355X
-PEAK_FP4_TFLOPS = 10100.0     # dense fp4 MFMA, MI355X (context: not the issued instruction)
+PEAK_FP4_TFLOPS = 10100.0     # dense FP4 MFMA, MI355X: the roofline's compute peak
+PEAK_F16_TFLOPS = 2500.0      # dense f16 MFMA, MI355X: the instruction the exact path issues
 PEAK_HBM_GBPS = 8000.0
 ROTATE_BYTES = 600 << 20      # > 2 x 256 MB Infinity Cache
 GRAPH_STEPS = 8               # steps captured per HIP graph
+
+# the step: (workload, the M values it contributes)
+STEP = (("attn_proj_n768_k6144", (16, 32, 64, 128, 256, 512, 1024)),
+        ("moe_expert_n2048_k6144", (16, 32, 64, 256, 1024)),
+        ("large_n6144_k6144", (4096, 8192)))
 
 
 def algo_bytes(M, N, K):
@@ -41,16 +49,31 @@ def algo_bytes(M, N, K):
     return (M + N) * K * 9 // 16 + 2 * M * N + 4
 
 
+def roofline_frac(flops, nbytes, us):
+    """max(flops / dense FP4 peak, bytes / HBM bandwidth) / measured time."""
+    return max(flops / (PEAK_FP4_TFLOPS * 1e6), nbytes / (PEAK_HBM_GBPS * 1e3)) / us
+
+
+def shape_row(nv, m, n, k, us, **extra):
+    fl, by = 2.0 * m * n * k, algo_bytes(m, n, k)
+    return dict(M=m, N=n, K=k, plan=nv.nvfp4_gemm_plan(m, n, k), us=round(us, 3),
+                tflops=round(fl / us / 1e6, 2), gbps=round(by / us / 1e3, 1),
+                frac_roofline=round(roofline_frac(fl, by, us), 4),
+                frac_f16_mfma=round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4),
+                frac_hbm=round(by / us / 1e3 / PEAK_HBM_GBPS, 4), **extra)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the CPU baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", default="attn_proj_n768_k6144", help="workload of --profile-call")
     ap.add_argument("--profile-call", type=int, default=0, metavar="M",
                     help="for hardware-counter runs: one 256 MiB device copy (counter calibration), then 8 "
-                         "cold calls of the headline GEMM at this M; prints nothing else")
+                         "cold calls of the --workload GEMM at this M; prints nothing else")
     ap.add_argument("--profile-grouped", action="store_true",
                     help="for profiler runs: one 256 MiB device copy (counter calibration), then the grouped "
                          "MoE GEMM on packed weights (graph of 10 calls, replayed 4 times); prints its time")
@@ -65,7 +88,7 @@ def main():
                     help="run only the MoE expert FFN layer (512 tokens, top-8 of 256 experts) as the bench times "
                          "it, for a profiler")
     ap.add_argument("--graph", action="store_true",
-                    help="with --profile-call: time the call as the headline does (graphs of 64 calls over "
+                    help="with --profile-call: time the call as the bench does (graphs of back-to-back calls over "
                          "the rotating sets, replayed 8 times) instead of 8 eager calls")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --profile-call or "
@@ -77,7 +100,8 @@ def main():
     if args.traffic:
         if not args.profile_call and not args.profile_grouped:
             raise SystemExit("--traffic needs the --profile-call M or --profile-grouped the counters were taken with")
-        write_traffic_record(*args.traffic, args.requests, "grouped" if args.profile_grouped else args.profile_call)
+        write_traffic_record(*args.traffic, args.requests,
+                             "grouped" if args.profile_grouped else (args.workload, args.profile_call))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only; multi-GPU sharding is a design note, "
@@ -104,11 +128,16 @@ def main():
         nv.nvfp4_quantize(xt, R, K, gs, q, sf)
         return q, sf, gs
 
-    def sweep_inputs(name, rotate=True):
-        w = synth.WORKLOADS[name]
-        a, b = synth.single_operands(name)
+    def sweep_inputs(name, ms=None, rotate=True):
+        """Quantised operands of a workload (A at the largest M used), copied
+        into rotating buffer sets of more than ROTATE_BYTES together, plus
+        the alpha, outputs and workspaces of its M values."""
+        w = dict(synth.WORKLOADS[name])
+        w["ms"] = tuple(ms or w["ms"])
+        a, b = synth.single_operands(name, max(w["ms"]))
         qa, sfa, gsa = quantise(a)
         qb, sfb, gsb = quantise(b)
+        del a, b
         alpha = torch.empty(1, dtype=torch.float32, device=dev)
         nv.nvfp4_alpha_from_scales(gsa, gsb, alpha, 1)
         per_set = sum(t.numel() for t in (qa, sfa, qb, sfb))
@@ -125,7 +154,7 @@ def main():
         nv.nvfp4_gemm(qa[:m], sfa[:m], qb, sfb, alpha, outs[m], m, w["n"], w["k"], wss[m])
 
     if args.profile_call:
-        profile_call(torch, nv, sweep_inputs, call, args.profile_call, args.graph)
+        profile_call(torch, nv, sweep_inputs, call, args.workload, args.profile_call, args.graph)
         return
     if args.profile_grouped:
         profile_grouped(torch, nv, synth, quantise, stream)
@@ -145,20 +174,23 @@ def main():
         print(json.dumps(moe_ffn_workload(nv, torch, dev, stream, synth)), flush=True)
         return
 
-    # ---------------- headline: attention-projection sweep -----------------
-    # Steps are captured into HIP graphs, GRAPH_STEPS consecutive steps (each
-    # on the next buffer set) per graph, as a serving loop would capture a
-    # whole pass; single-step graphs cover a remainder.  The host enqueues one
-    # replay per GRAPH_STEPS steps and the GPU never waits on Python.
-    name = "attn_proj_n768_k6144"
-    w, sets, alpha, outs, wss = sweep_inputs(name)
-    ms = list(w["ms"])
-    N, K = w["n"], w["k"]
-    G = min(GRAPH_STEPS, len(sets))
-    multi = [capture(torch, lambda j=j: [call(w, sets[(j * G + t) % len(sets)], alpha, outs, wss, m)
-                                         for t in range(G) for m in ms])
-             for j in range((len(sets) + G - 1) // G)]
-    single = [capture(torch, lambda t=t: [call(w, sets[t], alpha, outs, wss, m) for m in ms]) for t in range(G)]
+    # ------------------------------- the step -------------------------------
+    # Steps are captured into HIP graphs, GRAPH_STEPS consecutive steps per
+    # graph, as a serving loop would capture a whole pass; step j reads buffer
+    # set j of each workload (modulo its count).  The host enqueues one replay
+    # per GRAPH_STEPS steps and the GPU never waits on Python.
+    inputs = [(name, ms) + sweep_inputs(name, ms) for name, ms in STEP]
+    period = int(np.lcm.reduce([len(inp[3]) for inp in inputs]))   # steps until the set pattern repeats
+    G = GRAPH_STEPS
+
+    def step(j):
+        for name, ms, w, sets, alpha, outs, wss in inputs:
+            for m in ms:
+                call(w, sets[j % len(sets)], alpha, outs, wss, m)
+
+    ngraphs = min(max(1, -(-period // G)), 16)
+    multi = [capture(torch, lambda j=j: [step(j * G + t) for t in range(G)]) for j in range(ngraphs)]
+    single = [capture(torch, lambda t=t: step(t)) for t in range(G)]
 
     def run_steps(n, first):
         i = 0
@@ -181,60 +213,59 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
     ms_per_step = wall * 1e3 / args.steps
-    flops_step = sum(2.0 * m * N * K for m in ms)
+    flops_step = sum(2.0 * m * inp[2]["n"] * inp[2]["k"] for inp in inputs for m in inp[1])
     value = flops_step / (ms_per_step * 1e-3) / 1e12
+    del multi, single
 
     # per-call durations: a graph of back-to-back calls of one shape over the
     # rotating sets, timed with HIP events on the launch stream
     shapes = []
-    for m in ms:
-        reps = min(len(sets), 64)
-        g = capture(torch, lambda: [call(w, sets[i], alpha, outs, wss, m) for i in range(reps)])
-        t_us = replay_us(torch, stream, g, reps)
-        del g
-        # the same calls on one buffer set (operands L2 / Infinity Cache resident)
-        g = capture(torch, lambda: [call(w, sets[0], alpha, outs, wss, m) for _ in range(reps)])
-        t_warm = replay_us(torch, stream, g, reps)
-        fl = 2.0 * m * N * K
-        by = algo_bytes(m, N, K)
-        shapes.append(dict(M=m, N=N, K=K, plan=nv.nvfp4_gemm_plan(m, N, K), us=round(t_us, 3), us_warm=round(t_warm, 3),
-                           tflops=round(fl / t_us / 1e6, 2), gbps=round(by / t_us / 1e3, 1),
-                           frac_f16_mfma=round(fl / t_us / 1e6 / PEAK_F16_TFLOPS, 4),
-                           frac_fp4_peak=round(fl / t_us / 1e6 / PEAK_FP4_TFLOPS, 4),
-                           frac_hbm=round(by / t_us / 1e3 / PEAK_HBM_GBPS, 4)))
-        del g
+    for name, ms, w, sets, alpha, outs, wss in inputs:
+        for m in ms:
+            reps = min(len(sets), 64)
+            g = capture(torch, lambda: [call(w, sets[i], alpha, outs, wss, m) for i in range(reps)])
+            t_us = replay_us(torch, stream, g, reps)
+            del g
+            # the same calls on one buffer set (operands L2 / Infinity Cache resident)
+            g = capture(torch, lambda: [call(w, sets[0], alpha, outs, wss, m) for _ in range(reps)])
+            t_warm = replay_us(torch, stream, g, reps)
+            del g
+            shapes.append(shape_row(nv, m, w["n"], w["k"], t_us, workload=name, us_warm=round(t_warm, 3)))
     dom = max(shapes, key=lambda r: r["us"])
-    fl = 2.0 * dom["M"] * N * K
-    by = algo_bytes(dom["M"], N, K)
-    mfma_bound = fl / by > PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    call_name = f"nvfp4_gemm M={dom['M']} N={N} K={K}"
-    traffic = read_traffic_record(TRAFFIC_RECORD, f"{call_name} ({dom['plan']})")
-    if mfma_bound:
-        roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_F16_TFLOPS, unit="TFLOP/s",
-                        frac=round(dom["tflops"] / PEAK_F16_TFLOPS, 4), traffic=traffic,
-                        kernel_call=f"{call_name} ({dom['plan']})", algorithmic_bytes=by,
-                        algorithmic_flops=fl)
-    else:
-        roofline = dict(bound="hbm", achieved=dom["gbps"], peak=PEAK_HBM_GBPS, unit="GB/s",
-                        frac=round(dom["gbps"] / PEAK_HBM_GBPS, 4), traffic=traffic,
-                        kernel_call=f"{call_name} ({dom['plan']})", algorithmic_bytes=by,
-                        algorithmic_flops=fl)
+    fl = 2.0 * dom["M"] * dom["N"] * dom["K"]
+    by = algo_bytes(dom["M"], dom["N"], dom["K"])
+    call_name = f"nvfp4_gemm M={dom['M']} N={dom['N']} K={dom['K']} ({dom['plan']})"
+    traffic = read_traffic_record(traffic_record_path(dom["workload"], dom["M"]), call_name)
+    mfma_bound = fl / (PEAK_FP4_TFLOPS * 1e6) >= by / (PEAK_HBM_GBPS * 1e3)
+    roofline = dict(bound="mfma" if mfma_bound else "hbm",
+                    achieved=dom["tflops"] if mfma_bound else dom["gbps"],
+                    peak=PEAK_FP4_TFLOPS if mfma_bound else PEAK_HBM_GBPS,
+                    unit="TFLOP/s" if mfma_bound else "GB/s",
+                    frac=round(roofline_frac(fl, by, dom["us"]), 4), traffic=traffic,
+                    kernel_call=call_name, us=dom["us"], algorithmic_bytes=by, algorithmic_flops=fl,
+                    frac_f16_mfma_issued=round(dom["tflops"] / PEAK_F16_TFLOPS, 4),
+                    note="frac = max(flops / dense FP4 peak, bytes / 8 TB/s) / time of the dominant call; the exact "
+                         "NVFP4 path issues f16 MFMAs (e4m3 scales per 16 elements are not powers of two), whose "
+                         "dense peak is 2.5 PFLOP/s: frac_f16_mfma_issued")
     # launch floor: a graph of 64 one-element fills (the smallest kernel)
     tiny = torch.zeros(1, dtype=torch.float32, device=dev)
     g = capture(torch, lambda: [tiny.fill_(float(i)) for i in range(64)])
     launch_floor = replay_us(torch, stream, g, 64)
     del g, tiny
-    del multi, single
-    del sets, outs, wss
+    del inputs
     torch.cuda.empty_cache()
 
     out = dict(metric=METRIC, value=round(value, 3), unit="TFLOPS", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_per_step, 5), gpu_ms_per_step=round(gpu_ms / args.steps, 5),
                higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="f16", data="synthetic",
-               config=dict(workload=f"{name}: nvfp4_gemm M in {ms} x N={N} x K={K}, bf16 out, "
-                                    f"rotating HBM-resident buffer sets (cold cache)",
-                           M=ms, N=N, K=K, block_size=16),
+               config=dict(workload="nvfp4_gemm over M=16..8192: attn_proj_n768_k6144 (M 16..1024 x 768 x 6144) + "
+                                    "moe_expert_n2048_k6144 (M 16..1024 x 2048 x 6144) + large_n6144_k6144 (M 4096, "
+                                    "8192 x 6144 x 6144), bf16 out; every call cold: rotating HBM-resident buffer "
+                                    "sets of more than 512 MB per workload",
+                           calls={name: list(ms) for name, ms in STEP}, K=6144, block_size=16,
+                           inputs="A ~ N(0,1), B ~ N(0,0.02), quantised on the GPU with per-tensor encode scales "
+                                  "2688/amax, alpha = 1/(gsA*gsB)"),
                roofline=roofline, shapes=shapes,
                launch_floor_us=dict(us=round(launch_floor, 3),
                                     note="per kernel in a graph of 64 one-element fills: the floor under every call"))
@@ -245,7 +276,6 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_headline_dominant_call.json")
 GROUPED_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_grouped_moe_packed.json")
 COPY_BYTES = 256 << 20
 
@@ -263,6 +293,11 @@ def kernel_sources_digest():
     return h.hexdigest()[:16]
 
 
+def traffic_record_path(workload, m):
+    """Counter record of one nvfp4_gemm call of a workload."""
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}_m{m}.json")
+
+
 def calibration_copy(torch):
     """A plain device copy of COPY_BYTES: it must fetch and write exactly
     COPY_BYTES, which calibrates the traffic counters."""
@@ -274,14 +309,14 @@ def calibration_copy(torch):
     del x, y
 
 
-def profile_call(torch, nv, sweep_inputs, call, m, graph=False):
+def profile_call(torch, nv, sweep_inputs, call, name, m, graph=False):
     """Workload of the profiler runs: a plain 256 MiB copy (its FETCH_SIZE and
-    WRITE_SIZE calibrate the counters), then 8 cold calls of one headline GEMM,
-    or (graph=True) the per-call timing of the headline: a graph of 64 calls
-    over the rotating sets, replayed 8 times, with its HIP-event time printed."""
+    WRITE_SIZE calibrate the counters), then 8 cold calls of one GEMM of the
+    step, or (graph=True) its per-call timing as the bench takes it: a graph
+    of back-to-back calls over the rotating sets, replayed 8 times, with its
+    HIP-event time printed."""
     calibration_copy(torch)
-    name = "attn_proj_n768_k6144"
-    w, sets, alpha, outs, wss = sweep_inputs(name)
+    w, sets, alpha, outs, wss = sweep_inputs(name, (m,))
     if m not in outs:
         raise SystemExit(f"M={m} is not a shape of {name}: {list(outs)}")
     if graph:
@@ -297,9 +332,12 @@ def profile_call(torch, nv, sweep_inputs, call, m, graph=False):
 
 
 def grouped_inputs(torch, nv, synth, quantise, dev):
-    """The grouped MoE workload: 512 tokens routed top-8 over 256 experts,
-    activations quantised on the GPU and gathered per expert, random expert
-    codes and scales, per-expert alpha."""
+    """The grouped MoE workload as stated: 512 tokens of N(0, 1) activations
+    routed top-8 over 256 experts, quantised on the GPU with their encode
+    scale and gathered per expert; each expert's [2048][6144] weights drawn
+    N(0, 0.02) (the same seeded draws as the parity test) and quantised on the
+    GPU with the expert's own encode scale; alpha[e] = 1 / (gs_a * gs_e)."""
+    from concurrent.futures import ThreadPoolExecutor
     g = synth.GROUPED
     T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
     tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
@@ -310,12 +348,24 @@ def grouped_inputs(torch, nv, synth, quantise, dev):
     qa, sfa = qa_tok[tok_t].contiguous(), sfa_tok[tok_t].contiguous()
     # the same tokens as bf16 activations, for the fused-quantisation call
     x_bf16 = torch.from_numpy(x32).to(dev).to(torch.bfloat16)
-    b = torch.from_numpy(synth.random_codes(g["seed_expert_base"], E * N, K)).to(dev)
-    bsf = torch.from_numpy(synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, 0x20, 0x38)).to(dev)
+    b = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    bsf = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
+    gs_e = torch.empty(E, dtype=torch.float32, device=dev)
+    ahead = 16
+    with ThreadPoolExecutor(8) as threads:
+        futs = {e: threads.submit(synth.expert_weights, e, N, K) for e in range(min(ahead, E))}
+        for e in range(E):
+            w = torch.from_numpy(futs.pop(e).result()).to(dev)
+            if e + ahead < E:
+                futs[e + ahead] = threads.submit(synth.expert_weights, e + ahead, N, K)
+            nv.nvfp4_global_scale(w, w.numel(), gs_e[e:e + 1])
+            nv.nvfp4_quantize(w, N, K, gs_e[e:e + 1], b[e], bsf[e])
+            del w
+    alpha = torch.empty(E, dtype=torch.float32, device=dev)
+    nv.nvfp4_alpha_from_scales(gsa, gs_e, alpha, E)
     active = int((np.diff(off) > 0).sum())
     return dict(rows=rows, N=N, K=K, E=E, T=T, qa=qa, sfa=sfa, b=b, bsf=bsf, off=torch.from_numpy(off).to(dev),
-                x_bf16=x_bf16, tok=tok_t.to(torch.int32), gsa=gsa,
-                alpha=torch.full((E,), 1.0, dtype=torch.float32, device=dev) / gsa,
+                x_bf16=x_bf16, tok=tok_t.to(torch.int32), gsa=gsa, alpha=alpha,
                 d=torch.empty((rows, N), dtype=torch.int16, device=dev), active=active,
                 rows_per_expert_max=int(np.diff(off).max()),
                 # expert weights of the active experts, activations, bf16 out, offsets, alphas
@@ -388,9 +438,10 @@ def write_traffic_record(fetch_csv, write_csv, requests_csv, target):
         call = grouped_call_name(int(off[-1]), g["n"], g["k"], g["experts"])
         match, path_out = "k_grouped", GROUPED_TRAFFIC_RECORD
     else:
-        w = synth.WORKLOADS["attn_proj_n768_k6144"]
-        call = f"nvfp4_gemm M={target} N={w['n']} K={w['k']} ({nv.nvfp4_gemm_plan(target, w['n'], w['k'])})"
-        match, path_out = "k_gemm", TRAFFIC_RECORD
+        name, m = target
+        w = synth.WORKLOADS[name]
+        call = f"nvfp4_gemm M={m} N={w['n']} K={w['k']} ({nv.nvfp4_gemm_plan(m, w['n'], w['k'])})"
+        match, path_out = "k_gemm", traffic_record_path(name, m)
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, counter)
@@ -486,21 +537,13 @@ def timed(torch, stream, fn, reps):
 
 def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call):
     res = {}
-    # MoE expert-shape sweep (cold, rotating) and large compute-bound shapes (warm)
-    for name, rotate, reps in (("moe_expert_n2048_k6144", True, 50), ("large_n6144_k6144", False, 10)):
-        w, sets, alpha, outs, wss = sweep_inputs(name, rotate)
-        rows = []
-        for m in w["ms"]:
-            us = timed(torch, stream, lambda i: call(w, sets[i % len(sets)], alpha, outs, wss, m), reps)
-            fl = 2.0 * m * w["n"] * w["k"]
-            by = algo_bytes(m, w["n"], w["k"])
-            rows.append(dict(M=m, N=w["n"], K=w["k"], plan=nv.nvfp4_gemm_plan(m, w["n"], w["k"]), us=round(us, 2),
-                             tflops=round(fl / us / 1e6, 2), gbps=round(by / us / 1e3, 1),
-                             frac_f16_mfma=round(fl / us / 1e6 / PEAK_F16_TFLOPS, 4),
-                             frac_fp4_peak=round(fl / us / 1e6 / PEAK_FP4_TFLOPS, 4)))
-        res[name] = dict(cache="cold (rotating sets)" if rotate else "warm", shapes=rows)
-        del sets, outs, wss
-        torch.cuda.empty_cache()
+    # the largest compute-bound shape, beyond the metric's range (cold, rotating sets)
+    w, sets, alpha, outs, wss = sweep_inputs("large_n6144_k6144", (16384,))
+    us = timed(torch, stream, lambda i: call(w, sets[i % len(sets)], alpha, outs, wss, 16384), 2 * len(sets))
+    res["large_n6144_k6144_m16384"] = dict(cache="cold (rotating sets)",
+                                           shapes=[shape_row(nv, 16384, w["n"], w["k"], us)])
+    del sets, outs, wss
+    torch.cuda.empty_cache()
 
     # grouped MoE: 512 tokens, top-8 of 256 experts, [rows_e, 6144] x [6144, 2048] per expert
     gi = grouped_inputs(torch, nv, synth, quantise, dev)
@@ -594,7 +637,7 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
     # MXFP4 (E8M0 scale per 32 elements, the scaled FP4 MFMA): the attention
     # sweep (cold, rotating sets) and the large shapes, random codes and scales
     mxr = {}
-    for name, rotate, reps in (("attn_proj_n768_k6144", True, 64), ("large_n6144_k6144", False, 10)):
+    for name, rotate, reps in (("attn_proj_n768_k6144", True, 64), ("large_n6144_k6144", True, 16)):
         w = synth.WORKLOADS[name]
         N, K = w["n"], w["k"]
         rows = []
@@ -629,18 +672,23 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
     # dequantised operands at the same shapes, cold as above (the MI355X
     # counterpart of the pages' FP4-vs-BF16 throughput comparison)
     ref = []
-    for (m, n, k) in [(m, 768, 6144) for m in synth.WORKLOADS["attn_proj_n768_k6144"]["ms"]] + [(8192, 6144, 6144)]:
+    step_shapes = [(m, synth.WORKLOADS[name]["n"], synth.WORKLOADS[name]["k"]) for name, ms in STEP for m in ms]
+    for (m, n, k) in step_shapes + [(16384, 6144, 6144)]:
         per = (m * k + k * n) * 2
         nsets = max(1, min(64, (ROTATE_BYTES + per - 1) // per))
-        xa = [torch.randn(m, k, device=dev, dtype=torch.bfloat16) for _ in range(nsets)]
-        xb = [torch.randn(k, n, device=dev, dtype=torch.bfloat16) for _ in range(nsets)]  # [K][N], contiguous
-        reps = max(nsets, 8) if m <= 1024 else 4
+        gen = torch.Generator(device=dev).manual_seed(m * 7 + n)
+        xa = [torch.randn(m, k, device=dev, dtype=torch.bfloat16, generator=gen) for _ in range(nsets)]
+        xb = [torch.randn(k, n, device=dev, dtype=torch.bfloat16, generator=gen)
+              for _ in range(nsets)]  # [K][N], contiguous
+        reps = max(nsets, 8) if m <= 1024 else 2 * nsets
         us = timed(torch, stream, lambda i: torch.matmul(xa[i % nsets], xb[i % nsets]), reps)
         ref.append(dict(M=m, N=n, K=k, us=round(us, 2), tflops=round(2.0 * m * n * k / us / 1e6, 1)))
         del xa, xb
         torch.cuda.empty_cache()
-    res["bf16_matmul_reference"] = dict(note="torch.matmul bf16 x bf16 -> bf16 (hipBLASLt), operands already "
-                                             "dequantised; context only", shapes=ref)
+    res["bf16_matmul_reference"] = dict(note="torch.matmul bf16 x bf16 -> bf16 (hipBLASLt) at every shape of "
+                                             "the step and M = 16384, operands already dequantised (N(0,1) "
+                                             "draws), rotating sets of more than 512 MB; context only",
+                                        shapes=ref)
 
     # quantiser (prologue): 16384 x 6144 fp32 -> NVFP4
     us, by = quantize_workload(nv, torch, dev, stream, synth)
@@ -718,37 +766,65 @@ def moe_ffn_workload(nv, torch, dev, stream, synth):
                 tflops=round(fl / us / 1e6, 2), algorithmic_bytes=by)
 
 
-def cpu_baseline(seconds):
-    """The oracle (numpy: LUT dequant to fp64, BLAS dgemm, RNE to bf16) on the
-    same sweep, repeated for about `seconds` of wall time."""
-    import synth
-    from oracle import nvfp4_ref as o
+def blas_info():
+    """(BLAS library name and version, its thread count) as numpy reports them."""
+    name = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        name = f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:
+        pass
+    threads = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"]
+                      or [0]) or None
     except Exception:
-        cores = len(os.sched_getaffinity(0))
-    name = "attn_proj_n768_k6144"
-    w = synth.WORKLOADS[name]
-    a, b = synth.single_operands(name)
-    gsa, gsb = o.global_encode_scale(a), o.global_encode_scale(b)
-    qa, sfa = o.quantize(a, gsa)
-    qb, sfb = o.quantize(b, gsb)
-    alpha = o.alpha_from_scales(gsa, gsb)
-    flops = 0.0
+        pass
+    return name, threads
+
+
+def cpu_baseline(seconds):
+    """The oracle (numpy: LUT dequant to fp64, BLAS dgemm, RNE to bf16) on the
+    step's fourteen shapes, whole passes repeated for at least `seconds` of
+    wall time.  The oracle's time does not depend on the values, so its
+    inputs are seeded random codes and scale bytes of the same shapes."""
+    import synth
+    from oracle import nvfp4_ref as o
+    blas, blas_threads = blas_info()
+    per_config = {}
+    data = {}
+    for name, ms in STEP:
+        w = synth.WORKLOADS[name]
+        mmax, n, k = max(ms), w["n"], w["k"]
+        data[name] = (synth.random_codes(8001, mmax, k), synth.random_scale_bytes(8002, mmax, k, 0x30, 0x40),
+                      synth.random_codes(8003, n, k), synth.random_scale_bytes(8004, n, k, 0x30, 0x40))
+        per_config[name] = dict(seconds=0.0, flops=0.0)
     passes = 0
     t0 = time.perf_counter()
     while True:
-        for m in w["ms"]:
-            o.gemm(qa[:m], sfa[:m], qb, sfb, alpha)
-            flops += 2.0 * m * w["n"] * w["k"]
+        for name, ms in STEP:
+            qa, sfa, qb, sfb = data[name]
+            w = synth.WORKLOADS[name]
+            for m in ms:
+                t = time.perf_counter()
+                o.gemm(qa[:m], sfa[:m], qb, sfb, np.float32(1.0))
+                per_config[name]["seconds"] += time.perf_counter() - t
+                per_config[name]["flops"] += 2.0 * m * w["n"] * w["k"]
         passes += 1
         if time.perf_counter() - t0 >= seconds:
             break
-    t = time.perf_counter() - t0
-    return dict(value=round(flops / t / 1e12, 5), unit="TFLOPS", cores=cores, kind="oracle",
-                sample=f"{passes} passes of the {name} sweep (M={list(w['ms'])}, N={w['n']}, K={w['k']}) "
-                       f"in {t:.1f} s: LUT dequant to fp64, dgemm, RNE to bf16")
+    total = time.perf_counter() - t0
+    flops = sum(v["flops"] for v in per_config.values())
+    return dict(value=round(flops / total / 1e12, 5), unit="TFLOPS", cores=len(os.sched_getaffinity(0)),
+                kind="oracle", blas=blas, blas_threads=blas_threads,
+                per_config={name: dict(tflops=round(v["flops"] / v["seconds"] / 1e12, 5),
+                                       seconds_per_pass=round(v["seconds"] / passes, 3))
+                            for name, v in per_config.items()},
+                sample=f"{passes} whole passes of the step's 14 shapes (M 16..1024 x 768, M 16..1024 x 2048, "
+                       f"M 4096 and 8192 x 6144; K = 6144) in {total:.1f} s on {len(os.sched_getaffinity(0))} "
+                       f"cores: LUT dequant to fp64, dgemm, RNE to bf16")
 
 
 if __name__ == "__main__":

@@ -103,8 +103,10 @@ nvfp4_status nvfp4_workspace_init(void* workspace, size_t workspace_bytes, void*
  *   status optional device int32: if non-NULL it is set to 0 when offsets are
  *          valid, or to 1 + (first bad expert) when offsets decrease or exceed
  *          rows; bad experts are skipped (their rows are not written).
- * Empty experts cost no weight traffic.  workspace: at least
- * nvfp4_grouped_workspace_size(rows, N, K, E) bytes, 256-byte aligned.
+ * Empty experts cost no weight traffic.  workspace, workspace_bytes:
+ * reserved.  No grouped kernel keeps scratch memory, so
+ * nvfp4_grouped_workspace_size() returns 0 and the arguments are ignored
+ * (NULL and 0 are valid).
  */
 nvfp4_status nvfp4_grouped_gemm(const uint8_t* a, const uint8_t* a_sf,
                                 const uint8_t* b, const uint8_t* b_sf,
@@ -275,6 +277,19 @@ nvfp4_status nvfp4_scales_to_128x4(const uint8_t* sf, uint8_t* tiled, int64_t ro
 nvfp4_status nvfp4_scales_from_128x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, void* stream);
 
 /*
+ * The same conversions for the 8 x 4 layout, the one use_8x4_sf_layout=True
+ * selects in the mm_fp4 signature ("The Art of Reading the Manual", section
+ * "The Message"; not described there either), read as: the scale matrix,
+ * zero-padded to a multiple of 8 rows and 4 columns, stored as 32-byte tiles
+ * of 8 rows x 4 columns in row-major tile order, the scale of row r and column
+ * c of a tile at byte (r % 8) * 4 + c % 4.  Sizes, padding, pointers and
+ * errors as for the 128 x 4 calls.
+ */
+size_t nvfp4_scales_8x4_size(int64_t rows, int64_t K);
+nvfp4_status nvfp4_scales_to_8x4(const uint8_t* sf, uint8_t* tiled, int64_t rows, int64_t K, void* stream);
+nvfp4_status nvfp4_scales_from_8x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, void* stream);
+
+/*
  * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
  * The pages never quantise (their test used random bytes); this follows the
  * block_size 16 and e4m3fn scale format of the pages above with these steps,
@@ -338,6 +353,22 @@ size_t nvfp4_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* Name of the kernel plan nvfp4_mx_gemm picks for a shape (static string). */
 const char* nvfp4_mx_gemm_plan(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Plan override, for tuning sweeps and tests only: every later call of the
+ * family in this process runs plan `kind` (the kinds are the library's
+ * kernel instantiations; a kind the family does not have leaves its own
+ * choice in place) with `splits` K splits where the plan can split K
+ * (splits <= 0: the plan's own count).  family: 0 = nvfp4_gemm, 1 =
+ * nvfp4_mx_gemm, 2 = the grouped GEMMs (kinds 0..3: per-wave dequantisation,
+ * shared f16 A tile, 32-row and 64-row register kernels; the packed and fused
+ * calls take kind 3 as 64-row passes and anything else as 32-row passes).
+ * kind < 0 restores the library's choice.  The plan and workspace queries
+ * follow the override.  Not synchronised with calls in flight on other
+ * threads: set it while no call of the family is being made.  ERR_SHAPE for
+ * an unknown family or out-of-range kind or splits (> 16).
+ */
+nvfp4_status nvfp4_force_plan(int32_t family, int32_t kind, int32_t splits);
 
 /* Message describing the calling thread's last error ("" if none). */
 const char* nvfp4_last_error(void);

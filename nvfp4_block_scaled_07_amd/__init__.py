@@ -48,6 +48,9 @@ SIGNATURES = {
     "nvfp4_scales_128x4_size": (_sz, [_i64, _i64]),
     "nvfp4_scales_to_128x4": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "nvfp4_scales_from_128x4": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "nvfp4_scales_8x4_size": (_sz, [_i64, _i64]),
+    "nvfp4_scales_to_8x4": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "nvfp4_scales_from_8x4": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_global_scale": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_alpha_from_scales": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
@@ -55,8 +58,12 @@ SIGNATURES = {
     "nvfp4_mx_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "nvfp4_mx_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nvfp4_mx_gemm_plan": (ctypes.c_char_p, [_i64, _i64, _i64]),
+    "nvfp4_force_plan": (ctypes.c_int, [_i32, _i32, _i32]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
 }
+
+# nvfp4_force_plan families
+FAMILY_GEMM, FAMILY_MX, FAMILY_GROUPED = 0, 1, 2
 
 _lib = None
 
@@ -81,8 +88,35 @@ def lib():
     return _lib
 
 
-def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _ptr(t, nbytes=0, name="tensor", fn="nvfp4"):
+    """Device pointer of t (None -> NULL, which the library checks itself).
+    A tensor must be on the GPU, contiguous and hold at least nbytes: a host
+    tensor, a strided view or a short buffer would otherwise reach a kernel
+    as a wild device address."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise Nvfp4Error(1, fn, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise Nvfp4Error(2, fn, f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise Nvfp4Error(2, fn, f"{name} holds {have} bytes, the call needs {nbytes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _n(*dims):
+    """Product of sizes, 0 if any is negative (the library rejects those)."""
+    out = 1
+    for d in dims:
+        if d < 0:
+            return 0
+        out *= d
+    return out
+
+
+def _bytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream=None):
@@ -95,6 +129,29 @@ def _stream(stream=None):
 def _check(status: int, fn: str):
     if status != 0:
         raise Nvfp4Error(status, fn, lib().nvfp4_last_error().decode())
+
+
+def nvfp4_force_plan(family: int, kind: int, splits: int = 0):
+    """Tuning and tests only: force the plan of a family (FAMILY_GEMM,
+    FAMILY_MX, FAMILY_GROUPED) for later calls; kind < 0 restores the
+    library's choice."""
+    _check(lib().nvfp4_force_plan(family, kind, splits), "nvfp4_force_plan")
+
+
+class forced_plan:
+    """Context manager around nvfp4_force_plan that restores the library's
+    own choice on exit."""
+
+    def __init__(self, family: int, kind: int, splits: int = 0):
+        self.family, self.kind, self.splits = family, kind, splits
+
+    def __enter__(self):
+        nvfp4_force_plan(self.family, self.kind, self.splits)
+        return self
+
+    def __exit__(self, *exc):
+        nvfp4_force_plan(self.family, -1, 0)
+        return False
 
 
 def nvfp4_last_error() -> str:
@@ -113,7 +170,8 @@ def nvfp4_workspace_init(workspace, stream=None):
     """Zero-fill a workspace tensor (needed once before its first use)."""
     if workspace is None:
         return None
-    st = lib().nvfp4_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    st = lib().nvfp4_workspace_init(_ptr(workspace, 0, "workspace", "nvfp4_workspace_init"), _bytes(workspace),
+                                    _stream(stream))
     _check(st, "nvfp4_workspace_init")
     return workspace
 
@@ -151,9 +209,11 @@ def nvfp4_mx_gemm(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, workspace=
     a: uint8 [M][K/2], a_sf: uint8 [M][K/32], b: uint8 [N][K/2],
     b_sf: uint8 [N][K/32], alpha: fp32 device scalar tensor or None,
     d: caller-allocated [M][N] bf16 (or int16/uint16) tensor, returned."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_mx_gemm(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(d), M, N, K,
-                             _ptr(workspace), ws_bytes, _stream(stream))
+    f = "nvfp4_mx_gemm"
+    st = lib().nvfp4_mx_gemm(_ptr(a, _n(M, K) // 2, "a", f), _ptr(a_sf, _n(M, K) // 32, "a_sf", f),
+                             _ptr(b, _n(N, K) // 2, "b", f), _ptr(b_sf, _n(N, K) // 32, "b_sf", f),
+                             _ptr(alpha, 4, "alpha", f), _ptr(d, 2 * _n(M, N), "d", f), M, N, K,
+                             _ptr(workspace, 0, "workspace", f), _bytes(workspace), _stream(stream))
     _check(st, "nvfp4_mx_gemm")
     return d
 
@@ -167,18 +227,24 @@ def nvfp4_gemm(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, workspace=Non
     a: uint8 [M][K/2], a_sf: uint8 [M][K/16], b: uint8 [N][K/2],
     b_sf: uint8 [N][K/16], alpha: fp32 device scalar tensor or None,
     d: caller-allocated [M][N] bf16 (or int16/uint16) tensor, returned."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_gemm(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(d), M, N, K,
-                          _ptr(workspace), ws_bytes, _stream(stream))
+    f = "nvfp4_gemm"
+    st = lib().nvfp4_gemm(_ptr(a, _n(M, K) // 2, "a", f), _ptr(a_sf, _n(M, K) // 16, "a_sf", f),
+                          _ptr(b, _n(N, K) // 2, "b", f), _ptr(b_sf, _n(N, K) // 16, "b_sf", f),
+                          _ptr(alpha, 4, "alpha", f), _ptr(d, 2 * _n(M, N), "d", f), M, N, K,
+                          _ptr(workspace, 0, "workspace", f), _bytes(workspace), _stream(stream))
     _check(st, "nvfp4_gemm")
     return d
 
 
 def nvfp4_grouped_gemm(a, a_sf, b, b_sf, offsets, alpha, d, rows: int, N: int, K: int, E: int,
                        workspace=None, status=None, stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_grouped_gemm(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(offsets), _ptr(alpha), _ptr(d),
-                                  rows, N, K, E, _ptr(workspace), ws_bytes, _ptr(status), _stream(stream))
+    f = "nvfp4_grouped_gemm"
+    st = lib().nvfp4_grouped_gemm(_ptr(a, _n(rows, K) // 2, "a", f), _ptr(a_sf, _n(rows, K) // 16, "a_sf", f),
+                                  _ptr(b, _n(E, N, K) // 2, "b", f), _ptr(b_sf, _n(E, N, K) // 16, "b_sf", f),
+                                  _ptr(offsets, 4 * _n(E + 1), "offsets", f), _ptr(alpha, 4 * _n(E), "alpha", f),
+                                  _ptr(d, 2 * _n(rows, N), "d", f), rows, N, K, E,
+                                  _ptr(workspace, 0, "workspace", f), _bytes(workspace),
+                                  _ptr(status, 4, "status", f), _stream(stream))
     _check(st, "nvfp4_grouped_gemm")
     return d
 
@@ -191,7 +257,11 @@ def nvfp4_grouped_packed_size(N: int, K: int, E: int):
 
 
 def nvfp4_grouped_pack_b(b, b_sf, N: int, K: int, E: int, packed, packed_sf, stream=None):
-    st = lib().nvfp4_grouped_pack_b(_ptr(b), _ptr(b_sf), N, K, E, _ptr(packed), _ptr(packed_sf), _stream(stream))
+    f = "nvfp4_grouped_pack_b"
+    cb, sb = nvfp4_grouped_packed_size(N, K, E)
+    st = lib().nvfp4_grouped_pack_b(_ptr(b, _n(E, N, K) // 2, "b", f), _ptr(b_sf, _n(E, N, K) // 16, "b_sf", f),
+                                    N, K, E, _ptr(packed, cb, "packed", f), _ptr(packed_sf, sb, "packed_sf", f),
+                                    _stream(stream))
     _check(st, "nvfp4_grouped_pack_b")
     return packed, packed_sf
 
@@ -209,8 +279,13 @@ def grouped_pack(b, b_sf, N: int, K: int, E: int, device="cuda"):
 
 def nvfp4_grouped_gemm_packed(a, a_sf, packed, packed_sf, offsets, alpha, d, rows: int, N: int, K: int, E: int,
                               status=None, stream=None):
-    st = lib().nvfp4_grouped_gemm_packed(_ptr(a), _ptr(a_sf), _ptr(packed), _ptr(packed_sf), _ptr(offsets),
-                                         _ptr(alpha), _ptr(d), rows, N, K, E, _ptr(status), _stream(stream))
+    f = "nvfp4_grouped_gemm_packed"
+    cb, sb = nvfp4_grouped_packed_size(N, K, E)
+    st = lib().nvfp4_grouped_gemm_packed(_ptr(a, _n(rows, K) // 2, "a", f), _ptr(a_sf, _n(rows, K) // 16, "a_sf", f),
+                                         _ptr(packed, cb, "packed", f), _ptr(packed_sf, sb, "packed_sf", f),
+                                         _ptr(offsets, 4 * _n(E + 1), "offsets", f),
+                                         _ptr(alpha, 4 * _n(E), "alpha", f), _ptr(d, 2 * _n(rows, N), "d", f),
+                                         rows, N, K, E, _ptr(status, 4, "status", f), _stream(stream))
     _check(st, "nvfp4_grouped_gemm_packed")
     return d
 
@@ -219,9 +294,13 @@ def nvfp4_grouped_gemm_fused(x, row_token, a_global_scale, b, b_sf, offsets, alp
                              K: int, E: int, status=None, stream=None):
     """Grouped GEMM quantising bf16 activations x [T][K] on load: A row i is
     x[row_token[i]] (x[i] when row_token is None); b, b_sf as nvfp4_grouped_gemm."""
-    st = lib().nvfp4_grouped_gemm_fused(_ptr(x), _ptr(row_token), _ptr(a_global_scale), _ptr(b), _ptr(b_sf),
-                                        _ptr(offsets), _ptr(alpha), _ptr(d), rows, T, N, K, E, _ptr(status),
-                                        _stream(stream))
+    f = "nvfp4_grouped_gemm_fused"
+    st = lib().nvfp4_grouped_gemm_fused(_ptr(x, 2 * _n(T, K), "x", f), _ptr(row_token, 4 * _n(rows), "row_token", f),
+                                        _ptr(a_global_scale, 4, "a_global_scale", f),
+                                        _ptr(b, _n(E, N, K) // 2, "b", f), _ptr(b_sf, _n(E, N, K) // 16, "b_sf", f),
+                                        _ptr(offsets, 4 * _n(E + 1), "offsets", f),
+                                        _ptr(alpha, 4 * _n(E), "alpha", f), _ptr(d, 2 * _n(rows, N), "d", f),
+                                        rows, T, N, K, E, _ptr(status, 4, "status", f), _stream(stream))
     _check(st, "nvfp4_grouped_gemm_fused")
     return d
 
@@ -229,31 +308,44 @@ def nvfp4_grouped_gemm_fused(x, row_token, a_global_scale, b, b_sf, offsets, alp
 def nvfp4_grouped_gemm_packed_fused(x, row_token, a_global_scale, packed, packed_sf, offsets, alpha, d, rows: int,
                                     T: int, N: int, K: int, E: int, status=None, stream=None):
     """nvfp4_grouped_gemm_fused on weights packed by nvfp4_grouped_pack_b."""
-    st = lib().nvfp4_grouped_gemm_packed_fused(_ptr(x), _ptr(row_token), _ptr(a_global_scale), _ptr(packed),
-                                               _ptr(packed_sf), _ptr(offsets), _ptr(alpha), _ptr(d), rows, T, N, K,
-                                               E, _ptr(status), _stream(stream))
+    f = "nvfp4_grouped_gemm_packed_fused"
+    cb, sb = nvfp4_grouped_packed_size(N, K, E)
+    st = lib().nvfp4_grouped_gemm_packed_fused(_ptr(x, 2 * _n(T, K), "x", f),
+                                               _ptr(row_token, 4 * _n(rows), "row_token", f),
+                                               _ptr(a_global_scale, 4, "a_global_scale", f),
+                                               _ptr(packed, cb, "packed", f), _ptr(packed_sf, sb, "packed_sf", f),
+                                               _ptr(offsets, 4 * _n(E + 1), "offsets", f),
+                                               _ptr(alpha, 4 * _n(E), "alpha", f), _ptr(d, 2 * _n(rows, N), "d", f),
+                                               rows, T, N, K, E, _ptr(status, 4, "status", f), _stream(stream))
     _check(st, "nvfp4_grouped_gemm_packed_fused")
     return d
 
 
 def nvfp4_quantize_rows_bf16(x, row_token, gs, q, sf, rows: int, T: int, K: int, stream=None):
     """NVFP4 of bf16 rows x[row_token[i]] (x[i] when row_token is None)."""
-    st = lib().nvfp4_quantize_rows_bf16(_ptr(x), _ptr(row_token), _ptr(gs), _ptr(q), _ptr(sf), rows, T, K,
-                                        _stream(stream))
+    f = "nvfp4_quantize_rows_bf16"
+    st = lib().nvfp4_quantize_rows_bf16(_ptr(x, 2 * _n(T, K), "x", f), _ptr(row_token, 4 * _n(rows), "row_token", f),
+                                        _ptr(gs, 4, "gs", f), _ptr(q, _n(rows, K) // 2, "q", f),
+                                        _ptr(sf, _n(rows, K) // 16, "sf", f), rows, T, K, _stream(stream))
     _check(st, "nvfp4_quantize_rows_bf16")
     return q, sf
 
 
 def nvfp4_swiglu_quantize(gu, rows: int, I: int, gs, q, sf, stream=None):
     """h = silu(gate) * up of bf16 gu [rows][2I], quantised to NVFP4 (q, sf)."""
-    st = lib().nvfp4_swiglu_quantize(_ptr(gu), rows, I, _ptr(gs), _ptr(q), _ptr(sf), _stream(stream))
+    f = "nvfp4_swiglu_quantize"
+    st = lib().nvfp4_swiglu_quantize(_ptr(gu, 4 * _n(rows, I), "gu", f), rows, I, _ptr(gs, 4, "gs", f),
+                                     _ptr(q, _n(rows, I) // 2, "q", f), _ptr(sf, _n(rows, I) // 16, "sf", f),
+                                     _stream(stream))
     _check(st, "nvfp4_swiglu_quantize")
     return q, sf
 
 
 def nvfp4_moe_combine(down, rows_of, weight, out, T: int, H: int, top_k: int, rows: int, stream=None):
-    st = lib().nvfp4_moe_combine(_ptr(down), _ptr(rows_of), _ptr(weight), _ptr(out), T, H, top_k, rows,
-                                 _stream(stream))
+    f = "nvfp4_moe_combine"
+    st = lib().nvfp4_moe_combine(_ptr(down, 2 * _n(rows, H), "down", f), _ptr(rows_of, 4 * _n(T, top_k), "rows_of", f),
+                                 _ptr(weight, 4 * _n(T, top_k), "weight", f), _ptr(out, 2 * _n(T, H), "out", f),
+                                 T, H, top_k, rows, _stream(stream))
     _check(st, "nvfp4_moe_combine")
     return out
 
@@ -267,11 +359,19 @@ def nvfp4_moe_ffn(x, gs_x, row_token, offsets, w_gu, w_gu_sf, alpha_gu, gs_h, w_
                   stream=None):
     """One MoE layer's experts: fused gate/up grouped GEMM, SwiGLU + NVFP4,
     down grouped GEMM, weighted combine (weights packed by nvfp4_grouped_pack_b)."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().nvfp4_moe_ffn(_ptr(x), _ptr(gs_x), _ptr(row_token), _ptr(offsets), _ptr(w_gu), _ptr(w_gu_sf),
-                             _ptr(alpha_gu), _ptr(gs_h), _ptr(w_d), _ptr(w_d_sf), _ptr(alpha_d), _ptr(token_rows),
-                             _ptr(token_weight), _ptr(out), T, H, I, E, top_k, _ptr(workspace), ws_bytes,
-                             _ptr(status), _stream(stream))
+    f = "nvfp4_moe_ffn"
+    gcb, gsb = nvfp4_grouped_packed_size(2 * I, H, E)
+    dcb, dsb = nvfp4_grouped_packed_size(H, I, E)
+    rows = _n(T, top_k)
+    st = lib().nvfp4_moe_ffn(_ptr(x, 2 * _n(T, H), "x", f), _ptr(gs_x, 4, "gs_x", f),
+                             _ptr(row_token, 4 * rows, "row_token", f), _ptr(offsets, 4 * _n(E + 1), "offsets", f),
+                             _ptr(w_gu, gcb, "w_gu", f), _ptr(w_gu_sf, gsb, "w_gu_sf", f),
+                             _ptr(alpha_gu, 4 * _n(E), "alpha_gu", f), _ptr(gs_h, 4, "gs_h", f),
+                             _ptr(w_d, dcb, "w_d", f), _ptr(w_d_sf, dsb, "w_d_sf", f),
+                             _ptr(alpha_d, 4 * _n(E), "alpha_d", f), _ptr(token_rows, 4 * rows, "token_rows", f),
+                             _ptr(token_weight, 4 * rows, "token_weight", f), _ptr(out, 2 * _n(T, H), "out", f),
+                             T, H, I, E, top_k, _ptr(workspace, 0, "workspace", f), _bytes(workspace),
+                             _ptr(status, 4, "status", f), _stream(stream))
     _check(st, "nvfp4_moe_ffn")
     return out
 
@@ -282,30 +382,60 @@ def nvfp4_scales_128x4_size(rows: int, K: int) -> int:
 
 def nvfp4_scales_to_128x4(sf, tiled, rows: int, K: int, stream=None):
     """Linear [rows][K/16] scales -> the 128 x 4 tiled layout."""
-    _check(lib().nvfp4_scales_to_128x4(_ptr(sf), _ptr(tiled), rows, K, _stream(stream)), "nvfp4_scales_to_128x4")
+    f = "nvfp4_scales_to_128x4"
+    _check(lib().nvfp4_scales_to_128x4(_ptr(sf, _n(rows, K) // 16, "sf", f),
+                                       _ptr(tiled, nvfp4_scales_128x4_size(rows, K), "tiled", f), rows, K,
+                                       _stream(stream)), f)
     return tiled
 
 
 def nvfp4_scales_from_128x4(tiled, sf, rows: int, K: int, stream=None):
     """The 128 x 4 tiled layout -> linear [rows][K/16] scales."""
-    _check(lib().nvfp4_scales_from_128x4(_ptr(tiled), _ptr(sf), rows, K, _stream(stream)),
-           "nvfp4_scales_from_128x4")
+    f = "nvfp4_scales_from_128x4"
+    _check(lib().nvfp4_scales_from_128x4(_ptr(tiled, nvfp4_scales_128x4_size(rows, K), "tiled", f),
+                                         _ptr(sf, _n(rows, K) // 16, "sf", f), rows, K, _stream(stream)), f)
+    return sf
+
+
+def nvfp4_scales_8x4_size(rows: int, K: int) -> int:
+    return int(lib().nvfp4_scales_8x4_size(rows, K))
+
+
+def nvfp4_scales_to_8x4(sf, tiled, rows: int, K: int, stream=None):
+    """Linear [rows][K/16] scales -> the 8 x 4 tiled layout."""
+    f = "nvfp4_scales_to_8x4"
+    _check(lib().nvfp4_scales_to_8x4(_ptr(sf, _n(rows, K) // 16, "sf", f),
+                                     _ptr(tiled, nvfp4_scales_8x4_size(rows, K), "tiled", f), rows, K,
+                                     _stream(stream)), f)
+    return tiled
+
+
+def nvfp4_scales_from_8x4(tiled, sf, rows: int, K: int, stream=None):
+    """The 8 x 4 tiled layout -> linear [rows][K/16] scales."""
+    f = "nvfp4_scales_from_8x4"
+    _check(lib().nvfp4_scales_from_8x4(_ptr(tiled, nvfp4_scales_8x4_size(rows, K), "tiled", f),
+                                       _ptr(sf, _n(rows, K) // 16, "sf", f), rows, K, _stream(stream)), f)
     return sf
 
 
 def nvfp4_quantize(x, R: int, K: int, global_scale, q, sf, stream=None):
-    st = lib().nvfp4_quantize(_ptr(x), R, K, _ptr(global_scale), _ptr(q), _ptr(sf), _stream(stream))
+    f = "nvfp4_quantize"
+    st = lib().nvfp4_quantize(_ptr(x, 4 * _n(R, K), "x", f), R, K, _ptr(global_scale, 4, "global_scale", f),
+                              _ptr(q, _n(R, K) // 2, "q", f), _ptr(sf, _n(R, K) // 16, "sf", f), _stream(stream))
     _check(st, "nvfp4_quantize")
     return q, sf
 
 
 def nvfp4_global_scale(x, n: int, gs, stream=None):
-    st = lib().nvfp4_global_scale(_ptr(x), n, _ptr(gs), _stream(stream))
+    f = "nvfp4_global_scale"
+    st = lib().nvfp4_global_scale(_ptr(x, 4 * _n(n), "x", f), n, _ptr(gs, 4, "gs", f), _stream(stream))
     _check(st, "nvfp4_global_scale")
     return gs
 
 
 def nvfp4_alpha_from_scales(gs_a, gs_b, alpha, count: int, stream=None):
-    st = lib().nvfp4_alpha_from_scales(_ptr(gs_a), _ptr(gs_b), _ptr(alpha), count, _stream(stream))
+    f = "nvfp4_alpha_from_scales"
+    st = lib().nvfp4_alpha_from_scales(_ptr(gs_a, 4, "gs_a", f), _ptr(gs_b, 4 * _n(count), "gs_b", f),
+                                       _ptr(alpha, 4 * _n(count), "alpha", f), count, _stream(stream))
     _check(st, "nvfp4_alpha_from_scales")
     return alpha

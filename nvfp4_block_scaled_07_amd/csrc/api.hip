@@ -46,25 +46,11 @@ nvfp4_status check_k(int64_t K) {
   return NVFP4_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* nvfp4_last_error(void) { return g_err; }
-
-size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return 0;
-  return nvfp4::choose_plan(M, N, K).workspace;
-}
-
-const char* nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return "none";
-  return nvfp4::choose_plan(M, N, K).name;
-}
-
-nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
-                        const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+// Checks, plan choice and launch of nvfp4_gemm.
+nvfp4_status gemm_call(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                       const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_gemm launch";
   if (M < 0 || N < 0) return fail(NVFP4_ERR_SHAPE, "M = %lld, N = %lld must be >= 0", (long long)M, (long long)N);
   nvfp4_status s = check_k(K);
   if (s != NVFP4_OK) return s;
@@ -84,7 +70,38 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
     if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
   nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 0, 1, 1};
-  return hip_status(nvfp4::launch_gemm(plan, p, (hipStream_t)stream), "nvfp4_gemm launch");
+  return hip_status(nvfp4::launch_gemm(plan, p, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_err; }
+
+nvfp4_status nvfp4_force_plan(int32_t family, int32_t kind, int32_t splits) {
+  if (family < 0 || family >= nvfp4::kForceFamilies)
+    return fail(NVFP4_ERR_SHAPE, "family = %d: 0 (nvfp4_gemm), 1 (nvfp4_mx_gemm) or 2 (grouped)", family);
+  if (kind > 0xFFFE || splits > 16)
+    return fail(NVFP4_ERR_SHAPE, "kind = %d, splits = %d out of range", kind, splits);
+  nvfp4::set_forced_plan(family, kind, splits);
+  return ok();
+}
+
+size_t nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return 0;
+  return nvfp4::choose_plan(M, N, K).workspace;
+}
+
+const char* nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22)) return "none";
+  return nvfp4::choose_plan(M, N, K).name;
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                        const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return gemm_call(a, a_sf, b, b_sf, alpha, d, M, N, K, workspace, workspace_bytes, stream);
 }
 
 size_t nvfp4_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -388,25 +405,16 @@ nvfp4_status nvfp4_moe_ffn(const uint16_t* x, const float* gs_x, const int32_t* 
   if (rows > 0 && E > 0) {
     // gate/up: the tokens gathered and quantised once into the workspace,
     // then the packed grouped GEMM (measured faster here than quantising on
-    // load, which every one of an expert's 2I / 256 column tiles repeats);
-    // NVFP4_FFN_FUSED=1 selects the fused kernel (tuning only)
-    const char* env = getenv("NVFP4_FFN_FUSED");
-    const bool fused = env && atoi(env) == 1;
-    if (fused) {
-      nvfp4::GroupedLaunch p1{nullptr, nullptr, w_gu, w_gu_sf, offsets, alpha_gu, gu, rows, 2 * I, H, E,
-                              x, row_token, gs_x, T};
-      e = nvfp4::launch_grouped_fused(p1, true, status, st, true);
-    } else {
-      uint8_t* aq = ws + w.aq;
-      uint8_t* asf = ws + w.asf;
-      nvfp4::GroupedLaunch pc{nullptr, nullptr, nullptr, nullptr, offsets, nullptr, nullptr, rows, 2 * I, H, E,
-                              x, row_token, gs_x, T};
-      e = nvfp4::launch_grouped_fused(pc, true, status, st, false);  // offsets and tokens into status
-      if (e == hipSuccess) e = nvfp4::launch_quantize_rows_bf16(x, row_token, rows, T, H, gs_x, aq, asf, st);
-      if (e == hipSuccess) {
-        nvfp4::GroupedLaunch p1{aq, asf, w_gu, w_gu_sf, offsets, alpha_gu, gu, rows, 2 * I, H, E};
-        e = nvfp4::launch_grouped_packed(p1, nullptr, st, true);
-      }
+    // load, which every one of an expert's 2I / 256 column tiles repeats)
+    uint8_t* aq = ws + w.aq;
+    uint8_t* asf = ws + w.asf;
+    nvfp4::GroupedLaunch pc{nullptr, nullptr, nullptr, nullptr, offsets, nullptr, nullptr, rows, 2 * I, H, E,
+                            x, row_token, gs_x, T};
+    e = nvfp4::launch_grouped_fused(pc, true, status, st, false);  // offsets and tokens into status
+    if (e == hipSuccess) e = nvfp4::launch_quantize_rows_bf16(x, row_token, rows, T, H, gs_x, aq, asf, st);
+    if (e == hipSuccess) {
+      nvfp4::GroupedLaunch p1{aq, asf, w_gu, w_gu_sf, offsets, alpha_gu, gu, rows, 2 * I, H, E};
+      e = nvfp4::launch_grouped_packed(p1, nullptr, st, true);
     }
     if (e == hipSuccess) e = nvfp4::launch_swiglu_quantize(gu, rows, I, gs_h, hq, hsf, st);
     if (e == hipSuccess) {
@@ -437,6 +445,26 @@ nvfp4_status nvfp4_scales_from_128x4(const uint8_t* tiled, uint8_t* sf, int64_t 
   if (!sf || !tiled) return fail(NVFP4_ERR_NULL, "sf and tiled must be non-NULL");
   return hip_status(nvfp4::launch_scales_from_128x4(tiled, sf, rows, K, (hipStream_t)stream),
                     "nvfp4_scales_from_128x4 launch");
+}
+
+size_t nvfp4_scales_8x4_size(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0 || K % 16) return 0;
+  return nvfp4::tiled8x4_bytes(rows, K);
+}
+
+nvfp4_status nvfp4_scales_to_8x4(const uint8_t* sf, uint8_t* tiled, int64_t rows, int64_t K, void* stream) {
+  if (rows < 0 || K < 0 || K % 16) return fail(NVFP4_ERR_SHAPE, "rows >= 0 and K >= 0 with K %% 16 == 0 required");
+  if (rows == 0 || K == 0) return ok();
+  if (!sf || !tiled) return fail(NVFP4_ERR_NULL, "sf and tiled must be non-NULL");
+  return hip_status(nvfp4::launch_scales_to_8x4(sf, tiled, rows, K, (hipStream_t)stream), "nvfp4_scales_to_8x4 launch");
+}
+
+nvfp4_status nvfp4_scales_from_8x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, void* stream) {
+  if (rows < 0 || K < 0 || K % 16) return fail(NVFP4_ERR_SHAPE, "rows >= 0 and K >= 0 with K %% 16 == 0 required");
+  if (rows == 0 || K == 0) return ok();
+  if (!sf || !tiled) return fail(NVFP4_ERR_NULL, "sf and tiled must be non-NULL");
+  return hip_status(nvfp4::launch_scales_from_8x4(tiled, sf, rows, K, (hipStream_t)stream),
+                    "nvfp4_scales_from_8x4 launch");
 }
 
 nvfp4_status nvfp4_quantize(const float* x, int64_t R, int64_t K, const float* global_scale, uint8_t* q,

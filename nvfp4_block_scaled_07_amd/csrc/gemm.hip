@@ -45,6 +45,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -1617,6 +1618,23 @@ static const int64_t kTargetBlocks = 384;   // 1.5 work-groups per CU
 static const int64_t kK4Blocks = 192;
 static const int64_t kMinStagesPerSplit = 6;
 
+// Forced plans (nvfp4_force_plan; tuning sweeps and tests): per operation
+// family, 0 = none, else (kind + 1) | splits << 16, one word so that kind and
+// splits are always read together.
+static std::atomic<int> g_forced[kForceFamilies];
+
+void set_forced_plan(int family, int kind, int splits) {
+  g_forced[family].store(kind < 0 ? 0 : (kind + 1) | ((splits < 0 ? 0 : splits) << 16));
+}
+
+static bool forced_plan(int family, int* kind, int* splits) {
+  const int v = g_forced[family].load();
+  if (v == 0) return false;
+  *kind = (v & 0xFFFF) - 1;
+  *splits = v >> 16;
+  return true;
+}
+
 static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) {
   const int64_t tiles = pl.tiles_m * pl.tiles_n;
   const int64_t nk = K / k.bk;
@@ -1692,13 +1710,11 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
     else if (t128 >= 3 * kCUs) kind = 15;
     else kind = 9;
   }
-  // NVFP4_PLAN=<kind>[,<splits>] forces a plan (tuning sweeps only)
-  if (const char* env = getenv("NVFP4_PLAN")) {
-    int fk = -1, fs = 0;
-    if (sscanf(env, "%d,%d", &fk, &fs) >= 1 && fk >= 0 && fk < kNumKinds) {
-      kind = fk;
-      forced_splits = fs;
-    }
+  // a plan forced by nvfp4_force_plan (tuning sweeps and tests only)
+  int fk = -1, fs = 0;
+  if (forced_plan(kForceGemm, &fk, &fs) && fk < kNumKinds) {
+    kind = fk;
+    forced_splits = fs;
   }
   const PlanKind& k = kKinds[kind];
   pl.kind = kind;
@@ -1754,7 +1770,7 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
 // with at most one work-group per CU); else 256x256 tiles of 8 waves while
 // they fill the CUs, then 128x128 (two work-groups per CU) while those fill
 // them, else 64x64 with split-K up to about 1.5 work-groups per CU.
-// NVFP4_MX_PLAN=<kind>[,<splits>] forces one (tuning sweeps only).
+// nvfp4_force_plan can force one (tuning sweeps and tests only).
 GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   int kind = -1, forced_splits = 0;
@@ -1769,12 +1785,10 @@ GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K) {
     }
   }
   if (kind < 0) kind = t256 >= kCUs ? 3 : (t128 >= kCUs ? 1 : 2);
-  if (const char* env = getenv("NVFP4_MX_PLAN")) {
-    int fk = -1, fs = 0;
-    if (sscanf(env, "%d,%d", &fk, &fs) >= 1 && fk >= 0 && fk < kNumMxKinds) {
-      kind = fk;
-      forced_splits = fs;
-    }
+  int fk = -1, fs = 0;
+  if (forced_plan(kForceMx, &fk, &fs) && fk < kNumMxKinds) {
+    kind = fk;
+    forced_splits = fs;
   }
   const PlanKind& k = kMxKinds[kind];
   pl.kind = kind;
@@ -1808,6 +1822,11 @@ hipError_t launch_mx_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) 
 
 // The host sees only the total row count: experts averaging more than 40
 // rows get 64-row passes.
+static void grouped_forced(int* gk) {
+  int fk = -1, fs = 0;
+  if (forced_plan(kForceGrouped, &fk, &fs) && fk <= 3) *gk = fk;
+}
+
 static bool tall_experts(const GroupedLaunch& p) { return p.rows > 40 * (int64_t)p.E; }
 
 hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, bool compute) {
@@ -1823,10 +1842,10 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
   // register kernel takes 32-row passes over each expert (4 waves per SIMD);
   // when the experts average more than 40 rows, 64-row passes (2 waves per
   // SIMD, but every weight byte read once for up to 64 rows) are faster.
-  // NVFP4_GPLAN=<0|1|2|3> forces the per-wave-dequant, shared-f16-A,
-  // 32-row or 64-row register kernel (tuning and tests only).
+  // nvfp4_force_plan can force the per-wave-dequant, shared-f16-A, 32-row
+  // or 64-row register kernel (kinds 0..3; tuning and tests only).
   int gk = (p.K / 256) % 2 == 0 ? (tall_experts(p) ? 3 : 2) : 1;
-  if (const char* env = getenv("NVFP4_GPLAN")) gk = atoi(env);
+  grouped_forced(&gk);
   if (gk >= 2 && (p.K / 256) % 2) gk = 1;
   if (gk == 0) {
     const unsigned tiles_n = (unsigned)((p.N + CfgGrouped::BN - 1) / CfgGrouped::BN);
@@ -1942,7 +1961,7 @@ hipError_t launch_grouped_packed(GroupedLaunch p, int32_t* status, hipStream_t s
   const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
   // row passes of 32 or 64 rows, chosen as for the unpacked weights
   int gk = tall_experts(p) ? 3 : 2;
-  if (const char* env = getenv("NVFP4_GPLAN")) gk = atoi(env);
+  grouped_forced(&gk);
   if (gk == 3)
     hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, true>), dim3(tiles_n * (unsigned)p.E),
                        dim3(CfgGroupedReg64::kThreads), 0, stream, p);
@@ -1981,7 +2000,8 @@ hipError_t launch_grouped_fused(GroupedLaunch p, bool packed, int32_t* status, h
   // 32 or 64 rows chosen as for the unfused calls
   const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
   int gk = tall_experts(p) ? 3 : 2;
-  if (const char* env = getenv("NVFP4_GPLAN")) gk = atoi(env) == 3 ? 3 : 2;
+  grouped_forced(&gk);
+  gk = gk == 3 ? 3 : 2;
   const dim3 grid(tiles_n * (unsigned)p.E);
   if (packed) {
     if (gk == 3)
@@ -2002,6 +2022,7 @@ hipError_t launch_grouped_fused(GroupedLaunch p, bool packed, int32_t* status, h
 }
 
 size_t grouped_workspace(int64_t, int64_t, int64_t, int32_t) { return 0; }
+
 
 __global__ void k_fill_zero(uint32_t* p, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;

@@ -48,6 +48,10 @@ struct GemmPlan {
   size_t workspace;
 };
 
+// Plan families that nvfp4_force_plan can force (tuning sweeps and tests).
+constexpr int kForceGemm = 0, kForceMx = 1, kForceGrouped = 2, kForceFamilies = 3;
+void set_forced_plan(int family, int kind, int splits);
+
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
 // MXFP4 (E8M0 scales per 32 elements): GemmLaunch with a_sf / b_sf of K/32 bytes per row.
@@ -63,6 +67,7 @@ size_t packed_b_bytes(int64_t N, int64_t K, int32_t E, size_t* sf_bytes);
 hipError_t launch_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64_t K, int32_t E, uint8_t* pb,
                          uint8_t* psf, hipStream_t stream);
 size_t grouped_workspace(int64_t rows, int64_t N, int64_t K, int32_t E);
+
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);
 
 // MoE expert FFN pieces (moe.hip): SwiGLU of a [rows][2I] bf16 gate/up
@@ -78,6 +83,10 @@ hipError_t launch_moe_combine(const uint16_t* down, const int32_t* rows_of, cons
 size_t tiled128x4_bytes(int64_t rows, int64_t K);
 hipError_t launch_scales_to_128x4(const uint8_t* sf, uint8_t* tiled, int64_t rows, int64_t K, hipStream_t stream);
 hipError_t launch_scales_from_128x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, hipStream_t stream);
+// ... and the 8 x 4 tiles
+size_t tiled8x4_bytes(int64_t rows, int64_t K);
+hipError_t launch_scales_to_8x4(const uint8_t* sf, uint8_t* tiled, int64_t rows, int64_t K, hipStream_t stream);
+hipError_t launch_scales_from_8x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, hipStream_t stream);
 
 hipError_t launch_quantize(const float* x, int64_t R, int64_t K, const float* gs, uint8_t* q, uint8_t* sf,
                            hipStream_t stream);

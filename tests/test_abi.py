@@ -247,3 +247,75 @@ def test_scale_layout_error_paths_and_sizes():
     assert L.nvfp4_scales_from_128x4(FAKE, None, 4, 64, None) == 1
     assert L.nvfp4_scales_from_128x4(FAKE, FAKE, -1, 64, None) == 2
     assert L.nvfp4_scales_to_128x4(None, None, 0, 64, None) == 0
+
+
+def test_force_plan_sets_and_restores_the_choice():
+    L = nv.lib()
+    auto = nv.nvfp4_gemm_plan(1024, 768, 6144)
+    with nv.forced_plan(nv.FAMILY_GEMM, 0):
+        assert nv.nvfp4_gemm_plan(1024, 768, 6144) == "tile256x256_mfma32"
+        assert nv.nvfp4_gemm_workspace_size(1024, 768, 6144) == 0    # that kind never splits K
+    assert nv.nvfp4_gemm_plan(1024, 768, 6144) == auto
+    with nv.forced_plan(nv.FAMILY_GEMM, 9, 5):                          # K-group tile, 5 splits
+        assert nv.nvfp4_gemm_plan(1024, 768, 6144) == "tile64x64k4_mfma32"
+        assert nv.nvfp4_gemm_workspace_size(1024, 768, 6144) == 4096 + 192 * 5 * 64 * 64 * 4
+    with nv.forced_plan(nv.FAMILY_GEMM, 999):                           # no such kind: own choice kept
+        assert nv.nvfp4_gemm_plan(1024, 768, 6144) == auto
+    auto_mx = nv.nvfp4_mx_gemm_plan(8192, 6144, 6144)
+    with nv.forced_plan(nv.FAMILY_MX, 2):
+        assert nv.nvfp4_mx_gemm_plan(8192, 6144, 6144) == "mx64x64_fp4mfma"
+    assert nv.nvfp4_mx_gemm_plan(8192, 6144, 6144) == auto_mx
+    assert L.nvfp4_force_plan(3, 0, 0) == 2 and "family" in nv.nvfp4_last_error()
+    assert L.nvfp4_force_plan(-1, 0, 0) == 2
+    assert L.nvfp4_force_plan(0, 1, 17) == 2
+    assert nv.nvfp4_gemm_plan(1024, 768, 6144) == auto
+
+
+class _FakeTensor:
+    """Stands in for a torch tensor in the binding's pointer checks."""
+
+    def __init__(self, cuda=True, contiguous=True, nbytes=1 << 20):
+        self.is_cuda, self._c, self._n = cuda, contiguous, nbytes
+
+    def is_contiguous(self):
+        return self._c
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return FAKE
+
+
+def test_binding_rejects_host_strided_and_short_tensors():
+    ok = _FakeTensor()
+    M, N, K = 16, 32, 256
+    d = _FakeTensor(nbytes=2 * M * N)
+    for bad, status, what in ((_FakeTensor(cuda=False), 1, "GPU tensor"),
+                              (_FakeTensor(contiguous=False), 2, "contiguous"),
+                              (_FakeTensor(nbytes=M * K // 2 - 1), 2, "bytes")):
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_gemm(bad, ok, ok, ok, None, d, M, N, K)
+        assert e.value.status == status and what in str(e.value), str(e.value)
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.nvfp4_gemm(ok, ok, ok, ok, None, _FakeTensor(nbytes=2 * M * N - 2), M, N, K)
+    assert "d holds" in str(e.value)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_grouped_gemm(ok, ok, ok, ok, _FakeTensor(nbytes=4 * 8), None, ok, 64, 64, 256, 8)   # offsets [E+1]
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_quantize(_FakeTensor(nbytes=4 * 64 * 16 - 4), 64, 16, None, ok, ok)
+
+
+def test_8x4_layout_error_paths_and_sizes():
+    L = nv.lib()
+    assert L.nvfp4_scales_8x4_size(9, 80) == 16 * 8
+    assert L.nvfp4_scales_8x4_size(1, 16) == 32
+    assert L.nvfp4_scales_8x4_size(4, 40) == 0
+    assert L.nvfp4_scales_to_8x4(FAKE, FAKE, 4, 40, None) == 2
+    assert L.nvfp4_scales_to_8x4(None, FAKE, 4, 64, None) == 1
+    assert L.nvfp4_scales_from_8x4(FAKE, None, 4, 64, None) == 1
+    assert L.nvfp4_scales_from_8x4(FAKE, FAKE, -1, 64, None) == 2
+    assert L.nvfp4_scales_to_8x4(None, None, 0, 64, None) == 0

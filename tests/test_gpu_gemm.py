@@ -1,7 +1,6 @@
 """GPU GEMM parity with the oracle through the C ABI, at every plan the
 library picks for the page workloads, plus ragged, degenerate and invariant
 cases."""
-import functools
 import json
 import os
 
@@ -98,39 +97,6 @@ def test_decode_and_prefill_sweeps(name):
         assert st["strict_2ulp_frac"] > 0.999
 
 
-@functools.lru_cache(maxsize=1)
-def _oracle_quantized_large_b(gsb):
-    _, b = synth.single_operands("large_n6144_k6144", 4096)
-    return o.quantize(b, gsb)
-
-
-@pytest.mark.parametrize("m", [4096, 8192, 16384])
-def test_large_sampled_rows(m):
-    name = "large_n6144_k6144"
-    a, b = synth.single_operands(name, m)
-    gsb = o.global_encode_scale(b)
-    qb, sfb = _oracle_quantized_large_b(gsb)
-    gsa = o.global_encode_scale(a)
-    at, bt = dev(a), dev(b)
-    gsa_t, gsb_t = gpu_global_scale(at), gpu_global_scale(bt)
-    alpha_t = torch.empty(1, dtype=torch.float32, device="cuda")
-    nv.nvfp4_alpha_from_scales(gsa_t, gsb_t, alpha_t, 1)
-    alpha = o.alpha_from_scales(gsa, gsb)
-    assert host(alpha_t)[0] == alpha
-    qa_t, sfa_t = gpu_quantize(at, gsa_t)
-    qb_t, sfb_t = gpu_quantize(bt, gsb_t)
-    del at, bt
-    say(name, "M =", m, "plan", nv.nvfp4_gemm_plan(m, 6144, 6144))
-    d = gpu_gemm(qa_t, sfa_t, qb_t, sfb_t, alpha_t, m, 6144, 6144)
-    rows = np.unique(np.concatenate([np.random.default_rng(m).choice(m, 48, replace=False),
-                                     [0, 127, 128, m - 1]]))
-    np.testing.assert_array_equal(host(qb_t), qb)
-    qa_r, sfa_r = o.quantize(a[rows], gsa)
-    ridx = torch.from_numpy(rows).cuda()
-    np.testing.assert_array_equal(host(qa_t[ridx]), qa_r)
-    check_gemm(bits(d[ridx]), qa_r, sfa_r, qb, sfb, alpha, f"large M={m} sampled rows")
-
-
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 129, 512), (100, 200, 768), (65, 96, 256),
                                    (129, 130, 1024), (33, 5, 2048), (300, 1000, 256)])
 def test_ragged_shapes(M, N, K):
@@ -166,7 +132,7 @@ def test_zero_sized_calls_are_noops():
     assert (host(d) == 7).all()
 
 
-def test_split_k_workspace_reuse_and_counters_return_to_zero(monkeypatch):
+def test_split_k_workspace_reuse_and_counters_return_to_zero(force_plan):
     # one workspace, zero-filled once, serves several split-K shapes in a row
     # (auto plans: the K-group and register tiles, and the skinny split-K
     # tile forced for M = 16 and 64);
@@ -175,18 +141,12 @@ def test_split_k_workspace_reuse_and_counters_return_to_zero(monkeypatch):
               (16, 768, 6144, None), (32, 768, 6144, "10,2"), (16, 768, 6144, "3")]
     need = 0
     for (M, N, K, forced) in shapes:
-        if forced:
-            monkeypatch.setenv("NVFP4_PLAN", forced)
-        else:
-            monkeypatch.delenv("NVFP4_PLAN", raising=False)
+        force_plan(nv.FAMILY_GEMM, *map(int, forced.split(","))) if forced else force_plan(nv.FAMILY_GEMM, -1)
         assert nv.nvfp4_gemm_workspace_size(M, N, K) > 0, (M, N, K)
         need = max(need, nv.nvfp4_gemm_workspace_size(M, N, K))
     ws = nv.nvfp4_workspace_init(torch.empty(need, dtype=torch.uint8, device="cuda"))
     for (M, N, K, forced) in shapes:
-        if forced:
-            monkeypatch.setenv("NVFP4_PLAN", forced)
-        else:
-            monkeypatch.delenv("NVFP4_PLAN", raising=False)
+        force_plan(nv.FAMILY_GEMM, *map(int, forced.split(","))) if forced else force_plan(nv.FAMILY_GEMM, -1)
         a, b = synth.random_codes(M, M, K), synth.random_codes(N, N, K)
         asf = synth.random_scale_bytes(M + 1, M, K, lo=0x30, hi=0x40)
         bsf = synth.random_scale_bytes(N + 1, N, K, lo=0x30, hi=0x40)
@@ -236,9 +196,9 @@ def test_graph_capture_replays_match_eager():
             np.testing.assert_array_equal(bits(d), e)
 
 
-def test_every_plan_kind_forced(monkeypatch):
+def test_every_plan_kind_forced(force_plan):
     # each kernel instantiation (plan kind), with and without split-K, on a
-    # ragged shape; the plan is forced through NVFP4_PLAN=<kind>,<splits>
+    # ragged shape; the plan is forced through nvfp4_force_plan(kind, splits)
     M, N, K = 200, 330, 1536
     a, b = synth.random_codes(91, M, K), synth.random_codes(92, N, K)
     asf = synth.random_scale_bytes(93, M, K, lo=0x28, hi=0x48)
@@ -247,7 +207,7 @@ def test_every_plan_kind_forced(monkeypatch):
     seen = set()
     for kind in range(24):  # past the last kind the plan falls back to auto (deduplicated)
         for splits in (1, 3):
-            monkeypatch.setenv("NVFP4_PLAN", f"{kind},{splits}")
+            force_plan(nv.FAMILY_GEMM, kind, splits)
             plan = nv.nvfp4_gemm_plan(M, N, K)
             if plan in seen and splits == 1:
                 continue
@@ -258,12 +218,12 @@ def test_every_plan_kind_forced(monkeypatch):
             # bitwise deterministic: a second call (fresh workspace) repeats every bit
             d2 = gpu_gemm(at, asft, bt, bsft, scalar(1.25), M, N, K, d_fill=0x1234)
             np.testing.assert_array_equal(bits(d2), bits(d), err_msg=f"plan {plan} splits {splits} rerun")
-    monkeypatch.delenv("NVFP4_PLAN")
+    force_plan(nv.FAMILY_GEMM, -1)
     assert len(seen) >= 6
 
 
 @pytest.mark.parametrize("M,N,K", [(40, 200, 1536), (16, 768, 6144), (1, 17, 256)])
-def test_register_tiles_split_k_forced(monkeypatch, M, N, K):
+def test_register_tiles_split_k_forced(force_plan, M, N, K):
     # the register-streamed tiles (128- and 256-element K units) with split-K
     # forced on ragged shapes: partial rows and columns, K of one unit
     a, b = synth.random_codes(M + 101, M, K), synth.random_codes(N + 102, N, K)
@@ -273,7 +233,7 @@ def test_register_tiles_split_k_forced(monkeypatch, M, N, K):
     seen = set()
     for kind in range(10, 16):   # past the last kind the plan falls back to auto
         for splits in (1, 2, 3):
-            monkeypatch.setenv("NVFP4_PLAN", f"{kind},{splits}")
+            force_plan(nv.FAMILY_GEMM, kind, splits)
             key = (nv.nvfp4_gemm_plan(M, N, K), nv.nvfp4_gemm_workspace_size(M, N, K))
             if not key[0].startswith("kreg") or key in seen:
                 continue
@@ -281,11 +241,11 @@ def test_register_tiles_split_k_forced(monkeypatch, M, N, K):
             say("register tile", M, N, K, kind, splits, key)
             d = gpu_gemm(at, asft, bt, bsft, scalar(0.5), M, N, K, d_fill=0x7FC1)
             check_gemm(bits(d), a, asf, b, bsf, np.float32(0.5), f"{key} splits {splits}")
-    monkeypatch.delenv("NVFP4_PLAN")
+    force_plan(nv.FAMILY_GEMM, -1)
     assert len(seen) >= (4 if K == 256 else 11)
 
 
-def test_maximum_k_every_plan_kind(monkeypatch):
+def test_maximum_k_every_plan_kind(force_plan):
     # K = 2^22, the largest supported K: a row of codes is 2 MB, so a 256-row
     # operand tile spans 512 MB of 32-bit buffer offsets.  Every plan kind
     # (split-K forced to 3 where it applies) on a ragged 17 x 24 output,
@@ -304,7 +264,7 @@ def test_maximum_k_every_plan_kind(monkeypatch):
     seen = set()
     for kind in range(24):
         for splits in (1, 3):
-            monkeypatch.setenv("NVFP4_PLAN", f"{kind},{splits}")
+            force_plan(nv.FAMILY_GEMM, kind, splits)
             key = (nv.nvfp4_gemm_plan(M, N, K), nv.nvfp4_gemm_workspace_size(M, N, K))
             if key in seen:
                 continue
@@ -314,5 +274,5 @@ def test_maximum_k_every_plan_kind(monkeypatch):
             got = o.bf16_to_f64(bits(d))
             assert (np.abs(got - want) <= tol).all(), f"{key}: outside tolerance"
             assert np.linalg.norm(got - s) / np.linalg.norm(s) <= 1e-2, key
-    monkeypatch.delenv("NVFP4_PLAN")
+    force_plan(nv.FAMILY_GEMM, -1)
     assert len(seen) >= 10

@@ -1,5 +1,7 @@
-"""GPU grouped-by-expert GEMM parity with the oracle: the 512-token, 256-expert,
-top-8 MoE workload (sampled experts) and adversarial row distributions."""
+"""GPU grouped-by-expert GEMM parity with the oracle: adversarial row
+distributions, every grouped kernel, invalid offsets and the packed weight
+layout (the 512-token, 256-expert workload itself, every expert, is in
+test_gpu_moe_workload.py)."""
 import numpy as np
 import pytest
 import torch
@@ -7,7 +9,7 @@ import torch
 import nvfp4_block_scaled_07_amd as nv
 import synth
 from oracle import nvfp4_ref as o
-from tests.gpu_util import bits, check_gemm, dev, gpu_global_scale, gpu_quantize, host, say
+from tests.gpu_util import bits, check_gemm, dev, host, say
 
 pytestmark = pytest.mark.gpu
 SENTINEL = 0x7FC1
@@ -20,45 +22,6 @@ def _grouped(a_t, asf_t, b_t, bsf_t, off_t, alpha_t, rows, N, K, E, status=True)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     nv.nvfp4_grouped_gemm(a_t, asf_t, b_t, bsf_t, off_t, alpha_t, d, rows, N, K, E, ws, st)
     return d, st
-
-
-def test_moe_workload_512_tokens_256_experts():
-    g = synth.GROUPED
-    T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
-    tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
-    rows = int(off[-1])
-    assert rows == T * g["top_k"]
-    say("moe: quantise token activations")
-    x = synth.token_activations(T, K)
-    gsa = o.global_encode_scale(x)
-    qa_tok, sfa_tok = o.quantize(x, gsa)
-    xt = dev(x)
-    gsa_t = gpu_global_scale(xt)
-    assert host(gsa_t)[0] == gsa
-    qa_t_tok, sfa_t_tok = gpu_quantize(xt, gsa_t)
-    np.testing.assert_array_equal(host(qa_t_tok), qa_tok)
-    np.testing.assert_array_equal(host(sfa_t_tok), sfa_tok)
-    # rows ordered by expert then token (a gather of the quantised tokens)
-    qa, sfa = qa_tok[tok], sfa_tok[tok]
-    tok_t = torch.from_numpy(tok).cuda()
-    qa_t, sfa_t = qa_t_tok[tok_t].contiguous(), sfa_t_tok[tok_t].contiguous()
-    # expert weights: seeded random code and scale bytes (1.6 GB of codes)
-    say("moe: expert weights")
-    b = synth.random_codes(g["seed_expert_base"], E * N, K).reshape(E, N, K // 2)
-    bsf = synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, lo=0x20, hi=0x38).reshape(E, N, K // 16)
-    alpha = np.random.default_rng(77).uniform(0.5, 2.0, E).astype(np.float32) / np.float32(gsa)
-    b_t, bsf_t = dev(b), dev(bsf)
-    say("moe: grouped gemm rows", rows)
-    d, st = _grouped(qa_t, sfa_t, b_t, bsf_t, dev(off), dev(alpha), rows, N, K, E)
-    assert int(host(st)[0]) == 0
-    db = bits(d)
-    experts = np.unique(np.concatenate([np.random.default_rng(5).choice(E, 20, replace=False),
-                                        [0, E - 1, int(np.argmax(np.diff(off)))]]))
-    for e in experts:
-        lo, hi = int(off[e]), int(off[e + 1])
-        if hi > lo:
-            check_gemm(db[lo:hi], qa[lo:hi], sfa[lo:hi], b[e], bsf[e], alpha[e], f"expert {e}")
-    assert not (db == SENTINEL).any()
 
 
 def _small_problem(kind, rows=300, E=8, N=192, K=512, seed=0):
@@ -120,12 +83,12 @@ def test_invalid_offsets_reported_and_skipped():
 
 
 @pytest.mark.parametrize("gplan,K", [(0, 768), (1, 768), (2, 1536), (2, 768), (3, 1024), (3, 1536), (3, 768)])
-def test_every_grouped_kernel(gplan, K, monkeypatch):
-    # each grouped kernel (forced through NVFP4_GPLAN; K = 1536 lets the
+def test_every_grouped_kernel(gplan, K, force_plan):
+    # each grouped kernel (forced through nvfp4_force_plan; K = 1536 lets the
     # register kernels' prefetch depth 2 divide K / 256, K = 768 does not and
     # must fall back), ragged N, experts of 0, 1, 5, 65 and 129 rows (several
     # row passes of 32 or 64 rows)
-    monkeypatch.setenv("NVFP4_GPLAN", str(gplan))
+    force_plan(nv.FAMILY_GROUPED, gplan)
     rows, E, N = 300, 8, 330
     off, a, asf, b, bsf, alpha = _small_problem([0, 0, 5, 5, 70, 70, 71, 200, 250], rows, E, N, K, seed=40)
     say("grouped kernel", gplan, "K", K)
@@ -169,9 +132,9 @@ def _np_pack(b, bsf, N, K, E):
 
 @pytest.mark.parametrize("gplan", [2, 3])
 @pytest.mark.parametrize("kind", ["alternate", [0, 0, 5, 5, 70, 70, 71, 200, 250]])
-def test_packed_weights_layout_and_gemm(kind, gplan, monkeypatch):
+def test_packed_weights_layout_and_gemm(kind, gplan, force_plan):
     # gplan 2 / 3: passes of 32 / 64 rows over each expert's packed weights
-    monkeypatch.setenv("NVFP4_GPLAN", str(gplan))
+    force_plan(nv.FAMILY_GROUPED, gplan)
     rows, E, N, K = 300, 8, 330, 1024
     off, a, asf, b, bsf, alpha = _small_problem(kind, rows, E, N, K, seed=60)
     say("grouped packed", kind, "gplan", gplan)
@@ -193,24 +156,3 @@ def test_packed_weights_layout_and_gemm(kind, gplan, monkeypatch):
     # same bits as the unpacked grouped kernel (same arithmetic, same order)
     d2, _ = _grouped(dev(a), dev(asf), b_t, bsf_t, dev(off), dev(alpha), rows, N, K, E)
     np.testing.assert_array_equal(bits(d2), db)
-
-
-def test_packed_moe_workload_sampled_experts():
-    g = synth.GROUPED
-    T, E, N, K = g["tokens"], g["experts"], g["n"], g["k"]
-    tok, off = synth.routing(g["seed_router"], T, E, g["top_k"])
-    rows = int(off[-1])
-    say("packed moe")
-    a = synth.random_codes(71, rows, K)
-    asf = synth.random_scale_bytes(72, rows, K, lo=0x30, hi=0x40)
-    b = synth.random_codes(g["seed_expert_base"], E * N, K).reshape(E, N, K // 2)
-    bsf = synth.random_scale_bytes(g["seed_expert_base"] + 1, E * N, K, lo=0x20, hi=0x38).reshape(E, N, K // 16)
-    pb, psf = nv.grouped_pack(dev(b), dev(bsf), N, K, E)
-    d = torch.full((rows, N), SENTINEL, dtype=torch.int16, device="cuda")
-    nv.nvfp4_grouped_gemm_packed(dev(a), dev(asf), pb, psf, dev(off), None, d, rows, N, K, E)
-    db = bits(d)
-    for e in (0, 17, 128, 255, int(np.argmax(np.diff(off)))):
-        lo, hi = int(off[e]), int(off[e + 1])
-        if hi > lo:
-            check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], np.float32(1), f"packed moe expert {e}")
-    assert not (db == SENTINEL).any()

@@ -2,7 +2,8 @@
 quantiser (codes and scales equal to the oracle's wherever they are unique),
 the combine (at its fp32 summation bound), and nvfp4_moe_ffn (bit for bit
 equal to the same steps called one by one, and within 1e-2 relative
-Frobenius error of the oracle)."""
+Frobenius error of the oracle).  At the pages' shape every stage is compared
+element by element: each GEMM with the oracle fed the stage's own inputs."""
 import numpy as np
 import pytest
 import torch
@@ -11,6 +12,7 @@ import nvfp4_block_scaled_07_amd as nv
 import synth
 from oracle import moe_ref as m
 from oracle import nvfp4_ref as o
+from tests import oracle_pool as op
 from tests.gpu_util import bits, check_gemm, dev, host, say, scalar
 
 pytestmark = pytest.mark.gpu
@@ -156,19 +158,95 @@ def test_moe_ffn_small_against_oracle():
     assert fr <= 1e-2
 
 
-def test_moe_ffn_pages_shape_sampled_tokens():
-    T, H, I, E, k = 512, 6144, 2048, 256, 8
+@pytest.mark.timeout(1200)
+def test_moe_ffn_pages_shape_every_token():
+    # the pages' layer: 512 tokens, top-8 of 256 experts, H = 6144, I = 2048,
+    # each expert's weights seeded on their own.  Every element of every
+    # stage is checked: gate/up against the oracle at the GEMM tolerance, the
+    # SwiGLU codes where unique, down against the oracle fed with the GPU's own
+    # h, the combine at its summation bound, and the layer end to end against
+    # the pure-oracle chain (relative Frobenius error).
+    T, H, I, E, k, seed = 512, 6144, 2048, 256, 8, 400
+    rows = T * k
+    tok, off = synth.routing(seed, T, E, k)
+    tok = tok.astype(np.int32)
+    tr = synth.token_rows(tok, T, k)
+    tw = synth.routing_weights(seed + 1, T, k)
+    x = _bf16(synth.token_activations(T, H))
+    x32 = o.bf16_bits_to_f32(x)
+    gs_x = o.global_encode_scale(x32)
     say("moe ffn 512 tokens: weights")
-    P = _ffn_problem(T, H, I, E, k, seed=400)
+    w_gu = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+    w_gu_sf = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device="cuda")
+    w_d = torch.empty((E, H, I // 2), dtype=torch.uint8, device="cuda")
+    w_d_sf = torch.empty((E, H, I // 16), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        for t, v in zip((w_gu, w_gu_sf, w_d, w_d_sf), op.ffn_expert_weights(seed, e, H, I)):
+            t[e].copy_(torch.from_numpy(v))
+    # scales calibrated with the oracle on the first expert's rows, as in _ffn_problem
+    qa, sfa = o.quantize(o.gather_rows(x32, tok, rows), gs_x)
+    e0 = int(np.argmax(np.diff(off) > 0))
+    wg0, wgs0, wd0, wds0 = op.ffn_expert_weights(seed, e0, H, I)
+    s_gu = o.gemm_fp64(qa[off[e0]:off[e0 + 1]], sfa[off[e0]:off[e0 + 1]], wg0, wgs0)
+    a_gu = np.full(E, 2.0 / np.sqrt(np.mean(s_gu ** 2)), np.float32)
+    h = m.swiglu(o.bf16_rne(s_gu * np.float64(a_gu[0])), I)
+    gs_h = np.float32(2688.0 / (2.0 * np.abs(h).max()))
+    hq0, hsf0 = o.quantize(h.astype(np.float32), gs_h)
+    s_d = o.gemm_fp64(hq0, hsf0, wd0, wds0)
+    a_d = np.full(E, 1.0 / np.sqrt(np.mean(s_d ** 2)), np.float32)
+
     say("moe ffn 512 tokens: run")
-    out, _ = _run_ffn(P, T, H, I, E, k)
-    tokens = [0, 311]
-    ref, _ = m.moe_ffn(P["x"], P["gs_x"], P["tok"], P["off"], P["w_gu"], P["w_gu_sf"], P["a_gu"], P["gs_h"],
-                       P["w_d"], P["w_d_sf"], P["a_d"], P["tr"], P["tw"], I, tokens=tokens)
-    for i, t in enumerate(tokens):
-        fr = _frob(out[t], ref[i])
-        say("token", t, "relative Frobenius error", fr)
-        assert fr <= 1e-2
+    pgu, pgusf = nv.grouped_pack(w_gu, w_gu_sf, 2 * I, H, E)
+    pd, pdsf = nv.grouped_pack(w_d, w_d_sf, H, I, E)
+    del w_gu, w_gu_sf, w_d, w_d_sf
+    x_t, tok_t, off_t, tr_t, tw_t = dev(x.view(np.int16)), dev(tok), dev(off), dev(tr), dev(tw)
+    gs_x_t, gs_h_t, a_gu_t, a_d_t = scalar(gs_x), scalar(gs_h), dev(a_gu), dev(a_d)
+    ws = torch.empty(nv.nvfp4_moe_ffn_workspace_size(T, H, I, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    nv.nvfp4_moe_ffn(x_t, gs_x_t, tok_t, off_t, pgu, pgusf, a_gu_t, gs_h_t, pd, pdsf, a_d_t, tr_t, tw_t, out,
+                     T, H, I, E, k, ws, st)
+    assert int(host(st)[0]) == 0
+    # the same steps one by one, for their intermediates
+    gu = torch.empty((rows, 2 * I), dtype=torch.int16, device="cuda")
+    nv.nvfp4_grouped_gemm_packed_fused(x_t, tok_t, gs_x_t, pgu, pgusf, off_t, a_gu_t, gu, rows, T, 2 * I, H, E)
+    hq = torch.empty((rows, I // 2), dtype=torch.uint8, device="cuda")
+    hsf = torch.empty((rows, I // 16), dtype=torch.uint8, device="cuda")
+    nv.nvfp4_swiglu_quantize(gu, rows, I, gs_h_t, hq, hsf)
+    down = torch.empty((rows, H), dtype=torch.int16, device="cuda")
+    nv.nvfp4_grouped_gemm_packed(hq, hsf, pd, pdsf, off_t, a_d_t, down, rows, H, I, E)
+    out2 = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    nv.nvfp4_moe_combine(down, tr_t, tw_t, out2, T, H, k, rows)
+    out_b, gu_b, hq_h, hsf_h, down_b = bits(out), bits(gu), host(hq), host(hsf), bits(down)
+    np.testing.assert_array_equal(out_b, bits(out2))
+
+    say("moe ffn 512 tokens: oracle, every expert")
+    jobs = []
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            jobs.append((seed, e, H, I, qa[lo:hi], sfa[lo:hi], a_gu[e], gs_h, a_d[e], gu_b[lo:hi], hq_h[lo:hi],
+                         hsf_h[lo:hi], down_b[lo:hi]))
+    st_gu, st_d = op.Stats(), op.Stats()
+    chain = np.zeros((rows, H), np.uint16)
+    with op.make_pool() as pool:
+        for e, sg, sd, ch in pool.imap(op.ffn_expert_oracle, jobs):
+            st_gu.add(sg.check(f"gate/up expert {e}", strict_frac=None))
+            st_d.add(sd.check(f"down expert {e}", strict_frac=None))
+            chain[int(off[e]):int(off[e + 1])] = ch
+    st_gu.check("gate/up")
+    st_d.check("down (GPU h)")
+    assert st_gu.n == rows * 2 * I and st_d.n == rows * H
+    say("gate/up", st_gu.n, "elements, frob", st_gu.frob, "; down", st_d.n, "elements, frob", st_d.frob)
+    amb, n = _check_swiglu_codes(hq_h, hsf_h, gu_b, I, gs_h)
+    say("swiglu: ambiguous blocks", amb, "of", n)
+    assert amb <= n // 100
+    ref = m.moe_combine(down_b, tr, tw)
+    tol = m.combine_tolerance(down_b, tr, tw, ref)
+    assert (np.abs(o.bf16_to_f64(out_b) - o.bf16_to_f64(ref)) <= tol).all(), "combine outside its bound"
+    fr = _frob(out_b, m.moe_combine(chain, tr, tw))
+    say("layer vs the pure-oracle chain: relative Frobenius error", fr)
+    assert fr <= 1e-2
 
 
 def test_moe_ffn_graph_replays_match_eager():

@@ -1,7 +1,8 @@
 """GPU parity of the MXFP4 GEMM (nvfp4_mx_gemm) with the MX oracle, through
 the C ABI: every MX plan (LDS-staged and register tiles) forced on ragged shapes, the attention-projection
-sweep and sampled rows of the large shapes with seeded random codes and E8M0
-scales, determinism, and the no-op / error paths that need a device."""
+sweep with seeded random codes and E8M0 scales, determinism, and the no-op /
+error paths that need a device (the large shapes, every element, are in
+test_gpu_large.py)."""
 import numpy as np
 import pytest
 import torch
@@ -49,7 +50,7 @@ def _check(d_bits, a, asf, b, bsf, alpha, label, rows=None):
     assert np.mean(err <= 2 * o.bf16_ulp(ref)) > 0.999, label
 
 
-def test_every_mx_plan_forced_on_ragged_shapes(monkeypatch):
+def test_every_mx_plan_forced_on_ragged_shapes(force_plan):
     # each MX tile, with and without split-K, on shapes that cut every tile edge
     for (M, N, K) in [(200, 330, 1536), (1, 1, 256), (257, 129, 512)]:
         a, asf, b, bsf = _operands(M + N, M, N, K)
@@ -57,7 +58,7 @@ def test_every_mx_plan_forced_on_ragged_shapes(monkeypatch):
         seen = set()
         for kind in range(10):   # past the last kind the plan falls back to auto
             for splits in (1, 3):
-                monkeypatch.setenv("NVFP4_MX_PLAN", f"{kind},{splits}")
+                force_plan(nv.FAMILY_MX, kind, splits)
                 plan = nv.nvfp4_mx_gemm_plan(M, N, K)
                 if (plan, nv.nvfp4_mx_gemm_workspace_size(M, N, K)) in seen:
                     continue
@@ -67,7 +68,7 @@ def test_every_mx_plan_forced_on_ragged_shapes(monkeypatch):
                 _check(bits(d), a, asf, b, bsf, np.float32(0.75), f"{M}x{N}x{K} {plan} s{splits}")
                 d2 = _mx_gemm(at, asft, bt, bsft, scalar(0.75), M, N, K, fill=0x1234)
                 np.testing.assert_array_equal(bits(d2), bits(d), err_msg=f"{plan} rerun not bitwise equal")
-        monkeypatch.delenv("NVFP4_MX_PLAN")
+        force_plan(nv.FAMILY_MX, -1)
 
 
 def test_attention_projection_sweep():
@@ -82,16 +83,6 @@ def test_attention_projection_sweep():
         _check(bits(d), a[:m], asf[:m], b, bsf, None, f"mx M={m}")
 
 
-@pytest.mark.parametrize("m", [4096, 8192])
-def test_large_shapes_sampled_rows(m):
-    N = K = 6144
-    a, asf, b, bsf = _operands(7200 + m, m, N, K)
-    say("mx large", m, N, K, nv.nvfp4_mx_gemm_plan(m, N, K))
-    d = _mx_gemm(dev(a), dev(asf), dev(b), dev(bsf), scalar(0.5), m, N, K)
-    rows = np.random.default_rng(m).choice(m, 48, replace=False)
-    _check(bits(d), a, asf, b, bsf, np.float32(0.5), f"mx large {m}", rows=np.sort(rows))
-
-
 def test_zero_sized_and_bad_k():
     d = torch.zeros((0, 8), dtype=torch.int16, device="cuda")
     x = torch.zeros((16, 128), dtype=torch.uint8, device="cuda")
@@ -101,7 +92,7 @@ def test_zero_sized_and_bad_k():
     assert e.value.status == 2
 
 
-def test_every_mx_plan_at_maximum_k(monkeypatch):
+def test_every_mx_plan_at_maximum_k(force_plan):
     # K = 2^22 (2 MB code rows, 128 KB scale rows) on every MX plan, with and
     # without split-K, against one oracle evaluation
     M, N, K = 17, 24, 1 << 22
@@ -116,7 +107,7 @@ def test_every_mx_plan_at_maximum_k(monkeypatch):
     seen = set()
     for kind in range(10):
         for splits in (1, 3):
-            monkeypatch.setenv("NVFP4_MX_PLAN", f"{kind},{splits}")
+            force_plan(nv.FAMILY_MX, kind, splits)
             key = (nv.nvfp4_mx_gemm_plan(M, N, K), nv.nvfp4_mx_gemm_workspace_size(M, N, K))
             if key in seen:
                 continue
@@ -125,5 +116,5 @@ def test_every_mx_plan_at_maximum_k(monkeypatch):
             got = o.bf16_to_f64(bits(_mx_gemm(at, asft, bt, bsft, scalar(alpha), M, N, K)))
             assert (np.abs(got - want) <= tol).all(), f"{key}: outside tolerance"
             assert np.linalg.norm(got - s) / np.linalg.norm(s) <= 1e-2, key
-    monkeypatch.delenv("NVFP4_MX_PLAN")
+    force_plan(nv.FAMILY_MX, -1)
     assert len(seen) >= 8

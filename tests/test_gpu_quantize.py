@@ -36,23 +36,6 @@ def test_workload_tensors_with_global_scale(name):
         _check_quant(x, gs_ref, gs_t, f"{name} {lab}")
 
 
-def test_large_activation_sampled_rows():
-    # 16384 x 6144 activations: global scale over the whole tensor, codes
-    # compared on a seeded sample of rows (rows are independent given gs)
-    a, _ = synth.single_operands("large_n6144_k6144", 16384)
-    at = dev(a)
-    say("global scale large A")
-    gs_t = gpu_global_scale(at)
-    gs_ref = o.global_encode_scale(a)
-    assert host(gs_t)[0] == gs_ref
-    say("quantize large A")
-    q, sf = gpu_quantize(at, gs_t)
-    rows = np.unique(np.concatenate([np.random.default_rng(0).choice(16384, 384, replace=False), [0, 16383]]))
-    q_ref, sf_ref = o.quantize(a[rows], gs_ref)
-    np.testing.assert_array_equal(host(sf[torch.from_numpy(rows).to(sf.device)]), sf_ref)
-    np.testing.assert_array_equal(host(q[torch.from_numpy(rows).to(q.device)]), q_ref)
-
-
 def test_rounding_ties_and_edges():
     # blocks with amax exactly 6 and gs = 1 (scale 1, r = 1) carrying every
     # e2m1 tie and its fp32 neighbours; zero blocks; -0; saturation
@@ -132,3 +115,44 @@ def test_e2m1_rounding_sweep_over_fp32_patterns():
         for lo in range(0, x.shape[0], 1 << 16):
             part = np.ascontiguousarray(x[lo:lo + (1 << 16)])
             _check_quant(part, np.float32(1), None, f"e2m1 sweep sign {sign:+.0f} rows {lo}")
+
+
+def _e4m3_midpoints() -> np.ndarray:
+    """Every midpoint between consecutive non-negative finite e4m3 values
+    (codes 0x00..0x7E), plus the one above 448 that saturation removes."""
+    v = np.array([o.e4m3_value(c) for c in range(0x7F)], np.float64)
+    mids = np.concatenate([(v[:-1] + v[1:]) / 2, [464.0]])
+    assert (mids.astype(np.float32).astype(np.float64) == mids).all()   # exact in fp32
+    return mids.astype(np.float32)
+
+
+def test_e4m3_scale_ties_and_subnormal_seam():
+    # t = (amax / 6) * gs lands exactly on every e4m3 midpoint (the scale
+    # rounds to the even code), with its fp32 neighbours on either side.
+    # 1) gs = 1, block amax = 6 * mid: 6 * mid is exact and so is (6 * mid) / 6.
+    mids = _e4m3_midpoints()
+    seam = np.float32(2.0 ** -6 - 2.0 ** -10)        # between 7 * 2^-9 (0x07) and 2^-6 (0x08)
+    assert seam in mids
+    ts = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    rng = np.random.default_rng(12)
+    blocks = np.zeros((len(ts), 16), np.float32)
+    blocks[:, 0] = np.float32(6.0) * ts
+    blocks[:, 1:] = (rng.uniform(-1, 1, (len(ts), 15)) * blocks[:, :1]).astype(np.float32)
+    flat = np.concatenate([blocks.reshape(-1), np.zeros((-blocks.size) % 64, np.float32)])
+    x = flat.reshape(-1, 64)
+    _check_quant(x, np.float32(1), None, "e4m3 ties, gs = 1")
+    # the oracle's scale bytes at the exact midpoints are the even codes
+    _, sf = o.quantize(blocks[: len(mids)], np.float32(1))
+    lo = np.array([c for c in range(0x7E)] + [0x7E])
+    even = np.where(lo % 2 == 0, lo, lo + 1)
+    even[-1] = 0x7E                                       # 464 saturates to 448
+    np.testing.assert_array_equal(sf[:, 0], even)
+    # 2) block amax = 6 and gs = the midpoint itself, for the seam and a few
+    # subnormal, normal and top midpoints (one tensor scale per call)
+    for gs in [seam, mids[0], mids[3], mids[40], mids[100], mids[-2], mids[-1]]:
+        blk = np.zeros((4, 64), np.float32)
+        blk[:, ::16] = 6.0
+        blk[:, 1::16] = -6.0 * np.float32(0.3)
+        blk[:, 5::16] = np.float32(2.9)
+        gs_t = torch.tensor([gs], dtype=torch.float32, device="cuda")
+        _check_quant(blk, np.float32(gs), gs_t, f"e4m3 tie gs = {float(gs)!r}")
