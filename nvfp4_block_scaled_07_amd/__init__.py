@@ -26,6 +26,7 @@ STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ER
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 SIGNATURES = {
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "nvfp4_gemm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "nvfp4_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nvfp4_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "nvfp4_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
@@ -215,6 +216,18 @@ def nvfp4_mx_gemm(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, workspace=
                              _ptr(alpha, 4, "alpha", f), _ptr(d, 2 * _n(M, N), "d", f), M, N, K,
                              _ptr(workspace, 0, "workspace", f), _bytes(workspace), _stream(stream))
     _check(st, "nvfp4_mx_gemm")
+    return d
+
+
+def nvfp4_gemm_noalloc(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, stream=None):
+    """nvfp4_gemm without a workspace: split-K scratch in the library's fixed
+    per-device array (calls overlapping on one GPU race); see include/nvfp4.h."""
+    f = "nvfp4_gemm_noalloc"
+    st = lib().nvfp4_gemm_noalloc(_ptr(a, _n(M, K) // 2, "a", f), _ptr(a_sf, _n(M, K) // 16, "a_sf", f),
+                                  _ptr(b, _n(N, K) // 2, "b", f), _ptr(b_sf, _n(N, K) // 16, "b_sf", f),
+                                  _ptr(alpha, 4, "alpha", f), _ptr(d, 2 * _n(M, N), "d", f), M, N, K,
+                                  _stream(stream))
+    _check(st, f)
     return d
 
 

@@ -46,11 +46,13 @@ nvfp4_status check_k(int64_t K) {
   return NVFP4_OK;
 }
 
-// Checks, plan choice and launch of nvfp4_gemm.
+// nvfp4_gemm and nvfp4_gemm_noalloc: the same checks, plans and kernels; the
+// second takes its split-K scratch from the library's fixed per-device array
+// instead of a caller workspace.
 nvfp4_status gemm_call(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
                        const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  const char* fn = "nvfp4_gemm launch";
+                       size_t workspace_bytes, void* stream, bool noalloc) {
+  const char* fn = noalloc ? "nvfp4_gemm_noalloc launch" : "nvfp4_gemm launch";
   if (M < 0 || N < 0) return fail(NVFP4_ERR_SHAPE, "M = %lld, N = %lld must be >= 0", (long long)M, (long long)N);
   nvfp4_status s = check_k(K);
   if (s != NVFP4_OK) return s;
@@ -64,10 +66,18 @@ nvfp4_status gemm_call(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, 
     return fail(NVFP4_ERR_UNSUPPORTED, "dimensions above 2^30 are not supported");
   const nvfp4::GemmPlan plan = nvfp4::choose_plan(M, N, K);
   if (plan.workspace > 0) {
-    if (!workspace || workspace_bytes < plan.workspace)
-      return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu workspace bytes, got %zu", plan.name, plan.workspace,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (noalloc) {
+      if (plan.workspace > nvfp4::kNoAllocScratchBytes)
+        return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu scratch bytes; nvfp4_gemm_noalloc holds at most %zu",
+                    plan.name, plan.workspace, nvfp4::kNoAllocScratchBytes);
+      hipError_t e = nvfp4::noalloc_scratch((hipStream_t)stream, &workspace);
+      if (e != hipSuccess) return hip_status(e, "nvfp4_gemm_noalloc scratch set-up");
+    } else {
+      if (!workspace || workspace_bytes < plan.workspace)
+        return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu workspace bytes, got %zu", plan.name, plan.workspace,
+                    workspace ? workspace_bytes : (size_t)0);
+      if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
+    }
   }
   nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 0, 1, 1};
   return hip_status(nvfp4::launch_gemm(plan, p, (hipStream_t)stream), fn);
@@ -101,7 +111,12 @@ const char* nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K) {
 nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
                         const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return gemm_call(a, a_sf, b, b_sf, alpha, d, M, N, K, workspace, workspace_bytes, stream);
+  return gemm_call(a, a_sf, b, b_sf, alpha, d, M, N, K, workspace, workspace_bytes, stream, false);
+}
+
+nvfp4_status nvfp4_gemm_noalloc(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                                const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_call(a, a_sf, b, b_sf, alpha, d, M, N, K, nullptr, 0, stream, true);
 }
 
 size_t nvfp4_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {

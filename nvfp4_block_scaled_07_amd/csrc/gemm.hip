@@ -46,6 +46,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -2022,6 +2023,38 @@ hipError_t launch_grouped_fused(GroupedLaunch p, bool packed, int32_t* status, h
 }
 
 size_t grouped_workspace(int64_t, int64_t, int64_t, int32_t) { return 0; }
+
+// Scratch for nvfp4_gemm_noalloc, the entry point for callers that cannot
+// allocate device memory: the split-K arrival counters (first kCounterBytes)
+// and fp32 partial tiles that nvfp4_gemm keeps in its workspace.  Every GPU
+// that runs the library holds its own copy until the process ends.  In host
+// code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is handed to
+// kernels.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the counters must start at zero (every completed call leaves them so)
+    e = launch_workspace_init(p, kCounterBytes, stream);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 
 
 __global__ void k_fill_zero(uint32_t* p, int64_t n) {

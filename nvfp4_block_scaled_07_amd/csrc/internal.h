@@ -68,6 +68,13 @@ hipError_t launch_pack_b(const uint8_t* b, const uint8_t* b_sf, int64_t N, int64
                          uint8_t* psf, hipStream_t stream);
 size_t grouped_workspace(int64_t rows, int64_t N, int64_t K, int32_t E);
 
+// Scratch of nvfp4_gemm_noalloc: a fixed device array per GPU (this many
+// bytes), whose address is looked up, and whose counters are cleared on
+// `stream`, at the first call on each device.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);
 
 // MoE expert FFN pieces (moe.hip): SwiGLU of a [rows][2I] bf16 gate/up
