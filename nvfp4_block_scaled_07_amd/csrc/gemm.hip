@@ -1558,6 +1558,7 @@ typedef KCfg<64, 32, 4, 2, 2, 1> MxReg64x32;
 // large M: 256 K per stage (each row's codes one 128-byte line), 2 stages
 typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2> CfgTile256w8k256;  // 8 waves of 128x64
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2> CfgTile128k256;    // 4 waves of 64x64
+typedef Cfg<256, 192, 4, 2, 32, 256, 2, 0, 1, 2> CfgTile256x192;    // 8 waves of 64x96, 126 KB LDS
 // MXFP4 tiles (E8M0 scale per 32 elements, scaled FP4 MFMA)
 typedef Cfg<256, 256, 2, 2, 32, 256, 2, 0, 1, 1, 32> CfgMx256;      // 4 waves x 128x128, 136 KB LDS
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx128;      // 4 waves x 64x64, 68 KB (split-K)
@@ -1596,6 +1597,7 @@ static const PlanKind kKinds[] = {
     {"kreg64x32_mfma16", 64, 32, 256, true, true, false, KReg64x32::KS},
     {"tile256x256w8k256_mfma32", 256, 256, 256, false},
     {"tile128x128k256_mfma32", 128, 128, 256, true},
+    {"tile256x192w8k256_mfma32", 256, 192, 256, false},
 };
 static const PlanKind kMxKinds[] = {
     {"mx256x256_fp4mfma", 256, 256, 256, false, false, true},
@@ -1686,14 +1688,15 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
 // of 16x16, 32x16, 32x32, 64x32 that needs at most one work-group per CU;
 // above that, 64x64 K-group tiles (split-K while there are fewer than 192 of
 // them) until 128x128 tiles fill the CUs three times, then 128x128 tiles,
-// and 256x256 tiles of 8 waves once those fill the CUs twice (both staging
-// 256 K per stage: whole 128-byte lines per row).
+// and tiles of 8 waves, 256x256 or 256x192, once either fills the CUs twice
+// (all staging 256 K per stage: whole 128-byte lines per row).
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   int kind = -1;
   int forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
   if (M <= 512) {
     static const int kreg_kinds[] = {10, 11, 12, 13};  // 16x16, 32x16, 32x32, 64x32
     for (int kk : kreg_kinds) {
@@ -1704,10 +1707,17 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
       }
     }
   }
+  if (kind < 0 && M > 64 && (t256 >= 2 * kCUs || t192 >= 2 * kCUs)) {
+    // 256x256 or 256x192 tiles, one work-group per CU: the 192-column tile
+    // when its rounds of 256 work-groups cover less tile area (its 64x96
+    // wave tiles cost about 5% more dequantisation per MFMA)
+    const int64_t r256 = (t256 + kCUs - 1) / kCUs, r192 = (t192 + kCUs - 1) / kCUs;
+    if (r192 * 192 * 105 < r256 * 256 * 100) kind = 16;
+    else if (t256 >= 2 * kCUs) kind = 14;
+  }
   if (kind < 0) {
     if (M <= 32) kind = 3;
     else if (M <= 64) kind = 4;
-    else if (t256 >= 2 * kCUs) kind = 14;
     else if (t128 >= 3 * kCUs) kind = 15;
     else kind = 9;
   }
@@ -1761,6 +1771,7 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
     case 13: launch_kreg<KReg64x32>(pl, p, stream); break;
     case 14: launch_one<CfgTile256w8k256, false>(pl, p, stream); break;
     case 15: launch_one<CfgTile128k256, true>(pl, p, stream); break;
+    case 16: launch_one<CfgTile256x192, false>(pl, p, stream); break;
     default: launch_one<CfgTile64k4, true>(pl, p, stream); break;
   }
   return hipGetLastError();
