@@ -1565,6 +1565,7 @@ typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx128;      // 4 waves x
 typedef Cfg<64, 64, 2, 2, 32, 256, 3, 0, 1, 2, 32> CfgMx64;         // 4 waves x 32x32 (split-K)
 typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2, 32> CfgMx256w8;    // 8 waves x 128x64
 typedef Cfg<256, 256, 2, 4, 32, 128, 4, 0, 1, 2, 32> CfgMx256w8s4;  // the same, 4 stages of 128
+typedef Cfg<256, 192, 4, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx256x192;  // 8 waves x 64x96, 119 KB
 typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass
@@ -1609,6 +1610,7 @@ static const PlanKind kMxKinds[] = {
     {"mxreg32x16_fp4mfma", 32, 16, 256, true, true, true, MxReg32x16::KS},
     {"mxreg32x32_fp4mfma", 32, 32, 256, true, true, true, MxReg32x32::KS},
     {"mxreg64x32_fp4mfma", 64, 32, 256, true, true, true, MxReg64x32::KS},
+    {"mx256x192w8_fp4mfma", 256, 192, 256, false, false, true},
 };
 static constexpr int kNumMxKinds = (int)(sizeof(kMxKinds) / sizeof(kMxKinds[0]));
 static constexpr int kNumKinds = (int)(sizeof(kKinds) / sizeof(kKinds[0]));
@@ -1796,7 +1798,15 @@ GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K) {
       }
     }
   }
-  if (kind < 0) kind = t256 >= kCUs ? 3 : (t128 >= kCUs ? 1 : 2);
+  if (kind < 0) {
+    // 256x192 tiles when they fill the CUs twice and their rounds of 256
+    // work-groups cover less tile area than 256x256 tiles (its 64x96 wave
+    // tiles read about 11% more LDS bytes per MFMA)
+    const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
+    const int64_t r256 = (t256 + kCUs - 1) / kCUs, r192 = (t192 + kCUs - 1) / kCUs;
+    if (t192 >= 2 * kCUs && r192 * 192 * 112 < r256 * 256 * 100) kind = 9;
+    else kind = t256 >= kCUs ? 3 : (t128 >= kCUs ? 1 : 2);
+  }
   int fk = -1, fs = 0;
   if (forced_plan(kForceMx, &fk, &fs) && fk < kNumMxKinds) {
     kind = fk;
@@ -1823,6 +1833,7 @@ hipError_t launch_mx_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) 
     case 1: launch_one<CfgMx128, true>(pl, p, stream); break;
     case 3: launch_one<CfgMx256w8, false>(pl, p, stream); break;
     case 4: launch_one<CfgMx256w8s4, false>(pl, p, stream); break;
+    case 9: launch_one<CfgMx256x192, false>(pl, p, stream); break;
     case 5: launch_kreg<MxReg16x16>(pl, p, stream); break;
     case 6: launch_kreg<MxReg32x16>(pl, p, stream); break;
     case 7: launch_kreg<MxReg32x32>(pl, p, stream); break;
