@@ -85,7 +85,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf,
  * nvfp4_gemm for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same checks, plans, kernels and results as nvfp4_gemm, with the split-K
- * counters and partial tiles in a fixed 8 MiB array that the library holds on
+ * counters and partial tiles in a fixed 16 MiB array that the library holds on
  * each GPU it runs on, until the process ends.  No allocation and no workspace
  * argument.  The first call on a device looks the array up
  * (hipGetSymbolAddress) and clears its counters with a kernel on `stream`;
@@ -93,7 +93,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf,
  * shares the array: calls that may overlap on one GPU (other streams, other
  * threads) race and must be ordered by the caller.  A shape whose plan needs
  * more scratch than the array holds (none of the library's own plans does:
- * at most 4 MiB) returns NVFP4_ERR_WORKSPACE.
+ * at most 12 MiB) returns NVFP4_ERR_WORKSPACE.
  */
 nvfp4_status nvfp4_gemm_noalloc(const uint8_t* a, const uint8_t* a_sf,
                                 const uint8_t* b, const uint8_t* b_sf,

@@ -511,6 +511,44 @@ __device__ __forceinline__ void store_bf16(const typename C::Acc (&acc)[C::TM][C
   }
 }
 
+// Split-K exchange.  The partial tiles and the arrival counters are the only
+// memory the work-groups of one call share.  They are written and read only
+// with agent-coherent accesses (the sc1 cache policy: through to the level
+// where the L2s of all XCDs agree), so the exchange needs no L2 write-back or
+// invalidation of the whole cache, which costs microseconds while other
+// work-groups still stream.  Ordering: every wave's partial stores complete
+// (s_waitcnt vmcnt(0)) before the work-group barrier after which its arrival
+// is counted, and the last split issues its partial loads only after it has
+// read the count.  The accesses go through buffer descriptors bounded by the
+// tile's partial block, so an index outside it reads zero and writes nothing.
+constexpr int kCoherent = 16;  // buffer cache policy: sc1
+
+__device__ __forceinline__ rsrc_t partial_rsrc(const float* block, int slots, int tile_floats) {
+  return make_rsrc(block, (uint32_t)((int64_t)slots * tile_floats * 4));
+}
+__device__ __forceinline__ void store_coherent(const rsrc_t& r, uint32_t off, f4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ void store_coherent(const rsrc_t& r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ f4_t load_coherent4(const rsrc_t& r, uint32_t off) {
+  return __builtin_bit_cast(f4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ float load_coherent(const rsrc_t& r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent));
+}
+
+// Count one arrival at a tile's counter (thread 0 of the work-group, after
+// the barrier that follows its partial stores); true for the last of S.
+__device__ __forceinline__ bool count_arrival(int* counter, int S) {
+  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+}
+// The last split leaves the counter at zero for the next call.
+__device__ __forceinline__ void reset_counter(int* counter) {
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Split-K partials are kept in the accumulators' own register layout: float4
 // chunk i of lane l of wave slot w (within a K-group) sits at index
 // (w * kChunks + i) * 64 + l, so every store and every load of the reduction
@@ -523,11 +561,12 @@ struct PartLayout {
   static_assert(kQ * 4 == C::BM * C::BN, "partial tile size");
 };
 
+// Split z's partial tile into slot z of the tile's block (descriptor r).
 template <class C>
-__device__ __forceinline__ void store_partial(const typename C::Acc (&acc)[C::TM][C::TN], float* tile) {
+__device__ __forceinline__ void store_partial(const typename C::Acc (&acc)[C::TM][C::TN], const rsrc_t& r, int z) {
   typedef PartLayout<C> P;
   const int lane = threadIdx.x & 63, gw = wave_id() % C::kGroupWaves;
-  f4_t* dst = (f4_t*)tile + (int64_t)gw * P::kChunks * 64 + lane;
+  const uint32_t base = (uint32_t)(z * P::kQ + gw * P::kChunks * 64 + lane) * 16;
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
@@ -537,7 +576,7 @@ __device__ __forceinline__ void store_partial(const typename C::Acc (&acc)[C::TM
         f4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[tm][tn][4 * q + e];
-        dst[((tm * C::TN + tn) * P::kAccQ + q) * 64] = v;
+        store_coherent(r, base + (uint32_t)(((tm * C::TN + tn) * P::kAccQ + q) * 64 * 16), v);
       }
 }
 
@@ -548,12 +587,11 @@ __device__ __forceinline__ void store_partial(const typename C::Acc (&acc)[C::TM
 // where four waves per SIMD must fit), so a thread needs about
 // ceil(positions * S / kLoads) memory round trips.
 template <class C, int S>
-__device__ __forceinline__ void reduce_partials_s(const float* part, float alpha, uint16_t* out, int64_t ldo,
+__device__ __forceinline__ void reduce_partials_s(const rsrc_t& r, float alpha, uint16_t* out, int64_t ldo,
                                                   int rows_valid, int cols_valid) {
   typedef PartLayout<C> P;
   constexpr int kLoads = C::OCC >= 4 ? 8 : 16;
   constexpr int PB = S >= kLoads ? 1 : kLoads / S;  // positions per batch
-  const f4_t* src = (const f4_t*)part;
   for (int f0 = threadIdx.x; f0 < P::kQ; f0 += C::kThreads * PB) {
     f4_t v[PB][S];
 #pragma unroll
@@ -561,7 +599,7 @@ __device__ __forceinline__ void reduce_partials_s(const float* part, float alpha
       const int f = f0 + b * C::kThreads;
       if (f < P::kQ) {
 #pragma unroll
-        for (int z = 0; z < S; ++z) v[b][z] = src[z * P::kQ + f];
+        for (int z = 0; z < S; ++z) v[b][z] = load_coherent4(r, (uint32_t)(z * P::kQ + f) * 16);
       }
     }
 #pragma unroll
@@ -588,11 +626,11 @@ __device__ __forceinline__ void reduce_partials_s(const float* part, float alpha
 constexpr int kMaxSplits = 16;
 
 template <class C>
-__device__ __forceinline__ void reduce_partials(const float* part, int S, float alpha, uint16_t* out, int64_t ldo,
+__device__ __forceinline__ void reduce_partials(const rsrc_t& r, int S, float alpha, uint16_t* out, int64_t ldo,
                                                 int rows_valid, int cols_valid) {
   switch (S) {
 #define NVFP4_RED(n) \
-  case n: reduce_partials_s<C, n>(part, alpha, out, ldo, rows_valid, cols_valid); break;
+  case n: reduce_partials_s<C, n>(r, alpha, out, ldo, rows_valid, cols_valid); break;
     NVFP4_RED(2) NVFP4_RED(3) NVFP4_RED(4) NVFP4_RED(5) NVFP4_RED(6) NVFP4_RED(7) NVFP4_RED(8) NVFP4_RED(9)
     NVFP4_RED(10) NVFP4_RED(11) NVFP4_RED(12) NVFP4_RED(13) NVFP4_RED(14) NVFP4_RED(15) NVFP4_RED(16)
 #undef NVFP4_RED
@@ -703,22 +741,15 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   const int tid = threadIdx.x;
   constexpr int kTileFloats = C::BM * C::BN;
   int* counter = (int*)p.ws + tile;
-  float* part = p.ws + kCounterBytes / 4 + (int64_t)tile * S * kTileFloats;
-  if (lead) store_partial<C>(acc, part + (int64_t)z * kTileFloats);
-  // every wave's partial stores reach L2, then one agent-scope release (L2
-  // write-back) publishes them before the arrival is counted
-  __builtin_amdgcn_s_waitcnt(0);
+  const rsrc_t part = partial_rsrc(p.ws + kCounterBytes / 4 + (int64_t)tile * S * kTileFloats, S, kTileFloats);
+  if (lead) store_partial<C>(acc, part, z);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
   __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = prev == S - 1;
-    if (prev == S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
+  if (tid == 0) last_flag = count_arrival(counter, S);
   __syncthreads();
   if (!last_flag) return;
   reduce_partials<C>(part, S, alpha, out, p.N, A.rows, B.rows);
-  if (tid == 0) *counter = 0;  // ready for the next call
+  if (tid == 0) reset_counter(counter);
 }
 
 // Offsets check for the grouped GEMM: status = 0, or 1 + first bad expert.
@@ -1497,7 +1528,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   __syncthreads();
   const float alpha = p.alpha ? *p.alpha : 1.0f;
   // the work-group's tile, row-major, columns fastest (contiguous stores)
-  float* part = p.ws + kCounterBytes / 4 + ((int64_t)tile * S + z) * C::kTileFloats;
+  const rsrc_t part = partial_rsrc(p.ws + kCounterBytes / 4 + (int64_t)tile * S * C::kTileFloats, S, C::kTileFloats);
   for (int x = threadIdx.x; x < C::kTileFloats; x += C::kThreads) {
     const int row = x / C::BN, col = x % C::BN;
     const int rr = row & 15, cc = col & 15;
@@ -1505,31 +1536,25 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < C::KS; ++w) sum += red[w * C::kTileFloats + idx];
-    if (S > 1) part[x] = sum;
+    if (S > 1) store_coherent(part, (uint32_t)(z * C::kTileFloats + x) * 4, sum);
     else if (row < rows_a && col < rows_b) p.d[(m0 + row) * p.N + n0 + col] = f32_to_bf16_bits(alpha * sum);
   }
   if (S == 1) return;
   // split K: publish the partial, count arrivals, the last split sums all S
   // partials in split order and stores bf16 (then resets the counter)
   int* counter = (int*)p.ws + tile;
-  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = prev == S - 1;
-    if (prev == S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
+  if (threadIdx.x == 0) last_flag = count_arrival(counter, S);
   __syncthreads();
   if (!last_flag) return;
-  const float* parts = p.ws + kCounterBytes / 4 + (int64_t)tile * S * C::kTileFloats;
   for (int x = threadIdx.x; x < C::kTileFloats; x += C::kThreads) {
     const int row = x / C::BN, col = x % C::BN;
     float sum = 0.f;
-    for (int zz = 0; zz < S; ++zz) sum += parts[(int64_t)zz * C::kTileFloats + x];
+    for (int zz = 0; zz < S; ++zz) sum += load_coherent(part, (uint32_t)(zz * C::kTileFloats + x) * 4);
     if (row < rows_a && col < rows_b) p.d[(m0 + row) * p.N + n0 + col] = f32_to_bf16_bits(alpha * sum);
   }
-  if (threadIdx.x == 0) *counter = 0;  // ready for the next call
+  if (threadIdx.x == 0) reset_counter(counter);
 }
 
 // ---------------------------------------------------------------------------
@@ -1620,7 +1645,7 @@ static_assert(kCounterBytes / 4 >= kCUs, "split-K runs only below kCUs tiles");
 static const int64_t kMaxPartialBytesPerTile = 256 * 1024;  // one CU reduces a tile
 
 static const int64_t kTargetBlocks = 384;   // 1.5 work-groups per CU
-static const int64_t kK4Blocks = 192;
+static const int64_t kK4Blocks = 768;  // K-group LDS tiles: target work-groups
 static const int64_t kMinStagesPerSplit = 6;
 
 // Forced plans (nvfp4_force_plan; tuning sweeps and tests): per operation
@@ -1644,21 +1669,27 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
   const int64_t tiles = pl.tiles_m * pl.tiles_n;
   const int64_t nk = K / k.bk;
   int64_t s = 1;
-  if (k.splitk && tiles < kCUs) {
+  const bool kgroup_lds = k.ks > 1 && !k.kreg;
+  const bool can_split = k.splitk && (tiles < kCUs || (kgroup_lds && tiles < 2 * kCUs) ||
+                                      (forced > 1 && tiles <= kCounterBytes / 4));
+  if (can_split) {
     if (forced > 0) {
       s = forced;
     } else if (k.kreg) {
-      // register K-group tiles split K in two only while there are at most a
-      // quarter as many tiles as CUs (cold sweeps: 16 x 768 x 6144 gains
-      // ~0.3 us; 3 or 4 splits, or 2 on larger grids, lose), keeping at
-      // least one K unit per wave in every split
-      s = tiles * 4 <= kCUs ? 2 : 1;
+      // register K-group tiles split K in two while there are at most half
+      // as many tiles as CUs (cold sweeps at K = 6144: 32 x 768 7.2 us
+      // against 7.4 unsplit, 16 x 2048 7.4 against 7.6; 3 or 4 splits, or 2
+      // on larger grids, lose), keeping at least one K unit per wave per split
+      s = tiles * 2 <= kCUs ? 2 : 1;
       if (s > nk / k.ks) s = nk / k.ks;
-    } else if (k.ks > 1) {
-      // K-group tiles: about 192 work-groups (three quarters of the CUs, one
-      // work-group each) measured best; more splits cost more in the reduction
-      // than they gain in occupancy
-      s = (kK4Blocks + tiles / 2) / tiles;
+    } else if (kgroup_lds) {
+      // K-group LDS tiles: about three work-groups per CU, at most 5 splits
+      // (cold sweeps at K = 6144: 1024 x 768, 192 tiles, 19.7 us at 4 splits
+      // against 23.3 unsplit and 20.7 / 22.4 at 3 / 6; 512 x 768, 96 tiles,
+      // 14.2 us at 5 against 15.4 / 15.6 at 6 / 8; 256 x 768, 48 tiles, 12.4
+      // us at 5 against 13.1 at 8; 2048 x 768, 384 tiles, 28.5 against 29.3)
+      s = kK4Blocks / tiles;
+      if (s > 5) s = 5;
     } else if (k.mx) {
       // MX LDS tiles: at most one work-group per CU (192 tiles of 64x64 at
       // 1024 x 768 x 6144: 20.8 us unsplit against 25.4 us split in two)
@@ -1685,11 +1716,13 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
 }
 
 // Plan choice, from sweeps on MI355X of the pages' shapes (K = 6144,
-// N = 768 / 2048 / 6144; cold below M = 4096, warm above): up to M = 512,
+// N = 768 / 2048 / 6144; cold below M = 4096, warm above): up to M = 128,
 // the register-streamed K-group tile (4 waves per work-group), the smallest
 // of 16x16, 32x16, 32x32, 64x32 that needs at most one work-group per CU;
-// above that, 64x64 K-group tiles (split-K while there are fewer than 192 of
-// them) until 128x128 tiles fill the CUs three times, then 128x128 tiles,
+// above that, 64x64 K-group tiles split K about three work-groups per CU
+// (256 x 768: 12.4 us against 13.2 for the 32x32 register tile; 512 x 768:
+// 14.2 against 19.7 for the 64x32 one) until 128x128 tiles fill the CUs
+// three times, then 128x128 tiles,
 // and tiles of 8 waves, 256x256 or 256x192, once either fills the CUs twice
 // (all staging 256 K per stage: whole 128-byte lines per row).
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
@@ -1699,7 +1732,7 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
-  if (M <= 512) {
+  if (M <= 128) {
     static const int kreg_kinds[] = {10, 11, 12, 13};  // 16x16, 32x16, 32x32, 64x32
     for (int kk : kreg_kinds) {
       const PlanKind& k = kKinds[kk];
@@ -1735,7 +1768,7 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   pl.tiles_m = (M + k.bm - 1) / k.bm;
   pl.tiles_n = (N + k.bn - 1) / k.bn;
   pl.group_m = 8;
-  if (!k.splitk || pl.tiles_m * pl.tiles_n >= kCUs) forced_splits = 1;
+  if (!k.splitk || pl.tiles_m * pl.tiles_n > kCounterBytes / 4) forced_splits = 1;
   plan_splits(pl, k, K, forced_splits);
   return pl;
 }

@@ -71,7 +71,7 @@ size_t grouped_workspace(int64_t rows, int64_t N, int64_t K, int32_t E);
 // Scratch of nvfp4_gemm_noalloc: a fixed device array per GPU (this many
 // bytes), whose address is looked up, and whose counters are cleared on
 // `stream`, at the first call on each device.
-constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 constexpr int kMaxDevices = 64;
 hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 

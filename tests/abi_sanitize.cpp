@@ -47,7 +47,7 @@ int main() {
                 int st = fam ? nvfp4_mx_gemm(F, F, F, F, NULL, D, M, N, K, NULL, 0, NULL)
                              : nvfp4_gemm(F, F, F, F, NULL, D, M, N, K, NULL, 0, NULL);
                 expect(st, NVFP4_ERR_WORKSPACE, "gemm without workspace");
-                if (!fam && ws > (size_t(8) << 20))
+                if (!fam && ws > (size_t(16) << 20))
                   expect(nvfp4_gemm_noalloc(F, F, F, F, NULL, D, M, N, K, NULL), NVFP4_ERR_WORKSPACE,
                          "noalloc beyond its scratch");
               }

@@ -56,7 +56,7 @@ def test_gemm_error_paths():
     assert _gemm(bsf=FAKE + 4) == 3
     assert _gemm(d=FAKE + 2) == 3
     # a split-K plan (M = 1024, N = 256: 64 K-group tiles of 64x64 split in
-    # three) needs a workspace
+    # five) needs a workspace
     need = nv.nvfp4_gemm_workspace_size(1024, 256, 6144)
     assert need > 0
     assert _gemm(M=1024, N=256, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
@@ -102,16 +102,21 @@ def test_plan_and_workspace_queries():
     assert nv.nvfp4_gemm_workspace_size(64, 768, 6144) == 0  # 192 register tiles: no split, no workspace
     # 48 register tiles of 16x16 split K two ways: counters + fp32 partial tiles
     assert nv.nvfp4_gemm_workspace_size(16, 768, 6144) == 4096 + 48 * 2 * 16 * 16 * 4
-    assert nv.nvfp4_gemm_plan(256, 2048, 6144).startswith("kreg64x32")
-    assert nv.nvfp4_gemm_plan(512, 768, 6144).startswith("kreg64x32")
+    # above M = 128 the K-group tile, split about three work-groups per CU
+    assert nv.nvfp4_gemm_plan(256, 2048, 6144).startswith("tile64x64k4")
+    assert nv.nvfp4_gemm_plan(512, 768, 6144).startswith("tile64x64k4")
+    assert nv.nvfp4_gemm_workspace_size(512, 768, 6144) == 4096 + 96 * 5 * 64 * 64 * 4
+    assert nv.nvfp4_gemm_workspace_size(1024, 768, 6144) == 4096 + 192 * 4 * 64 * 64 * 4
     assert nv.nvfp4_gemm_plan(512, 2048, 6144).startswith("tile64x64k4")
-    assert nv.nvfp4_gemm_workspace_size(32, 768, 6144) == 0          # 96 tiles: no split
+    assert nv.nvfp4_gemm_workspace_size(1024, 2048, 6144) == 0        # 512 tiles: no split
+    # 96 register tiles of 16x16 split K two ways
+    assert nv.nvfp4_gemm_workspace_size(32, 768, 6144) == 4096 + 96 * 2 * 16 * 16 * 4
     assert nv.nvfp4_gemm_plan(16, 768, 100) == "none"
     assert nv.nvfp4_gemm_workspace_size(16384, 6144, 6144) == 0
     # split-K plans: a 4096-byte counter block, then fp32 partial tiles
     ws = nv.nvfp4_gemm_workspace_size(1024, 256, 6144)
     tiles = (1024 // 64) * (256 // 64)
-    assert ws == 4096 + tiles * 3 * 64 * 64 * 4
+    assert ws == 4096 + tiles * 5 * 64 * 64 * 4
 
 
 def test_packed_grouped_error_paths():
