@@ -1647,6 +1647,7 @@ static const int64_t kMaxPartialBytesPerTile = 256 * 1024;  // one CU reduces a 
 static const int64_t kTargetBlocks = 384;   // 1.5 work-groups per CU
 static const int64_t kK4Blocks = 768;  // K-group LDS tiles: target work-groups
 static const int64_t kMinStagesPerSplit = 6;
+static const int64_t kMxTargetBlocks = 576;  // MX LDS tiles: target work-groups
 
 // Forced plans (nvfp4_force_plan; tuning sweeps and tests): per operation
 // family, 0 = none, else (kind + 1) | splits << 16, one word so that kind and
@@ -1691,9 +1692,11 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
       s = kK4Blocks / tiles;
       if (s > 5) s = 5;
     } else if (k.mx) {
-      // MX LDS tiles: at most one work-group per CU (192 tiles of 64x64 at
-      // 1024 x 768 x 6144: 20.8 us unsplit against 25.4 us split in two)
-      s = tiles * 2 <= kCUs ? kCUs / tiles : 1;
+      // MX LDS tiles: about two work-groups per CU, at least 6 stages per
+      // split (cold sweeps at K = 6144: 1024 x 768, 192 tiles of 64x64, 16.6
+      // us at 3 splits against 20.7 unsplit; 512 x 768, 96 tiles, 12.6 at 4
+      // against 15.3 at 2; 256 x 2048, 128 tiles, 14.8 at 4)
+      s = kMxTargetBlocks / tiles;
       if (s > nk / kMinStagesPerSplit) s = nk / kMinStagesPerSplit;
     } else {
       s = (kTargetBlocks + tiles - 1) / tiles;
@@ -1822,8 +1825,11 @@ GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   int kind = -1, forced_splits = 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (M <= 512) {
-    for (int kk = 5; kk <= 8; ++kk) {  // register tiles 16x16, 32x16, 32x32, 64x32
+  if (M <= 128) {
+    // register tiles 16x16, 32x16, 32x32, 64x32; above M = 128 the split
+    // 64x64 LDS tile is faster (512 x 768 x 6144: 12.6 us against 17.1 for
+    // the 64x32 register tile; 256 x 768: 11.3 against 12.0 for 32x32)
+    for (int kk = 5; kk <= 8; ++kk) {
       const PlanKind& k = kMxKinds[kk];
       if (((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) <= kCUs) {
         kind = kk;

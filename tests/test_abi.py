@@ -159,14 +159,15 @@ def test_mx_gemm_error_paths_and_queries():
     assert nv.nvfp4_mx_gemm_plan(16, 768, 100) == "none"
     assert nv.nvfp4_mx_gemm_plan(16384, 6144, 6144).startswith("mx256x256w8")
     assert nv.nvfp4_mx_gemm_plan(16, 768, 6144).startswith("mxreg16x16")
-    assert nv.nvfp4_mx_gemm_plan(512, 768, 6144).startswith("mxreg64x32")
+    assert nv.nvfp4_mx_gemm_plan(512, 768, 6144).startswith("mx64x64")
     assert nv.nvfp4_mx_gemm_plan(1024, 768, 6144).startswith("mx64x64")
     # 48 register tiles of 16x16 split K in two; 64 LDS tiles of 64x64 (M = 1024,
     # N = 256) split in four; 192 of them not at all
     assert nv.nvfp4_mx_gemm_workspace_size(16, 768, 6144) == 4096 + 48 * 2 * 16 * 16 * 4
     assert nv.nvfp4_mx_gemm_workspace_size(64, 768, 6144) == 0
     assert nv.nvfp4_mx_gemm_workspace_size(1024, 256, 6144) == 4096 + 64 * 4 * 64 * 64 * 4
-    assert nv.nvfp4_mx_gemm_workspace_size(1024, 768, 6144) == 0
+    # 192 tiles of 64x64 split K three ways (about two work-groups per CU)
+    assert nv.nvfp4_mx_gemm_workspace_size(1024, 768, 6144) == 4096 + 192 * 3 * 64 * 64 * 4
     assert call(M=16, N=768, K=6144) == 5 and "workspace" in nv.nvfp4_last_error()
     assert nv.nvfp4_mx_gemm_workspace_size(16384, 6144, 6144) == 0
 
