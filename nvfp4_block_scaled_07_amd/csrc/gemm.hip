@@ -1752,6 +1752,11 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
     const int64_t r256 = (t256 + kCUs - 1) / kCUs, r192 = (t192 + kCUs - 1) / kCUs;
     if (r192 * 192 * 105 < r256 * 256 * 100) kind = 16;
     else if (t256 >= 2 * kCUs) kind = 14;
+  } else if (kind < 0 && M > 64 && t192 % kCUs == 0 && t192 > 0) {
+    // exactly one round of 256x192 tiles (2048 x 6144 x 6144: 142 us against
+    // 155 for 128x128 tiles; at 1.5 rounds, 3072 x 6144, the 128x128 tiles
+    // win: 237 us against 257)
+    kind = 16;
   }
   if (kind < 0) {
     if (M <= 32) kind = 3;
