@@ -37,6 +37,7 @@ PEAK_F16_TFLOPS = 2500.0      # dense f16 MFMA, MI355X: the instruction the exac
 PEAK_HBM_GBPS = 8000.0
 ROTATE_BYTES = 600 << 20      # > 2 x 256 MB Infinity Cache
 GRAPH_STEPS = 8               # steps captured per HIP graph
+RAMP_S = 0.25                 # untimed clock ramp before the warmup steps (seconds)
 
 # the step: (workload, the M values it contributes)
 STEP = (("attn_proj_n768_k6144", (16, 32, 64, 128, 256, 512, 1024)),
@@ -70,6 +71,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--ramp-seconds", type=float, default=RAMP_S,
+                    help="untimed step replays before the warmup steps: the GPU clocks ramp up under sustained load")
     ap.add_argument("--workload", default="attn_proj_n768_k6144", help="workload of --profile-call")
     ap.add_argument("--profile-call", type=int, default=0, metavar="M",
                     help="for hardware-counter runs: one 256 MiB device copy (counter calibration), then 8 "
@@ -201,6 +204,13 @@ def main():
             single[(first + i) % G].replay()
             i += 1
 
+    # clock ramp: untimed replays of the step graphs for ramp_seconds (as the
+    # per-shape timings below replay for at least 50 ms before timing), then
+    # the warmup steps, then exactly `steps` timed steps
+    t_ramp = time.perf_counter()
+    while time.perf_counter() - t_ramp < args.ramp_seconds:
+        run_steps(G, 0)
+        torch.cuda.synchronize()
     run_steps(args.warmup, 0)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -256,7 +266,8 @@ def main():
     torch.cuda.empty_cache()
 
     out = dict(metric=METRIC, value=round(value, 3), unit="TFLOPS", n_gpus=1, steps=args.steps,
-               warmup=args.warmup, ms_per_step=round(ms_per_step, 5), gpu_ms_per_step=round(gpu_ms / args.steps, 5),
+               warmup=args.warmup, clock_ramp_s=args.ramp_seconds, ms_per_step=round(ms_per_step, 5),
+               gpu_ms_per_step=round(gpu_ms / args.steps, 5),
                higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="f16", data="synthetic",
                config=dict(workload="nvfp4_gemm over M=16..8192: attn_proj_n768_k6144 (M 16..1024 x 768 x 6144) + "
