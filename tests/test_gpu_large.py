@@ -1,9 +1,12 @@
-"""Full-output GPU parity of the large compute-bound GEMMs (M = 4096, 8192,
-16384 x N = 6144 x K = 6144), NVFP4 and MXFP4, through the C ABI.
+"""Full-output GPU parity of the large compute-bound GEMMs (M = 2048, 4096,
+8192, 16384 x N = 6144 x K = 6144), NVFP4 and MXFP4, through the C ABI.  The
+four M values take four different automatic plans on each path (NVFP4: one
+round of 256x192 tiles, two rounds of them, 256x256 tiles; MXFP4: 256x256 tiles
+at three quarters of a round, 256x192, 256x256).
 
 Every element of every output is compared with the oracle: the oracle runs
 on row blocks in a pool of CPU processes (rows of a GEMM are independent), and
-the three M values share one oracle evaluation because the workload's sweep is
+the M values share one oracle evaluation because the workload's sweep is
 nested (A is drawn at M = 16384 and the smaller M take its first rows)."""
 import numpy as np
 import pytest
@@ -17,7 +20,7 @@ from tests.gpu_util import bits, dev, gpu_global_scale, gpu_quantize, host, say
 
 pytestmark = pytest.mark.gpu
 
-MS = (4096, 8192, 16384)
+MS = (2048, 4096, 8192, 16384)
 N = K = 6144
 BLOCK = 1024
 
