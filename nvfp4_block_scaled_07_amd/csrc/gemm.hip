@@ -305,50 +305,73 @@ __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // l / 32 of the sub-step (one 16-byte chunk, low nibble first, exactly the
 // stored layout) and that block's E8M0 scale in the low byte of its scale
 // operand; the hardware applies both scales and accumulates in fp32.
+// The operands of sub-step ss + 1 are read from LDS while the MFMAs of
+// sub-step ss run (two register slots): with no dequantisation between the
+// reads and the MFMAs, the read latency is otherwise as long as a
+// sub-step's MFMAs.
+template <class C>
+struct MxFrags {
+  u4_t ac[C::TM], bc[C::TN];
+  uint32_t asw[C::TM], bsw[C::TN];
+};
+
+template <class C>
+__device__ __forceinline__ void mx_read(MxFrags<C>& f, const Smem<C>& sm, int buf, int ss, int wm, int wn, int r_in,
+                                        int g, int kgrp) {
+  const uint32_t a_base = lds_addr(sm.a[buf]), b_base = lds_addr(sm.b[buf]);
+  const uint32_t as_base = lds_addr(sm.asf[buf]), bs_base = lds_addr(sm.bsf[buf]);
+  const int c = C::KG * (ss * C::KS + kgrp) + g;  // chunk = MX block of this lane in the stage
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm) {
+    const int row = wm * C::kWM + tm * 32 + r_in;
+    ds_read128(f.ac[tm], a_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
+    ds_read32(f.asw[tm], as_base + row * C::SB + 4 * (c >> 2));
+  }
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const int row = wn * C::kWN + tn * 32 + r_in;
+    ds_read128(f.bc[tn], b_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
+    ds_read32(f.bsw[tn], bs_base + row * C::SB + 4 * (c >> 2));
+  }
+}
+
 template <class C>
 __device__ __forceinline__ void compute_stage_mx(const Smem<C>& sm, int buf, typename C::Acc (&acc)[C::TM][C::TN]) {
   typedef int v8i_t __attribute__((ext_vector_type(8)));
+  constexpr int NS = C::kSub / C::KS;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
   const int wm = gw / C::WN, wn = gw % C::WN;
   const int r_in = lane % 32, g = lane / 32;
-  const uint32_t a_base = lds_addr(sm.a[buf]), b_base = lds_addr(sm.b[buf]);
-  const uint32_t as_base = lds_addr(sm.asf[buf]), bs_base = lds_addr(sm.bsf[buf]);
+  MxFrags<C> f[2];
+  mx_read<C>(f[0], sm, buf, 0, wm, wn, r_in, g, kgrp);
 #pragma unroll
-  for (int ss = 0; ss < C::kSub / C::KS; ++ss) {
-    const int s = ss * C::KS + kgrp;
-    const int c = C::KG * s + g;  // chunk = MX block of this lane in the stage
-    u4_t ac[C::TM], bc[C::TN];
-    uint32_t asw[C::TM], bsw[C::TN];
+  for (int ss = 0; ss < NS; ++ss) {
+    MxFrags<C>& cur = f[ss & 1];
+    lgkm_wait();  // slot ss & 1 has landed (nothing else is in flight)
 #pragma unroll
     for (int tm = 0; tm < C::TM; ++tm) {
-      const int row = wm * C::kWM + tm * 32 + r_in;
-      ds_read128(ac[tm], a_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
-      ds_read32(asw[tm], as_base + row * C::SB + 4 * (c >> 2));
+      pin(cur.ac[tm]);
+      pin(cur.asw[tm]);
     }
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
-      const int row = wn * C::kWN + tn * 32 + r_in;
-      ds_read128(bc[tn], b_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
-      ds_read32(bsw[tn], bs_base + row * C::SB + 4 * (c >> 2));
+      pin(cur.bc[tn]);
+      pin(cur.bsw[tn]);
     }
-    lgkm_wait();
-    const int sh = 8 * (c & 3);
+    if (ss + 1 < NS) mx_read<C>(f[(ss + 1) & 1], sm, buf, ss + 1, wm, wn, r_in, g, kgrp);
+    const int sh = 8 * ((C::KG * (ss * C::KS + kgrp) + g) & 3);
     v8i_t av[C::TM], bv[C::TN];
     int sa[C::TM], sb[C::TN];
 #pragma unroll
     for (int tm = 0; tm < C::TM; ++tm) {
-      pin(ac[tm]);
-      pin(asw[tm]);
-      av[tm] = v8i_t{(int)ac[tm][0], (int)ac[tm][1], (int)ac[tm][2], (int)ac[tm][3], 0, 0, 0, 0};
-      sa[tm] = (int)(asw[tm] >> sh);
+      av[tm] = v8i_t{(int)cur.ac[tm][0], (int)cur.ac[tm][1], (int)cur.ac[tm][2], (int)cur.ac[tm][3], 0, 0, 0, 0};
+      sa[tm] = (int)(cur.asw[tm] >> sh);
     }
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
-      pin(bc[tn]);
-      pin(bsw[tn]);
-      bv[tn] = v8i_t{(int)bc[tn][0], (int)bc[tn][1], (int)bc[tn][2], (int)bc[tn][3], 0, 0, 0, 0};
-      sb[tn] = (int)(bsw[tn] >> sh);
+      bv[tn] = v8i_t{(int)cur.bc[tn][0], (int)cur.bc[tn][1], (int)cur.bc[tn][2], (int)cur.bc[tn][3], 0, 0, 0, 0};
+      sb[tn] = (int)(cur.bsw[tn] >> sh);
     }
 #pragma unroll
     for (int tm = 0; tm < C::TM; ++tm)
