@@ -31,8 +31,9 @@
 //  * Split-K: each split writes its fp32 partial tile to the workspace in the
 //    accumulators' register order; the last split of a tile to arrive
 //    (device-scope counter) sums the partials in split order, applies alpha
-//    and stores bf16, then resets the counter.  One launch, bitwise
-//    deterministic.
+//    and stores bf16, then resets the counter.  Partials and counters are
+//    accessed only with agent-coherent operations, so no cache-wide fence
+//    is needed.  One launch, bitwise deterministic.
 //  * Register streaming: small-M tiles (k_gemm_kreg) and the grouped MoE
 //    kernels (k_grouped_reg) load operands straight into VGPRs in whole
 //    128-byte lines per row, two or three 256-element K units ahead, and put
