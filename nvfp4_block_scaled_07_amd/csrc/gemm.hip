@@ -1760,7 +1760,10 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
   if (M <= 128) {
-    static const int kreg_kinds[] = {10, 11, 12, 13};  // 16x16, 32x16, 32x32, 64x32
+    // 16x16, 32x16, 32x32; the 64x32 register tile (13) lost to the split
+    // 64x64 K-group tile wherever it was the first fit (64 x 6144 x 6144:
+    // 20.0 us against 16.6; 64 x 8192: 20.2 against 19.6)
+    static const int kreg_kinds[] = {10, 11, 12};
     for (int kk : kreg_kinds) {
       const PlanKind& k = kKinds[kk];
       if (((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) <= kCUs) {
@@ -1768,6 +1771,10 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
         break;
       }
     }
+    // wide weights at M <= 32: 32x32 register tiles, up to four work-groups
+    // per CU, unsplit (16 x 16384 x 6144: 21.1 us against 28.2 for the
+    // skinny LDS tile; 32 x 16384: 23.8 against 35.4)
+    if (kind < 0 && M <= 32 && ((N + 31) / 32) <= 4 * kCUs) kind = 12;
   }
   if (kind < 0 && M > 64 && (t256 >= 2 * kCUs || t192 >= 2 * kCUs)) {
     // 256x256 or 256x192 tiles, one work-group per CU: the 192-column tile
@@ -1783,9 +1790,10 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
     kind = 16;
   }
   if (kind < 0) {
-    if (M <= 32) kind = 3;
-    else if (M <= 64) kind = 4;
-    else if (t128 >= 3 * kCUs) kind = 15;
+    // (the skinny split-K LDS tiles, kinds 3 and 4, lost to these at every
+    // M <= 64 measured: 64 x 16384 x 6144 on the split 64x64 K-group tile
+    // 26.8 us against 44.2)
+    if (t128 >= 3 * kCUs && M > 64) kind = 15;
     else kind = 9;
   }
   // a plan forced by nvfp4_force_plan (tuning sweeps and tests only)
