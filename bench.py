@@ -556,6 +556,17 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
     del sets, outs, wss
     torch.cuda.empty_cache()
 
+    # decode rows against a 16384 x 6144 weight (56.6 MB: the weight stream
+    # at M <= 64 without the launch floor dominating; cold, rotating sets)
+    w, sets, alpha, outs, wss = sweep_inputs("decode_wide_n16384_k6144")
+    rows = []
+    for m in w["ms"]:
+        us = timed(torch, stream, lambda i: call(w, sets[i % len(sets)], alpha, outs, wss, m), 2 * len(sets))
+        rows.append(shape_row(nv, m, w["n"], w["k"], us))
+    res["decode_wide_n16384_k6144"] = dict(cache="cold (rotating sets)", shapes=rows)
+    del sets, outs, wss
+    torch.cuda.empty_cache()
+
     # grouped MoE: 512 tokens, top-8 of 256 experts, [rows_e, 6144] x [6144, 2048] per expert
     gi = grouped_inputs(torch, nv, synth, quantise, dev)
     rows, N, K, E = gi["rows"], gi["N"], gi["K"], gi["E"]

@@ -37,6 +37,12 @@ WORKLOADS = {
     "large_n6144_k6144": dict(ms=(4096, 8192, 16384), n=K_HIDDEN, k=K_HIDDEN,
                               seed_a=4001, seed_b=4002, sigma_a=1.0, sigma_b=0.02,
                               unit_global_scale=False),
+    # decode rows against a weight large enough to stream from HBM (56.6 MB of
+    # codes and scales): not one of the pages' shapes; it shows the weight
+    # stream of the single GEMM at M <= 64 without the launch floor dominating
+    "decode_wide_n16384_k6144": dict(ms=(16, 32, 64), n=16384, k=K_HIDDEN,
+                                     seed_a=6001, seed_b=6002, sigma_a=1.0, sigma_b=0.02,
+                                     unit_global_scale=False),
 }
 
 GROUPED = dict(tokens=512, experts=NUM_EXPERTS, top_k=TOP_K, n=N_EXPERT, k=K_HIDDEN,

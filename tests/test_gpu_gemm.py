@@ -85,7 +85,7 @@ def test_random_bytes_like_the_page_smoke_test():
     assert st["n"] == M * N
 
 
-@pytest.mark.parametrize("name", ["attn_proj_n768_k6144", "moe_expert_n2048_k6144"])
+@pytest.mark.parametrize("name", ["attn_proj_n768_k6144", "moe_expert_n2048_k6144", "decode_wide_n16384_k6144"])
 def test_decode_and_prefill_sweeps(name):
     w = synth.WORKLOADS[name]
     ref, gpu = _quantized_workload(name)
