@@ -98,7 +98,13 @@ def test_decode_and_prefill_sweeps(name):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 129, 512), (100, 200, 768), (65, 96, 256),
-                                   (129, 130, 1024), (33, 5, 2048), (300, 1000, 256)])
+                                   (129, 130, 1024), (33, 5, 2048), (300, 1000, 256),
+                                   # automatic split plans on ragged tiles whose K stages do not
+                                   # divide evenly over the splits (K-group tile split five ways
+                                   # over 10 and 25 stages; register tiles split two ways)
+                                   (300, 500, 2560), (130, 1000, 6400), (20, 900, 2048),
+                                   # wide weights at decode M (32x32 register tiles, unsplit)
+                                   (24, 9000, 512)])
 def test_ragged_shapes(M, N, K):
     a, b = synth.random_codes(M * 7 + 1, M, K), synth.random_codes(N * 7 + 2, N, K)
     asf = synth.random_scale_bytes(M + 3, M, K, lo=0x28, hi=0x48, signed=True)
