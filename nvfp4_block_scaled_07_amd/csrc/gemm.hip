@@ -1629,6 +1629,7 @@ struct PlanKind {
   bool kreg;  // register-streamed K-group kernel
   bool mx;    // MXFP4 tile
   int ks;     // K-groups (waves) of a register-streamed or K-group LDS tile
+  int d;      // register-streamed tiles: K units in flight per wave
 };
 static const PlanKind kKinds[] = {
     {"tile256x256_mfma32", 256, 256, 128, false},
@@ -1641,10 +1642,10 @@ static const PlanKind kKinds[] = {
     {"tile256x256il_mfma32", 256, 256, 128, false},
     {"tile128x128il_mfma32", 128, 128, 128, true},
     {"tile64x64k4_mfma32", 64, 64, 256, true, false, false, 4},
-    {"kreg16x16_mfma16", 16, 16, 256, true, true, false, KReg16x16::KS},
-    {"kreg32x16_mfma16", 32, 16, 256, true, true, false, KReg32x16::KS},
-    {"kreg32x32_mfma16", 32, 32, 256, true, true, false, KReg32x32::KS},
-    {"kreg64x32_mfma16", 64, 32, 256, true, true, false, KReg64x32::KS},
+    {"kreg16x16_mfma16", 16, 16, 256, true, true, false, KReg16x16::KS, KReg16x16::D},
+    {"kreg32x16_mfma16", 32, 16, 256, true, true, false, KReg32x16::KS, KReg32x16::D},
+    {"kreg32x32_mfma16", 32, 32, 256, true, true, false, KReg32x32::KS, KReg32x32::D},
+    {"kreg64x32_mfma16", 64, 32, 256, true, true, false, KReg64x32::KS, KReg64x32::D},
     {"tile256x256w8k256_mfma32", 256, 256, 256, false},
     {"tile128x128k256_mfma32", 128, 128, 256, true},
     {"tile256x192w8k256_mfma32", 256, 192, 256, false},
@@ -1655,10 +1656,10 @@ static const PlanKind kMxKinds[] = {
     {"mx64x64_fp4mfma", 64, 64, 256, true, false, true},
     {"mx256x256w8_fp4mfma", 256, 256, 256, false, false, true},
     {"mx256x256w8s4_fp4mfma", 256, 256, 128, false, false, true},
-    {"mxreg16x16_fp4mfma", 16, 16, 256, true, true, true, MxReg16x16::KS},
-    {"mxreg32x16_fp4mfma", 32, 16, 256, true, true, true, MxReg32x16::KS},
-    {"mxreg32x32_fp4mfma", 32, 32, 256, true, true, true, MxReg32x32::KS},
-    {"mxreg64x32_fp4mfma", 64, 32, 256, true, true, true, MxReg64x32::KS},
+    {"mxreg16x16_fp4mfma", 16, 16, 256, true, true, true, MxReg16x16::KS, MxReg16x16::D},
+    {"mxreg32x16_fp4mfma", 32, 16, 256, true, true, true, MxReg32x16::KS, MxReg32x16::D},
+    {"mxreg32x32_fp4mfma", 32, 32, 256, true, true, true, MxReg32x32::KS, MxReg32x32::D},
+    {"mxreg64x32_fp4mfma", 64, 32, 256, true, true, true, MxReg64x32::KS, MxReg64x32::D},
     {"mx256x192w8_fp4mfma", 256, 192, 256, false, false, true},
 };
 static constexpr int kNumMxKinds = (int)(sizeof(kMxKinds) / sizeof(kMxKinds[0]));
@@ -1701,12 +1702,17 @@ static void plan_splits(GemmPlan& pl, const PlanKind& k, int64_t K, int forced) 
     if (forced > 0) {
       s = forced;
     } else if (k.kreg) {
-      // register K-group tiles split K in two while there are at most half
-      // as many tiles as CUs (cold sweeps at K = 6144: 32 x 768 7.2 us
-      // against 7.4 unsplit, 16 x 2048 7.4 against 7.6; 3 or 4 splits, or 2
-      // on larger grids, lose), keeping at least one K unit per wave per split
-      s = tiles * 2 <= kCUs ? 2 : 1;
-      if (s > nk / k.ks) s = nk / k.ks;
+      // register K-group tiles: the fewest splits that let every wave hold
+      // all its K units in flight at once (one memory round trip, ks * d
+      // units per work-group), at most one work-group per CU.  Each further
+      // round trip costs about 2 us on cold operands and a split exchange
+      // about 1.4 (cold sweeps, 16 x 768: K = 2048 4.7 us unsplit against 6.2
+      // split in two; K = 6144 7.0 split in two against 7.4 unsplit and 7.3
+      // in three; K = 12288 8.1 in four against 9.1 in two and 11.5 unsplit;
+      // 16 x 2048 x 12288, 128 tiles: 9.3 in two against 10.3 in four)
+      const int64_t per_wg = (int64_t)k.ks * k.d;
+      s = (nk + per_wg - 1) / per_wg;
+      while (s > 1 && tiles * s > kCUs) --s;
     } else if (kgroup_lds) {
       // K-group LDS tiles: about three work-groups per CU, at most 5 splits
       // (cold sweeps at K = 6144: 1024 x 768, 192 tiles, 19.7 us at 4 splits
