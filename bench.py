@@ -292,15 +292,17 @@ COPY_BYTES = 256 << 20
 
 
 def kernel_sources_digest():
-    """sha256 over the library's kernel sources: a traffic record only holds
-    for the kernels it was measured on."""
+    """sha256 over the library's kernel sources and its build script (which
+    holds the compiler flags): a traffic record only holds for the kernels it
+    was measured on."""
     import hashlib
     h = hashlib.sha256()
-    src = os.path.join(ROOT, "nvfp4_block_scaled_07_amd", "csrc")
-    for f in sorted(os.listdir(src)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(src, f), "rb").read())
+    pkg = os.path.join(ROOT, "nvfp4_block_scaled_07_amd")
+    src = os.path.join(pkg, "csrc")
+    files = [os.path.join(src, f) for f in sorted(os.listdir(src)) if f.endswith((".hip", ".h"))]
+    for path in files + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(path).encode())
+        h.update(open(path, "rb").read())
     return h.hexdigest()[:16]
 
 

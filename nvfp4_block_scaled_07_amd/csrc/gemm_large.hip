@@ -1,0 +1,23 @@
+// The two unsplit large-M NVFP4 tiles (plan kinds 14 and 16), built in a
+// source of their own so that they can take another instruction schedule
+// than the rest of the library: the build compiles this file with the
+// iterative ILP scheduler, which keeps more dequantisation work between the
+// MFMAs of these 8-wave tiles (8192 x 6144 x 6144 on the 256x256 tile:
+// about 3.5% faster; the same schedule doubles the time of the split 64x64
+// K-group tile, so it is not applied library-wide).  Results are bitwise the
+// same: the schedule reorders independent instructions only.
+#include "gemm_tile.h"
+
+namespace nvfp4 {
+
+typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2> CfgTile256w8k256;  // 8 waves of 128x64
+typedef Cfg<256, 192, 4, 2, 32, 256, 2, 0, 1, 2> CfgTile256x192;    // 8 waves of 64x96, 126 KB LDS
+
+void launch_large_tile(int kind, const GemmLaunch& p, unsigned grid, hipStream_t stream) {
+  if (kind == 14)
+    hipLaunchKernelGGL((k_gemm<CfgTile256w8k256, false>), dim3(grid), dim3(CfgTile256w8k256::kThreads), 0, stream, p);
+  else if (kind == 16)
+    hipLaunchKernelGGL((k_gemm<CfgTile256x192, false>), dim3(grid), dim3(CfgTile256x192::kThreads), 0, stream, p);
+}
+
+}  // namespace nvfp4

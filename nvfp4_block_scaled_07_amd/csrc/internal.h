@@ -54,6 +54,10 @@ void set_forced_plan(int family, int kind, int splits);
 
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
+// The unsplit 256x256 (plan kind 14) and 256x192 (kind 16) NVFP4 tiles, built
+// in their own source with another instruction schedule; p carries the plan's
+// tile counts, grid = their product.
+void launch_large_tile(int kind, const GemmLaunch& p, unsigned grid, hipStream_t stream);
 // MXFP4 (E8M0 scales per 32 elements): GemmLaunch with a_sf / b_sf of K/32 bytes per row.
 GemmPlan choose_mx_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mx_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);

@@ -33,7 +33,7 @@ def test_host_layer_under_address_and_undefined_behaviour_sanitizers(tmp_path):
         pytest.skip("the ROCm compilers are not installed")
     objs = []
     cmds = []
-    for f in ("api", "gemm", "layout", "moe", "quantize"):
+    for f in ("api", "gemm", "gemm_large", "layout", "moe", "quantize"):
         o = str(tmp_path / f"{f}.o")
         objs.append(o)
         cmds.append([HIPCC, "--offload-arch=gfx950", "-std=c++17", "-O2", "-g",
