@@ -11,12 +11,23 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
 namespace nvfp4 {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// f(std::integral_constant<int, I>) for I = 0 .. N - 1
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 // Split-K workspace: int32 arrival counters for up to 1024 tiles, then the
 // fp32 partial tiles.
@@ -254,6 +265,19 @@ __device__ __forceinline__ h2_t scale_pair(h2_t sp, int hi) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
 __device__ __forceinline__ void ds_read128(u4_t& v, uint32_t a) { asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a)); }
 __device__ __forceinline__ void ds_read32(uint32_t& v, uint32_t a) { asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(a)); }
+// The same with a compile-time byte offset, carried in the instruction's
+// 16-bit offset field when it fits.
+template <int OFF>
+__device__ __forceinline__ void ds_read128_at(u4_t& v, uint32_t a) {
+  if constexpr (OFF < 65536) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
+  else ds_read128(v, a + OFF);
+}
+// 16 bits, zero-extended
+template <int OFF>
+__device__ __forceinline__ void ds_read_u16_at(uint32_t& v, uint32_t a) {
+  if constexpr (OFF < 65536) asm volatile("ds_read_u16 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
+  else asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(a + OFF));
+}
 __device__ __forceinline__ void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void pin(u4_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
@@ -344,40 +368,71 @@ __device__ __forceinline__ void compute_stage_mx(const Smem<C>& sm, int buf, typ
   }
 }
 
+// Per-lane LDS read addresses of a dequantising tile, computed once per tile
+// (stage buffer 0, first row block): the code chunk of each sub-step of this
+// lane's K-group and the scale pair of its first sub-step.  Stage buffers, row
+// blocks and later sub-steps' scales are compile-time offsets from these.
 template <class C>
-__device__ __forceinline__ void compute_stage(const Smem<C>& sm, int buf, int tm_active,
-                                              typename C::Acc (&acc)[C::TM][C::TN]) {
-  if constexpr (C::kMx) {
-    compute_stage_mx<C>(sm, buf, acc);
-    return;
-  }
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = wave_id();
+struct ReadAddr {
+  static constexpr int kS = C::kSub / C::KS;  // sub-steps of one K-group per stage
+  uint32_t a[kS], b[kS];
+  uint32_t as, bs;
+};
+
+template <class C>
+__device__ __forceinline__ ReadAddr<C> read_addr(const Smem<C>& sm) {
+  ReadAddr<C> ra;
+  if constexpr (C::kMx) return ra;  // the scaled-FP4 stage computes its own
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
   const int wm = gw / C::WN, wn = gw % C::WN;
   const int r_in = lane % C::MF, g = lane / C::MF;
-  const uint32_t a_base = lds_addr(sm.a[buf]), b_base = lds_addr(sm.b[buf]);
-  const uint32_t as_base = lds_addr(sm.asf[buf]), bs_base = lds_addr(sm.bsf[buf]);
+  const int ra_row = wm * C::kWM + r_in, rb_row = wn * C::kWN + r_in;
+  // the swizzle depends on the row's low bits only, which row blocks keep
+  static_assert(C::kWM % swz_period<C::CH, C::MF>() == 0 && C::kWN % swz_period<C::CH, C::MF>() == 0 &&
+                    C::MF % swz_period<C::CH, C::MF>() == 0, "swizzle must not depend on the row block");
 #pragma unroll
-  for (int ss = 0; ss < C::kSub / C::KS; ++ss) {
-    const int s = ss * C::KS + kgrp;
-    const int c = C::KG * s + g;  // chunk of this lane: K offset 32c in the stage
+  for (int ss = 0; ss < ReadAddr<C>::kS; ++ss) {
+    const int c = C::KG * (ss * C::KS + kgrp) + g;
+    ra.a[ss] = lds_addr(sm.a[0]) + ra_row * C::RB + ((c ^ swz<C::CH, C::MF>(ra_row)) << 4);
+    ra.b[ss] = lds_addr(sm.b[0]) + rb_row * C::RB + ((c ^ swz<C::CH, C::MF>(rb_row)) << 4);
+    pin(ra.a[ss]);
+    pin(ra.b[ss]);
+  }
+  // the two scale bytes of chunk c (blocks 2c and 2c + 1) are at byte 2c
+  const int c0 = C::KG * kgrp + g;
+  ra.as = lds_addr(sm.asf[0]) + ra_row * C::SB + 2 * c0;
+  ra.bs = lds_addr(sm.bsf[0]) + rb_row * C::SB + 2 * c0;
+  pin(ra.as);
+  pin(ra.bs);
+  return ra;
+}
+
+// Multiply-accumulate one LDS stage (buffer BUF) into acc.
+template <class C, int BUF>
+__device__ __forceinline__ void compute_stage(const Smem<C>& sm, const ReadAddr<C>& ra, int tm_active,
+                                              typename C::Acc (&acc)[C::TM][C::TN]) {
+  if constexpr (C::kMx) {
+    compute_stage_mx<C>(sm, BUF, acc);
+    return;
+  }
+  constexpr int kScaleStep = 2 * C::KG * C::KS;  // scale bytes between a K-group's sub-steps
+#pragma unroll
+  for (int ss = 0; ss < ReadAddr<C>::kS; ++ss) {
     u4_t ac[C::TM], bc[C::TN];
     uint32_t asw[C::TM], bsw[C::TN];
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm) {
+    static_for<C::TM>([&](auto tmc) {
+      constexpr int tm = decltype(tmc)::value;
       if (tm < tm_active) {
-        const int row = wm * C::kWM + tm * C::MF + r_in;
-        ds_read128(ac[tm], a_base + row * C::RB + ((c ^ swz<C::CH, C::MF>(row)) << 4));
-        ds_read32(asw[tm], as_base + row * C::SB + 4 * (c >> 1));
+        ds_read128_at<BUF * C::BM * C::RB + tm * C::MF * C::RB>(ac[tm], ra.a[ss]);
+        ds_read_u16_at<BUF * C::BM * C::SB + tm * C::MF * C::SB>(asw[tm], ra.as + ss * kScaleStep);
       }
-    }
-#pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-      const int row = wn * C::kWN + tn * C::MF + r_in;
-      ds_read128(bc[tn], b_base + row * C::RB + ((c ^ swz<C::CH, C::MF>(row)) << 4));
-      ds_read32(bsw[tn], bs_base + row * C::SB + 4 * (c >> 1));
-    }
+    });
+    static_for<C::TN>([&](auto tnc) {
+      constexpr int tn = decltype(tnc)::value;
+      ds_read128_at<BUF * C::BN * C::RB + tn * C::MF * C::RB>(bc[tn], ra.b[ss]);
+      ds_read_u16_at<BUF * C::BN * C::SB + tn * C::MF * C::SB>(bsw[tn], ra.bs + ss * kScaleStep);
+    });
     lgkm_wait();
     h2_t asp[C::TM], bsp[C::TN];
 #pragma unroll
@@ -385,14 +440,14 @@ __device__ __forceinline__ void compute_stage(const Smem<C>& sm, int buf, int tm
       if (tm < tm_active) {
         pin(ac[tm]);
         pin(asw[tm]);
-        asp[tm] = e4m3x2_to_h2(asw[tm] >> (16 * (c & 1)));
+        asp[tm] = e4m3x2_to_h2(asw[tm]);
       }
     }
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
       pin(bc[tn]);
       pin(bsw[tn]);
-      bsp[tn] = e4m3x2_to_h2(bsw[tn] >> (16 * (c & 1)));
+      bsp[tn] = e4m3x2_to_h2(bsw[tn]);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -431,6 +486,23 @@ __device__ __forceinline__ void zero_acc(typename C::Acc (&acc)[C::TM][C::TN]) {
 // K-tiles [kt0, kt1) of the tile into acc (which is zeroed first).  Loads run
 // STAGES - 1 stages ahead of the MFMAs; each wait only drains the stage needed
 // next, so the later stages stay in flight across the barrier.
+// Stages i0 + J, i0 + J + 1, ... (J < STAGES) of the main loop: issue the DMA
+// of the stage STAGES - 1 ahead, compute this one, wait for the next.
+template <class C, int J>
+__device__ __forceinline__ void stage_steps(Smem<C>& sm, const ReadAddr<C>& ra, const Operand& A, const Operand& B,
+                                            int i0, int n, int kt0, int wave, int lane, int a_rows_dma,
+                                            int tm_active, typename C::Acc (&acc)[C::TM][C::TN]) {
+  if constexpr (J < C::STAGES) {
+    const int i = i0 + J;
+    if (i >= n) return;
+    const int pre = i + C::STAGES - 1;
+    if (pre < n) issue_stage<C>(sm, (J + C::STAGES - 1) % C::STAGES, A, B, kt0 + pre, wave, lane, a_rows_dma);
+    compute_stage<C, J>(sm, ra, tm_active, acc);
+    if (i + 1 < n) stage_ready<C>(min(C::STAGES - 2, n - 2 - i));
+    stage_steps<C, J + 1>(sm, ra, A, B, i0, n, kt0, wave, lane, a_rows_dma, tm_active, acc);
+  }
+}
+
 template <class C>
 __device__ __forceinline__ void mainloop(Smem<C>& sm, const Operand& A, const Operand& B, int kt0, int kt1,
                                          int tm_active, typename C::Acc (&acc)[C::TM][C::TN]) {
@@ -449,12 +521,10 @@ __device__ __forceinline__ void mainloop(Smem<C>& sm, const Operand& A, const Op
   for (int i = 0; i < C::STAGES - 1; ++i)
     if (i < n) issue_stage<C>(sm, i, A, B, kt0 + i, wave, lane, a_rows_dma);
   stage_ready<C>(min(C::STAGES - 2, n - 1));
-  for (int i = 0; i < n; ++i) {
-    const int pre = i + C::STAGES - 1;
-    if (pre < n) issue_stage<C>(sm, pre % C::STAGES, A, B, kt0 + pre, wave, lane, a_rows_dma);
-    compute_stage<C>(sm, i % C::STAGES, tm_active, acc);
-    if (i + 1 < n) stage_ready<C>(min(C::STAGES - 2, n - 2 - i));
-  }
+  const ReadAddr<C> ra = read_addr<C>(sm);
+  // unrolled by STAGES: each stage buffer's LDS offset is a constant
+  for (int i0 = 0; i0 < n; i0 += C::STAGES)
+    stage_steps<C, 0>(sm, ra, A, B, i0, n, kt0, wave, lane, a_rows_dma, tm_active, acc);
 }
 
 // alpha * acc -> bf16 stores; bounds checks only for partial tiles.
