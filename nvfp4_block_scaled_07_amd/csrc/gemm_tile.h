@@ -212,33 +212,18 @@ struct StageDma {
   static_assert(kMinPerWave * (C::STAGES - 2) <= 63, "vmcnt range");
 };
 
-// The DMA of one stage in four parts (A codes, B codes, A scales, B scales);
-// PART = -1 issues all of them.  Parts are issued in order.
-template <class C, int PART = -1>
+template <class C>
 __device__ __forceinline__ void issue_stage(Smem<C>& sm, int buf, const Operand& A, const Operand& B, int kt,
                                             int wave, int lane, int a_rows_dma) {
   typedef StageDma<C> D;
   constexpr int W = C::kWaves;
-  if constexpr (PART < 0 || PART == 0)
-    dma_tile<C::BM, C::RB, 16, C::MF, W, 0>(sm.a[buf], A.data, A.ld, A.rows, kt * C::RB, wave, lane, a_rows_dma);
-  if constexpr (PART < 0 || PART == 1)
-    dma_tile<C::BN, C::RB, 16, C::MF, W, D::A::kInst>(sm.b[buf], B.data, B.ld, B.rows, kt * C::RB, wave, lane);
-  if constexpr (PART < 0 || PART == 2)
-    dma_tile<C::BM, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst>(sm.asf[buf], A.sf, A.lds, A.rows,
-                                                                       kt * C::SB, wave, lane);
-  if constexpr (PART < 0 || PART == 3)
-    dma_tile<C::BN, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst>(sm.bsf[buf], B.sf, B.lds,
-                                                                                      B.rows, kt * C::SB, wave, lane);
+  dma_tile<C::BM, C::RB, 16, C::MF, W, 0>(sm.a[buf], A.data, A.ld, A.rows, kt * C::RB, wave, lane, a_rows_dma);
+  dma_tile<C::BN, C::RB, 16, C::MF, W, D::A::kInst>(sm.b[buf], B.data, B.ld, B.rows, kt * C::RB, wave, lane);
+  dma_tile<C::BM, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst>(sm.asf[buf], A.sf, A.lds, A.rows,
+                                                                     kt * C::SB, wave, lane);
+  dma_tile<C::BN, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst>(sm.bsf[buf], B.sf, B.lds,
+                                                                                    B.rows, kt * C::SB, wave, lane);
 }
-
-// The DMA of a later stage, issued from inside compute_stage.
-struct NextStage {
-  const Operand* A;
-  const Operand* B;
-  int buf, kt;
-  bool live;  // false past the last K tile
-  int wave, lane, a_rows_dma;
-};
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then a work-group barrier.  The empty asm
 // keeps the compiler from moving LDS accesses across it.
@@ -425,17 +410,15 @@ __device__ __forceinline__ ReadAddr<C> read_addr(const Smem<C>& sm) {
 
 // Multiply-accumulate one LDS stage (buffer BUF) into acc.
 template <class C, int BUF>
-__device__ __forceinline__ void compute_stage(Smem<C>& sm, const ReadAddr<C>& ra, int tm_active,
-                                              typename C::Acc (&acc)[C::TM][C::TN], const NextStage& nx) {
+__device__ __forceinline__ void compute_stage(const Smem<C>& sm, const ReadAddr<C>& ra, int tm_active,
+                                              typename C::Acc (&acc)[C::TM][C::TN]) {
   if constexpr (C::kMx) {
-    if (nx.live) issue_stage<C>(sm, nx.buf, *nx.A, *nx.B, nx.kt, nx.wave, nx.lane, nx.a_rows_dma);
     compute_stage_mx<C>(sm, BUF, acc);
     return;
-  } else {
+  }
   constexpr int kScaleStep = 2 * C::KG * C::KS;  // scale bytes between a K-group's sub-steps
-  constexpr int kS = ReadAddr<C>::kS;
-  static_for<kS>([&](auto ssc) {
-    constexpr int ss = decltype(ssc)::value;
+#pragma unroll
+  for (int ss = 0; ss < ReadAddr<C>::kS; ++ss) {
     u4_t ac[C::TM], bc[C::TN];
     uint32_t asw[C::TM], bsw[C::TN];
     static_for<C::TM>([&](auto tmc) {
@@ -450,14 +433,6 @@ __device__ __forceinline__ void compute_stage(Smem<C>& sm, const ReadAddr<C>& ra
       ds_read128_at<BUF * C::BN * C::RB + tn * C::MF * C::RB>(bc[tn], ra.b[ss]);
       ds_read_u16_at<BUF * C::BN * C::SB + tn * C::MF * C::SB>(bsw[tn], ra.bs + ss * kScaleStep);
     });
-    // the next stage's DMA, one part per sub-step (the rest with the last),
-    // behind this sub-step's reads: the address unit takes 72 instructions a
-    // stage, and issued all at once they stall every wave for over 1000 cycles
-    asm volatile("" ::: "memory");
-    if (nx.live) {
-      if constexpr (kS >= 4) issue_stage<C, ss>(sm, nx.buf, *nx.A, *nx.B, nx.kt, nx.wave, nx.lane, nx.a_rows_dma);
-      else if constexpr (ss + 1 == kS) issue_stage<C>(sm, nx.buf, *nx.A, *nx.B, nx.kt, nx.wave, nx.lane, nx.a_rows_dma);
-    }
     lgkm_wait();
     h2_t asp[C::TM], bsp[C::TN];
 #pragma unroll
@@ -495,7 +470,6 @@ __device__ __forceinline__ void compute_stage(Smem<C>& sm, const ReadAddr<C>& ra
         __builtin_amdgcn_sched_group_barrier(0x002, C::IL, 0);  // then IL VALU
       }
     }
-  });
   }
 }
 
@@ -522,8 +496,8 @@ __device__ __forceinline__ void stage_steps(Smem<C>& sm, const ReadAddr<C>& ra, 
     const int i = i0 + J;
     if (i >= n) return;
     const int pre = i + C::STAGES - 1;
-    compute_stage<C, J>(sm, ra, tm_active, acc,
-                        NextStage{&A, &B, (J + C::STAGES - 1) % C::STAGES, kt0 + pre, pre < n, wave, lane, a_rows_dma});
+    if (pre < n) issue_stage<C>(sm, (J + C::STAGES - 1) % C::STAGES, A, B, kt0 + pre, wave, lane, a_rows_dma);
+    compute_stage<C, J>(sm, ra, tm_active, acc);
     if (i + 1 < n) stage_ready<C>(min(C::STAGES - 2, n - 2 - i));
     stage_steps<C, J + 1>(sm, ra, A, B, i0, n, kt0, wave, lane, a_rows_dma, tm_active, acc);
   }
