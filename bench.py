@@ -291,18 +291,44 @@ GROUPED_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_grouped_moe_pac
 COPY_BYTES = 256 << 20
 
 
+def _strip_c_comments(text):
+    """C/C++ source without // and /* */ comments (string and character
+    literals kept) and without trailing blanks, so that a comment edit does not
+    change the digest."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(l.rstrip() for l in "".join(out).splitlines() if l.strip())
+
+
 def kernel_sources_digest():
-    """sha256 over the library's kernel sources and its build script (which
-    holds the compiler flags): a traffic record only holds for the kernels it
-    was measured on."""
+    """sha256 over the library's kernel sources (comments stripped) and the
+    build's source list and compiler flags: a traffic record only holds for the
+    kernels it was measured on."""
     import hashlib
+    from nvfp4_block_scaled_07_amd import build as b
     h = hashlib.sha256()
-    pkg = os.path.join(ROOT, "nvfp4_block_scaled_07_amd")
-    src = os.path.join(pkg, "csrc")
-    files = [os.path.join(src, f) for f in sorted(os.listdir(src)) if f.endswith((".hip", ".h"))]
-    for path in files + [os.path.join(pkg, "build.py")]:
-        h.update(os.path.basename(path).encode())
-        h.update(open(path, "rb").read())
+    src = os.path.join(ROOT, "nvfp4_block_scaled_07_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(_strip_c_comments(open(os.path.join(src, f)).read()).encode())
+    h.update(repr((b.SOURCES, b.SCHED_SOURCES, [x for x in b.FLAGS if not os.path.isabs(x)])).encode())
     return h.hexdigest()[:16]
 
 

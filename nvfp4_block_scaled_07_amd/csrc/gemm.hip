@@ -42,6 +42,16 @@
 //    packed once (k_pack_b) into the grouped kernel's lane order.
 //  * Work-group order is remapped so that work-groups sharing operand rows
 //    run on the same XCD (its own 4 MB L2).
+//  * The LDS read addresses of a lane are computed once per tile; stage
+//    buffers, row blocks and later sub-steps are compile-time offsets in the
+//    instructions' offset fields (the stage loop is unrolled by the number of
+//    stages), so the stage loop issues no address arithmetic.
+//
+// Files: the LDS-staged tile kernel k_gemm and its helpers are in
+// gemm_tile.h; the two large-M 8-wave NVFP4 tiles are instantiated in
+// gemm_large.hip (built with another instruction schedule); this file holds
+// the other tiles, the register-streamed and grouped kernels, the plans and
+// the launchers.
 #include <limits.h>
 #include <stdio.h>
 #include <stdlib.h>
