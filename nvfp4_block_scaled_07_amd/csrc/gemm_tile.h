@@ -483,9 +483,6 @@ __device__ __forceinline__ void zero_acc(typename C::Acc (&acc)[C::TM][C::TN]) {
       for (int j = 0; j < Mfma<C::MF>::kAcc; ++j) acc[tm][tn][j] = 0.0f;
 }
 
-// K-tiles [kt0, kt1) of the tile into acc (which is zeroed first).  Loads run
-// STAGES - 1 stages ahead of the MFMAs; each wait only drains the stage needed
-// next, so the later stages stay in flight across the barrier.
 // Stages i0 + J, i0 + J + 1, ... (J < STAGES) of the main loop: issue the DMA
 // of the stage STAGES - 1 ahead, compute this one, wait for the next.
 template <class C, int J>
@@ -503,6 +500,9 @@ __device__ __forceinline__ void stage_steps(Smem<C>& sm, const ReadAddr<C>& ra, 
   }
 }
 
+// K-tiles [kt0, kt1) of the tile into acc (which is zeroed first).  Loads run
+// STAGES - 1 stages ahead of the MFMAs; each wait only drains the stage needed
+// next, so the later stages stay in flight across the barrier.
 template <class C>
 __device__ __forceinline__ void mainloop(Smem<C>& sm, const Operand& A, const Operand& B, int kt0, int kt1,
                                          int tm_active, typename C::Acc (&acc)[C::TM][C::TN]) {
