@@ -272,6 +272,12 @@ __device__ __forceinline__ void ds_read128_at(u4_t& v, uint32_t a) {
   if constexpr (OFF < 65536) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
   else ds_read128(v, a + OFF);
 }
+// 8 bits, zero-extended
+template <int OFF>
+__device__ __forceinline__ void ds_read_u8_at(uint32_t& v, uint32_t a) {
+  if constexpr (OFF < 65536) asm volatile("ds_read_u8 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
+  else asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(a + OFF));
+}
 // 16 bits, zero-extended
 template <int OFF>
 __device__ __forceinline__ void ds_read_u16_at(uint32_t& v, uint32_t a) {
@@ -295,82 +301,10 @@ __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // sub-step ss run (two register slots): with no dequantisation between the
 // reads and the MFMAs, the read latency is otherwise as long as a
 // sub-step's MFMAs.
-template <class C>
-struct MxFrags {
-  u4_t ac[C::TM], bc[C::TN];
-  uint32_t asw[C::TM], bsw[C::TN];
-};
 
-template <class C>
-__device__ __forceinline__ void mx_read(MxFrags<C>& f, const Smem<C>& sm, int buf, int ss, int wm, int wn, int r_in,
-                                        int g, int kgrp) {
-  const uint32_t a_base = lds_addr(sm.a[buf]), b_base = lds_addr(sm.b[buf]);
-  const uint32_t as_base = lds_addr(sm.asf[buf]), bs_base = lds_addr(sm.bsf[buf]);
-  const int c = C::KG * (ss * C::KS + kgrp) + g;  // chunk = MX block of this lane in the stage
-#pragma unroll
-  for (int tm = 0; tm < C::TM; ++tm) {
-    const int row = wm * C::kWM + tm * 32 + r_in;
-    ds_read128(f.ac[tm], a_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
-    ds_read32(f.asw[tm], as_base + row * C::SB + 4 * (c >> 2));
-  }
-#pragma unroll
-  for (int tn = 0; tn < C::TN; ++tn) {
-    const int row = wn * C::kWN + tn * 32 + r_in;
-    ds_read128(f.bc[tn], b_base + row * C::RB + ((c ^ swz<C::CH, 32>(row)) << 4));
-    ds_read32(f.bsw[tn], bs_base + row * C::SB + 4 * (c >> 2));
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void compute_stage_mx(const Smem<C>& sm, int buf, typename C::Acc (&acc)[C::TM][C::TN]) {
-  typedef int v8i_t __attribute__((ext_vector_type(8)));
-  constexpr int NS = C::kSub / C::KS;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
-  const int wm = gw / C::WN, wn = gw % C::WN;
-  const int r_in = lane % 32, g = lane / 32;
-  MxFrags<C> f[2];
-  mx_read<C>(f[0], sm, buf, 0, wm, wn, r_in, g, kgrp);
-#pragma unroll
-  for (int ss = 0; ss < NS; ++ss) {
-    MxFrags<C>& cur = f[ss & 1];
-    lgkm_wait();  // slot ss & 1 has landed (nothing else is in flight)
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm) {
-      pin(cur.ac[tm]);
-      pin(cur.asw[tm]);
-    }
-#pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-      pin(cur.bc[tn]);
-      pin(cur.bsw[tn]);
-    }
-    if (ss + 1 < NS) mx_read<C>(f[(ss + 1) & 1], sm, buf, ss + 1, wm, wn, r_in, g, kgrp);
-    const int sh = 8 * ((C::KG * (ss * C::KS + kgrp) + g) & 3);
-    v8i_t av[C::TM], bv[C::TN];
-    int sa[C::TM], sb[C::TN];
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm) {
-      av[tm] = v8i_t{(int)cur.ac[tm][0], (int)cur.ac[tm][1], (int)cur.ac[tm][2], (int)cur.ac[tm][3], 0, 0, 0, 0};
-      sa[tm] = (int)(cur.asw[tm] >> sh);
-    }
-#pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-      bv[tn] = v8i_t{(int)cur.bc[tn][0], (int)cur.bc[tn][1], (int)cur.bc[tn][2], (int)cur.bc[tn][3], 0, 0, 0, 0};
-      sb[tn] = (int)(cur.bsw[tn] >> sh);
-    }
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[tm], bv[tn], acc[tm][tn], 4, 4, 0, sa[tm],
-                                                                       0, sb[tn]);
-  }
-}
-
-// Per-lane LDS read addresses of a dequantising tile, computed once per tile
-// (stage buffer 0, first row block): the code chunk of each sub-step of this
-// lane's K-group and the scale pair of its first sub-step.  Stage buffers, row
+// Per-lane LDS read addresses of a tile, computed once per tile (stage buffer
+// 0, first row block): the code chunk of each sub-step of this lane's K-group
+// and the scales of its first sub-step.  Stage buffers, row
 // blocks and later sub-steps' scales are compile-time offsets from these.
 template <class C>
 struct ReadAddr {
@@ -382,7 +316,6 @@ struct ReadAddr {
 template <class C>
 __device__ __forceinline__ ReadAddr<C> read_addr(const Smem<C>& sm) {
   ReadAddr<C> ra;
-  if constexpr (C::kMx) return ra;  // the scaled-FP4 stage computes its own
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int gw = wave % C::kGroupWaves, kgrp = wave / C::kGroupWaves;
   const int wm = gw / C::WN, wn = gw % C::WN;
@@ -399,13 +332,75 @@ __device__ __forceinline__ ReadAddr<C> read_addr(const Smem<C>& sm) {
     pin(ra.a[ss]);
     pin(ra.b[ss]);
   }
-  // the two scale bytes of chunk c (blocks 2c and 2c + 1) are at byte 2c
+  // chunk c's scales: NVFP4 bytes 2c and 2c + 1 (blocks of 16), MXFP4 byte c
+  constexpr int kScalePerChunk = 32 / C::SBLK;
   const int c0 = C::KG * kgrp + g;
-  ra.as = lds_addr(sm.asf[0]) + ra_row * C::SB + 2 * c0;
-  ra.bs = lds_addr(sm.bsf[0]) + rb_row * C::SB + 2 * c0;
+  ra.as = lds_addr(sm.asf[0]) + ra_row * C::SB + kScalePerChunk * c0;
+  ra.bs = lds_addr(sm.bsf[0]) + rb_row * C::SB + kScalePerChunk * c0;
   pin(ra.as);
   pin(ra.bs);
   return ra;
+}
+
+template <class C>
+struct MxFrags {
+  u4_t ac[C::TM], bc[C::TN];
+  uint32_t asw[C::TM], bsw[C::TN];  // the chunk's E8M0 scale byte
+};
+
+// LDS reads of MX sub-step SS of stage buffer BUF
+template <class C, int BUF, int SS>
+__device__ __forceinline__ void mx_read(MxFrags<C>& f, const ReadAddr<C>& ra) {
+  constexpr int kScale = SS * C::KG * C::KS;  // one scale byte per chunk
+  static_for<C::TM>([&](auto tmc) {
+    constexpr int tm = decltype(tmc)::value;
+    ds_read128_at<BUF * C::BM * C::RB + tm * 32 * C::RB>(f.ac[tm], ra.a[SS]);
+    ds_read_u8_at<BUF * C::BM * C::SB + tm * 32 * C::SB + kScale>(f.asw[tm], ra.as);
+  });
+  static_for<C::TN>([&](auto tnc) {
+    constexpr int tn = decltype(tnc)::value;
+    ds_read128_at<BUF * C::BN * C::RB + tn * 32 * C::RB>(f.bc[tn], ra.b[SS]);
+    ds_read_u8_at<BUF * C::BN * C::SB + tn * 32 * C::SB + kScale>(f.bsw[tn], ra.bs);
+  });
+}
+
+// One MX stage (buffer BUF): the next sub-step's reads are issued into the
+// other fragment set before this sub-step's MFMAs.
+template <class C, int BUF>
+__device__ __forceinline__ void compute_stage_mx(const ReadAddr<C>& ra, typename C::Acc (&acc)[C::TM][C::TN]) {
+  typedef int v8i_t __attribute__((ext_vector_type(8)));
+  constexpr int NS = C::kSub / C::KS;
+  MxFrags<C> f[2];
+  mx_read<C, BUF, 0>(f[0], ra);
+  static_for<NS>([&](auto ssc) {
+    constexpr int ss = decltype(ssc)::value;
+    MxFrags<C>& cur = f[ss & 1];
+    lgkm_wait();  // slot ss & 1 has landed (nothing else is in flight)
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      pin(cur.ac[tm]);
+      pin(cur.asw[tm]);
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      pin(cur.bc[tn]);
+      pin(cur.bsw[tn]);
+    }
+    if constexpr (ss + 1 < NS) mx_read<C, BUF, ss + 1>(f[(ss + 1) & 1], ra);
+    v8i_t av[C::TM], bv[C::TN];
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+      av[tm] = v8i_t{(int)cur.ac[tm][0], (int)cur.ac[tm][1], (int)cur.ac[tm][2], (int)cur.ac[tm][3], 0, 0, 0, 0};
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn)
+      bv[tn] = v8i_t{(int)cur.bc[tn][0], (int)cur.bc[tn][1], (int)cur.bc[tn][2], (int)cur.bc[tn][3], 0, 0, 0, 0};
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[tm], bv[tn], acc[tm][tn], 4, 4, 0,
+                                                                       (int)cur.asw[tm], 0, (int)cur.bsw[tn]);
+  });
 }
 
 // Multiply-accumulate one LDS stage (buffer BUF) into acc.
@@ -413,7 +408,7 @@ template <class C, int BUF>
 __device__ __forceinline__ void compute_stage(const Smem<C>& sm, const ReadAddr<C>& ra, int tm_active,
                                               typename C::Acc (&acc)[C::TM][C::TN]) {
   if constexpr (C::kMx) {
-    compute_stage_mx<C>(sm, BUF, acc);
+    compute_stage_mx<C, BUF>(ra, acc);
     return;
   }
   constexpr int kScaleStep = 2 * C::KG * C::KS;  // scale bytes between a K-group's sub-steps
