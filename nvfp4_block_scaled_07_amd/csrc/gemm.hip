@@ -900,11 +900,18 @@ typedef KCfg<64, 32, 4, 2, 2, 1> MxReg64x32;
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2> CfgTile128k256;    // 4 waves of 64x64
 // MXFP4 tiles (E8M0 scale per 32 elements, scaled FP4 MFMA)
 typedef Cfg<256, 256, 2, 2, 32, 256, 2, 0, 1, 1, 32> CfgMx256;      // 4 waves x 128x128, 136 KB LDS
-typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx128;      // 4 waves x 64x64, 68 KB (split-K)
+typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32, 2> CfgMx128;   // 4 waves x 64x64, 68 KB (split-K), waves 0-1 load
+                                                                     // (1024 x 6144 x 6144: 45.1 -> 42.0 us)
 typedef Cfg<64, 64, 2, 2, 32, 256, 3, 0, 1, 2, 32> CfgMx64;         // 4 waves x 32x32 (split-K)
-typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2, 32> CfgMx256w8;    // 8 waves x 128x64
-typedef Cfg<256, 256, 2, 4, 32, 128, 4, 0, 1, 2, 32> CfgMx256w8s4;  // the same, 4 stages of 128
-typedef Cfg<256, 192, 4, 2, 32, 256, 2, 0, 1, 2, 32> CfgMx256x192;  // 8 waves x 64x96, 119 KB
+// The 8-wave MX tiles issue each stage's loads from waves 0-3 only (one wave
+// per SIMD): the other four start their LDS reads and MFMAs at once instead
+// of waiting on the memory pipeline too (8192 x 6144 x 6144: 179.6 -> 172.0
+// us, 4096 x 6144 x 6144 on 256x192 tiles: 105.8 -> 98.9 us; bitwise the
+// same).  With no dequantisation the MX tiles' MFMAs are short enough for
+// that wait to show; on the NVFP4 tiles it made no difference or lost.
+typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2, 32, 4> CfgMx256w8;    // 8 waves x 128x64
+typedef Cfg<256, 256, 2, 4, 32, 128, 4, 0, 1, 2, 32> CfgMx256w8s4;     // all waves load, 4 stages of 128
+typedef Cfg<256, 192, 4, 2, 32, 256, 2, 0, 1, 2, 32, 4> CfgMx256x192;  // 8 waves x 64x96, 119 KB
 typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass

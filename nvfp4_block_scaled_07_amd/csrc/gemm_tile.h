@@ -56,7 +56,7 @@ struct Mfma<16> {
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int MF_, int BK_, int STAGES_, int IL_ = 0, int KS_ = 1,
-          int OCC_ = 1, int SBLK_ = 16>
+          int OCC_ = 1, int SBLK_ = 16, int DW_ = 0>
 struct Cfg {
   // SBLK: elements per scale: 16 (NVFP4, e4m3 scales, f16 MFMA after
   // dequantisation) or 32 (MXFP4, E8M0 scales, scaled FP4 MFMA)
@@ -75,6 +75,11 @@ struct Cfg {
   static constexpr int kGroupWaves = WM * WN;
   static constexpr int kWaves = KS * WM * WN;
   static constexpr int kThreads = kWaves * 64;
+  // DW > 0: only waves 0 .. DW - 1 issue the stage loads (the others go
+  // straight to their LDS reads and MFMAs while those wait on the memory
+  // pipeline); 0: every wave issues its share
+  static constexpr int kDmaWaves = DW_ == 0 ? kWaves : DW_;
+  static_assert(DW_ >= 0 && DW_ <= kWaves, "DMA waves");
   static constexpr int kWM = BM / WM;        // rows per wave
   static constexpr int kWN = BN / WN;        // cols per wave
   static constexpr int TM = kWM / MF;        // MFMA tiles per wave along M
@@ -142,12 +147,24 @@ constexpr int swz_period() {
   return CH == 8 ? (MF == 32 ? 16 : 8) : (CH == 4 ? (MF == 32 ? 8 : 4) : 8);
 }
 
-template <int ROWS, int BYTES, int VEC, int SWZ_MF, int NWAVES, int BASE>
+// wave < 0: this wave issues none of the tile's instructions.  UNIFORM: the
+// descriptor and scalar offsets are passed through readfirstlane (they are
+// uniform; with some waves skipping the loads the compiler no longer proves
+// it and would otherwise loop over lanes for every instruction).
+template <int ROWS, int BYTES, int VEC, int SWZ_MF, int NWAVES, int BASE, bool UNIFORM = false>
 __device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int64_t ld, int rows_valid, int col,
                                          int wave, int lane, int rows_dma = ROWS) {
   typedef DmaShape<ROWS, BYTES, VEC> D;
   static_assert(SWZ_MF == 0 || (2 * D::kRowsPerInst) % swz_period<D::kPerRow, SWZ_MF>() == 0, "swizzle period");
-  const rsrc_t rs = make_rsrc(base + col, (uint32_t)((int64_t)rows_valid * ld - col));
+  rsrc_t rs;
+  if constexpr (UNIFORM) {
+    const uint64_t pb = (uint64_t)(uintptr_t)(base + col);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pb), hi = __builtin_amdgcn_readfirstlane((uint32_t)(pb >> 32));
+    rs = make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
+                   __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)rows_valid * ld - col)));
+  } else {
+    rs = make_rsrc(base + col, (uint32_t)((int64_t)rows_valid * ld - col));
+  }
   const int lr = lane / D::kPerRow, p = lane % D::kPerRow;
   const bool full = rows_valid >= ROWS;  // uniform
   // per-lane byte offset within a group of kRowsPerInst rows (two variants:
@@ -165,7 +182,8 @@ __device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int6
   // only this wave's instructions: j = j0, j0 + NWAVES, ... (a loop over
   // every j with a per-j wave test costs a scalar branch per instruction of
   // the whole stage in every wave)
-  const int j0 = ((wave - BASE) % NWAVES + NWAVES) % NWAVES;
+  int j0 = ((wave - BASE) % NWAVES + NWAVES) % NWAVES;
+  if constexpr (UNIFORM) j0 = wave < 0 ? D::kInst : j0;
   constexpr int kPerWave = (D::kInst + NWAVES - 1) / NWAVES;
 #pragma unroll
   for (int jj = 0; jj < kPerWave; ++jj) {
@@ -173,7 +191,8 @@ __device__ __forceinline__ void dma_tile(uint8_t* dst, const uint8_t* base, int6
     if (j < D::kInst && j * D::kRowsPerInst < rows_dma) {
       const int r = j * D::kRowsPerInst + lr;
       if (D::kInst * D::kRowsPerInst == ROWS || r < ROWS) {
-        const uint32_t soff = (uint32_t)(j * D::kRowsPerInst * ld);
+        uint32_t soff = (uint32_t)(j * D::kRowsPerInst * ld);
+        if constexpr (UNIFORM) soff = __builtin_amdgcn_readfirstlane(soff);
         const uint32_t vo = (full || r < rows_valid) ? voff[j & 1] : 0x80000000u;
         if constexpr (VEC == 16)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 64 * VEC), 16, vo, soff, 0, 0);
@@ -205,10 +224,10 @@ struct StageDma {
   typedef DmaShape<C::BM, C::SB, SV> AS;
   typedef DmaShape<C::BN, C::SB, SV> BS;
   static constexpr int kTotal = A::kInst + B::kInst + AS::kInst + BS::kInst;
-  // Every wave issues at least this many load instructions per stage.  A's
+  // Every wave that issues loads issues at least this many per stage.  A's
   // code instructions come first and may be skipped (rows an expert does not
   // have), so only the instructions after them are counted.
-  static constexpr int kMinPerWave = (kTotal - A::kInst) / C::kWaves;
+  static constexpr int kMinPerWave = (kTotal - A::kInst) / C::kDmaWaves;
   static_assert(kMinPerWave * (C::STAGES - 2) <= 63, "vmcnt range");
 };
 
@@ -216,13 +235,15 @@ template <class C>
 __device__ __forceinline__ void issue_stage(Smem<C>& sm, int buf, const Operand& A, const Operand& B, int kt,
                                             int wave, int lane, int a_rows_dma) {
   typedef StageDma<C> D;
-  constexpr int W = C::kWaves;
-  dma_tile<C::BM, C::RB, 16, C::MF, W, 0>(sm.a[buf], A.data, A.ld, A.rows, kt * C::RB, wave, lane, a_rows_dma);
-  dma_tile<C::BN, C::RB, 16, C::MF, W, D::A::kInst>(sm.b[buf], B.data, B.ld, B.rows, kt * C::RB, wave, lane);
-  dma_tile<C::BM, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst>(sm.asf[buf], A.sf, A.lds, A.rows,
-                                                                     kt * C::SB, wave, lane);
-  dma_tile<C::BN, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst>(sm.bsf[buf], B.sf, B.lds,
-                                                                                    B.rows, kt * C::SB, wave, lane);
+  constexpr int W = C::kDmaWaves;
+  constexpr bool U = W < C::kWaves;
+  if constexpr (U) wave = wave < W ? wave : -1;
+  dma_tile<C::BM, C::RB, 16, C::MF, W, 0, U>(sm.a[buf], A.data, A.ld, A.rows, kt * C::RB, wave, lane, a_rows_dma);
+  dma_tile<C::BN, C::RB, 16, C::MF, W, D::A::kInst, U>(sm.b[buf], B.data, B.ld, B.rows, kt * C::RB, wave, lane);
+  dma_tile<C::BM, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst, U>(sm.asf[buf], A.sf, A.lds, A.rows,
+                                                                        kt * C::SB, wave, lane);
+  dma_tile<C::BN, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst, U>(sm.bsf[buf], B.sf, B.lds,
+                                                                                       B.rows, kt * C::SB, wave, lane);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then a work-group barrier.  The empty asm
