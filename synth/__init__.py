@@ -170,3 +170,15 @@ def adversarial_offsets(kind: str, rows: int, experts: int) -> np.ndarray:
     offsets = np.zeros(experts + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(counts)
     return offsets
+
+
+def fp32_bit_patterns(lo: int, hi: int, negative: bool = False) -> np.ndarray:
+    """The fp32 values whose bit patterns are lo, lo + 1, ..., hi - 1 (all
+    below 2^31), with the sign bit set when ``negative``: the inputs of the
+    exhaustive rounding sweep."""
+    if not 0 <= lo <= hi <= 1 << 31:
+        raise ValueError("pattern range must lie in [0, 2^31]")
+    bits = np.arange(lo, hi, dtype=np.uint32)
+    if negative:
+        bits |= np.uint32(0x80000000)
+    return bits.view(np.float32)

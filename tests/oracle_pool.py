@@ -54,6 +54,16 @@ def quantize_block(args):
 
 
 # ---------------------------------------------------------------------------
+# The exhaustive e2m1 rounding sweep.
+# ---------------------------------------------------------------------------
+def e2m1_codes_of_patterns(args):
+    """The oracle's e2m1 codes of the fp32 values of bit patterns [lo, hi)
+    (sign bit set when negative)."""
+    lo, hi, negative = args
+    return o.e2m1_encode(synth.fp32_bit_patterns(lo, hi, negative))
+
+
+# ---------------------------------------------------------------------------
 # Element-by-element comparison of GPU output rows with the oracle.
 # ---------------------------------------------------------------------------
 class Stats:

@@ -5,6 +5,7 @@ import torch
 
 import synth
 from oracle import nvfp4_ref as o
+from tests import oracle_pool as op
 from tests.gpu_util import dev, gpu_global_scale, gpu_quantize, host, say
 
 pytestmark = pytest.mark.gpu
@@ -115,6 +116,44 @@ def test_e2m1_rounding_sweep_over_fp32_patterns():
         for lo in range(0, x.shape[0], 1 << 16):
             part = np.ascontiguousarray(x[lo:lo + (1 << 16)])
             _check_quant(part, np.float32(1), None, f"e2m1 sweep sign {sign:+.0f} rows {lo}")
+
+
+def test_e2m1_rounding_exhaustive_up_to_six():
+    # every fp32 bit pattern of magnitude <= 6 in both signs (2 x 1,086,324,737
+    # values, -0, subnormals and 6 itself included), 15 to a block behind an
+    # anchor of 6: the block scale is 1 (0x38) and r = 1, so each code must be
+    # the oracle's e2m1 code of the value itself.  Larger magnitudes cannot
+    # keep r = 1 (they raise the block amax); the scale tests cover them.
+    top = int(np.float32(6.0).view(np.uint32)) + 1
+    chunk = 1 << 24
+    jobs = [(lo, min(lo + chunk, top), neg) for neg in (False, True) for lo in range(0, top, chunk)]
+    done = 0
+    with op.make_pool() as pool:
+        for i, ((lo, hi, neg), want) in enumerate(zip(jobs, pool.imap(op.e2m1_codes_of_patterns, jobs))):
+            if i % 16 == 0:
+                say("e2m1 exhaustive", f"chunk {i} of {len(jobs)}", "negative" if neg else "positive", hex(lo))
+            vals = synth.fp32_bit_patterns(lo, hi, neg)
+            n = len(vals)
+            nb = -(-n // 15)
+            body = np.zeros(nb * 15, np.float32)
+            body[:n] = vals
+            blk = np.empty((nb, 16), np.float32)
+            blk[:, 0] = 6.0
+            blk[:, 1:] = body.reshape(nb, 15)
+            q_t, sf_t = gpu_quantize(dev(blk), None)
+            sf, q = host(sf_t), host(q_t)
+            assert (sf == 0x38).all(), f"patterns {hex(lo)}..{hex(hi)}: a block scale is not 1"
+            codes = np.empty((nb, 16), np.uint8)
+            codes[:, 0::2] = q & 0xF
+            codes[:, 1::2] = q >> 4
+            assert (codes[:, 0] == 0x7).all()
+            got = codes[:, 1:].reshape(-1)[:n]
+            if not np.array_equal(got, want):
+                j = int(np.flatnonzero(got != want)[0])
+                raise AssertionError(f"e2m1 code of fp32 pattern {int(vals[j:j + 1].view(np.uint32)[0]):#010x} "
+                                     f"({vals[j]!r}): GPU {got[j]:#x}, oracle {want[j]:#x}")
+            done += n
+    assert done == 2 * top
 
 
 def _e4m3_midpoints() -> np.ndarray:

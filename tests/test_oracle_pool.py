@@ -62,3 +62,20 @@ def test_ffn_helper_matches_the_layer_oracle():
     e_, st_gu, st_d, chain = op.ffn_expert_oracle((seed, e, H, I, qa, sfa, a_gu, gs_h, a_d, gu, hq, hsf, down))
     assert e_ == e and st_gu.bad == 0 and st_d.bad == 0 and st_gu.n == 4 * 2 * I and st_d.n == 4 * H
     np.testing.assert_array_equal(chain, down)
+
+
+def test_e2m1_sweep_helpers():
+    # the pattern generator gives the fp32 values of consecutive bit patterns,
+    # and the pool helper returns the oracle's codes of exactly those values
+    six = int(np.float32(6.0).view(np.uint32))
+    v = synth.fp32_bit_patterns(six - 2, six + 2)
+    assert v[2] == np.float32(6.0) and v[1] == np.nextafter(np.float32(6.0), np.float32(0))
+    neg = synth.fp32_bit_patterns(0, 3, negative=True)
+    assert np.signbit(neg).all() and neg[0] == 0 and neg[1] == -np.float32(2.0 ** -149)
+    lo, hi = int(np.float32(0.2).view(np.uint32)), int(np.float32(0.3).view(np.uint32))
+    for negative in (False, True):
+        got = op.e2m1_codes_of_patterns((lo, hi, negative))
+        np.testing.assert_array_equal(got, o.e2m1_encode(synth.fp32_bit_patterns(lo, hi, negative)))
+        quarter = int(np.float32(0.25).view(np.uint32)) - lo      # the 0 / 0.5 tie rounds to 0
+        sign = 0x8 if negative else 0
+        assert got[quarter] == sign and got[quarter + 1] == (sign | 1) and got[quarter - 1] == sign
