@@ -740,6 +740,40 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
                                              "draws), rotating sets of more than 512 MB; context only",
                                         shapes=ref)
 
+    # decode calls on scales in the tiled layouts (nvfp4_gemm_sf; the register
+    # tiles read them in place) against the same calls on linear scales, cold
+    tiled = []
+    for name, m in (("attn_proj_n768_k6144", 16), ("attn_proj_n768_k6144", 64), ("moe_expert_n2048_k6144", 64)):
+        w, sets, alpha, outs, wss = sweep_inputs(name, (m,))
+        n, k = w["n"], w["k"]
+        layouts = ((nv.SF_128x4, "sf128x4_us", nv.nvfp4_scales_128x4_size, nv.nvfp4_scales_to_128x4),
+                   (nv.SF_8x4, "sf8x4_us", nv.nvfp4_scales_8x4_size, nv.nvfp4_scales_to_8x4))
+        tsets = []
+        for qa, sfa, qb, sfb in sets:
+            t = {}
+            for lay, _, size, to in layouts:
+                ta = torch.empty(size(m, k), dtype=torch.uint8, device=dev)
+                tb = torch.empty(size(n, k), dtype=torch.uint8, device=dev)
+                to(sfa[:m], ta, m, k)
+                to(sfb, tb, n, k)
+                t[lay] = (ta, tb)
+            tsets.append(t)
+        reps, ns = 2 * len(sets), len(sets)
+        row = dict(M=m, N=n, K=k, plan=nv.nvfp4_gemm_plan(m, n, k),
+                   linear_us=round(timed(torch, stream, lambda i: call(w, sets[i % ns], alpha, outs, wss, m), reps), 2))
+        for lay, key, _, _ in layouts:
+            need = nv.nvfp4_gemm_sf_workspace_size(m, n, k, lay)
+            ws = nv.nvfp4_workspace_init(torch.empty(need, dtype=torch.uint8, device=dev)) if need else None
+            row[key] = round(timed(torch, stream, lambda i: nv.nvfp4_gemm_sf(
+                sets[i % ns][0][:m], tsets[i % ns][lay][0], sets[i % ns][2], tsets[i % ns][lay][1], alpha, outs[m],
+                m, n, k, lay, ws), reps), 2)
+        tiled.append(row)
+        del sets, tsets, outs, wss
+        torch.cuda.empty_cache()
+    res["tiled_scales"] = dict(note="nvfp4_gemm_sf with both scale tensors in the 128 x 4 or 8 x 4 tiled layout, "
+                                    "read in place by the register tiles, against nvfp4_gemm on linear scales; "
+                                    "cold (rotating sets)", shapes=tiled)
+
     # quantiser (prologue): 16384 x 6144 fp32 -> NVFP4
     us, by = quantize_workload(nv, torch, dev, stream, synth)
     res["quantize_16384x6144"] = dict(us=round(us, 2), gbps=round(by / us / 1e3, 1),

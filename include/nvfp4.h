@@ -309,6 +309,32 @@ nvfp4_status nvfp4_scales_to_8x4(const uint8_t* sf, uint8_t* tiled, int64_t rows
 nvfp4_status nvfp4_scales_from_8x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, void* stream);
 
 /*
+ * nvfp4_gemm with both scale tensors in one of the tiled layouts above, the
+ * switch that use_8x4_sf_layout is in the mm_fp4 signature ("The Art of
+ * Reading the Manual", section "The Message"): sf_layout 1 = the 128 x 4
+ * layout of nvfp4_scales_to_128x4, 2 = the 8 x 4 layout of
+ * nvfp4_scales_to_8x4, 0 = linear (then the call is nvfp4_gemm).  a_sf holds
+ * the tiled bytes of the M x K operand (nvfp4_scales_128x4_size(M, K) or
+ * nvfp4_scales_8x4_size(M, K)), b_sf those of the N x K operand; padding
+ * bytes are not read.  The plans of small M (the register tiles, M <= 128 at
+ * most widths) read the tiled scales in place.  Every other plan first
+ * writes linear copies of both into the workspace (two conversion launches
+ * on stream, then the GEMM), so the workspace must hold
+ * nvfp4_gemm_sf_workspace_size(M, N, K, sf_layout) bytes, 256-byte aligned,
+ * zero-filled once before first use as for nvfp4_gemm.  Everything else
+ * (arguments, alignment, results bit for bit, errors) is as for nvfp4_gemm;
+ * an sf_layout outside 0..2 is NVFP4_ERR_SHAPE.  The layouts are readings:
+ * the pages name the switch and describe no layout.
+ */
+nvfp4_status nvfp4_gemm_sf(const uint8_t* a, const uint8_t* a_sf,
+                           const uint8_t* b, const uint8_t* b_sf,
+                           const float* alpha, uint16_t* d,
+                           int64_t M, int64_t N, int64_t K, int32_t sf_layout,
+                           void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes of nvfp4_gemm_sf (0 for invalid sizes or layouts). */
+size_t nvfp4_gemm_sf_workspace_size(int64_t M, int64_t N, int64_t K, int32_t sf_layout);
+
+/*
  * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
  * The pages never quantise (their test used random bytes); this follows the
  * block_size 16 and e4m3fn scale format of the pages above with these steps,

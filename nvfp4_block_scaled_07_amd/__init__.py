@@ -28,6 +28,8 @@ SIGNATURES = {
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "nvfp4_gemm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "nvfp4_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_gemm_sf": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "nvfp4_gemm_sf_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "nvfp4_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "nvfp4_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
                                           _vp, _vp]),
@@ -246,6 +248,36 @@ def nvfp4_gemm(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, workspace=Non
                           _ptr(alpha, 4, "alpha", f), _ptr(d, 2 * _n(M, N), "d", f), M, N, K,
                           _ptr(workspace, 0, "workspace", f), _bytes(workspace), _stream(stream))
     _check(st, "nvfp4_gemm")
+    return d
+
+
+# scale layouts of nvfp4_gemm_sf
+SF_LINEAR, SF_128x4, SF_8x4 = 0, 1, 2
+
+
+def _sf_bytes(rows: int, K: int, sf_layout: int) -> int:
+    if sf_layout == SF_128x4:
+        return nvfp4_scales_128x4_size(rows, K)
+    if sf_layout == SF_8x4:
+        return nvfp4_scales_8x4_size(rows, K)
+    return _n(rows, K) // 16
+
+
+def nvfp4_gemm_sf_workspace_size(M: int, N: int, K: int, sf_layout: int) -> int:
+    return int(lib().nvfp4_gemm_sf_workspace_size(M, N, K, sf_layout))
+
+
+def nvfp4_gemm_sf(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, sf_layout: int, workspace=None,
+                  stream=None):
+    """nvfp4_gemm with a_sf and b_sf in the scale layout sf_layout (SF_128x4,
+    SF_8x4 or SF_LINEAR, tiled bytes as nvfp4_scales_to_128x4 / _8x4 write
+    them); see include/nvfp4.h.  d is returned."""
+    f = "nvfp4_gemm_sf"
+    st = lib().nvfp4_gemm_sf(_ptr(a, _n(M, K) // 2, "a", f), _ptr(a_sf, _sf_bytes(M, K, sf_layout), "a_sf", f),
+                             _ptr(b, _n(N, K) // 2, "b", f), _ptr(b_sf, _sf_bytes(N, K, sf_layout), "b_sf", f),
+                             _ptr(alpha, 4, "alpha", f), _ptr(d, 2 * _n(M, N), "d", f), M, N, K, sf_layout,
+                             _ptr(workspace, 0, "workspace", f), _bytes(workspace), _stream(stream))
+    _check(st, f)
     return d
 
 

@@ -49,10 +49,27 @@ nvfp4_status check_k(int64_t K) {
 // nvfp4_gemm and nvfp4_gemm_noalloc: the same checks, plans and kernels; the
 // second takes its split-K scratch from the library's fixed per-device array
 // instead of a caller workspace.
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Whether nvfp4_gemm_sf converts the tiled scales of this plan into linear
+// copies first (every plan but the register tiles, which read them in place).
+bool converts_scales(const nvfp4::GemmPlan& plan, int32_t sf_layout) {
+  return sf_layout != 0 && !nvfp4::plan_reads_tiled_scales(plan);
+}
+
+// Workspace of a GEMM call: the plan's own (split-K counters and partial
+// tiles), then, when the scales are converted, linear copies of a_sf and b_sf.
+size_t gemm_workspace(const nvfp4::GemmPlan& plan, int64_t M, int64_t N, int64_t K, int32_t sf_layout) {
+  if (!converts_scales(plan, sf_layout)) return plan.workspace;
+  return align256(plan.workspace) + align256((size_t)M * (size_t)(K / 16)) + align256((size_t)N * (size_t)(K / 16));
+}
+
 nvfp4_status gemm_call(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
                        const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* workspace,
-                       size_t workspace_bytes, void* stream, bool noalloc) {
-  const char* fn = noalloc ? "nvfp4_gemm_noalloc launch" : "nvfp4_gemm launch";
+                       size_t workspace_bytes, void* stream, bool noalloc, int32_t sf_layout = 0) {
+  const char* fn = noalloc ? "nvfp4_gemm_noalloc launch" : (sf_layout ? "nvfp4_gemm_sf launch" : "nvfp4_gemm launch");
+  if (sf_layout < 0 || sf_layout > 2 || (noalloc && sf_layout != 0))
+    return fail(NVFP4_ERR_SHAPE, "sf_layout = %d: 0 (linear), 1 (128 x 4) or 2 (8 x 4)", sf_layout);
   if (M < 0 || N < 0) return fail(NVFP4_ERR_SHAPE, "M = %lld, N = %lld must be >= 0", (long long)M, (long long)N);
   nvfp4_status s = check_k(K);
   if (s != NVFP4_OK) return s;
@@ -65,7 +82,8 @@ nvfp4_status gemm_call(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, 
   if (M > (1ll << 30) || N > (1ll << 30) || K > (1ll << 30))
     return fail(NVFP4_ERR_UNSUPPORTED, "dimensions above 2^30 are not supported");
   const nvfp4::GemmPlan plan = nvfp4::choose_plan(M, N, K);
-  if (plan.workspace > 0) {
+  const size_t need = gemm_workspace(plan, M, N, K, sf_layout);
+  if (need > 0) {
     if (noalloc) {
       if (plan.workspace > nvfp4::kNoAllocScratchBytes)
         return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu scratch bytes; nvfp4_gemm_noalloc holds at most %zu",
@@ -73,13 +91,26 @@ nvfp4_status gemm_call(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, 
       hipError_t e = nvfp4::noalloc_scratch((hipStream_t)stream, &workspace);
       if (e != hipSuccess) return hip_status(e, "nvfp4_gemm_noalloc scratch set-up");
     } else {
-      if (!workspace || workspace_bytes < plan.workspace)
-        return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu workspace bytes, got %zu", plan.name, plan.workspace,
+      if (!workspace || workspace_bytes < need)
+        return fail(NVFP4_ERR_WORKSPACE, "plan %s needs %zu workspace bytes, got %zu", plan.name, need,
                     workspace ? workspace_bytes : (size_t)0);
       if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "workspace must be 256-byte aligned");
     }
   }
-  nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 0, 1, 1};
+  nvfp4::GemmLaunch p{a, a_sf, b, b_sf, alpha, d, (float*)workspace, M, N, K, 0, 0, 1, 1, sf_layout};
+  if (converts_scales(plan, sf_layout)) {
+    uint8_t* lin_a = (uint8_t*)workspace + align256(plan.workspace);
+    uint8_t* lin_b = lin_a + align256((size_t)M * (size_t)(K / 16));
+    hipError_t e = sf_layout == 1 ? nvfp4::launch_scales_from_128x4(a_sf, lin_a, M, K, (hipStream_t)stream)
+                                  : nvfp4::launch_scales_from_8x4(a_sf, lin_a, M, K, (hipStream_t)stream);
+    if (e == hipSuccess)
+      e = sf_layout == 1 ? nvfp4::launch_scales_from_128x4(b_sf, lin_b, N, K, (hipStream_t)stream)
+                         : nvfp4::launch_scales_from_8x4(b_sf, lin_b, N, K, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "nvfp4_gemm_sf scale conversion");
+    p.a_sf = lin_a;
+    p.b_sf = lin_b;
+    p.sf_layout = 0;
+  }
   return hip_status(nvfp4::launch_gemm(plan, p, (hipStream_t)stream), fn);
 }
 
@@ -117,6 +148,17 @@ nvfp4_status nvfp4_gemm(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
 nvfp4_status nvfp4_gemm_noalloc(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
                                 const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, void* stream) {
   return gemm_call(a, a_sf, b, b_sf, alpha, d, M, N, K, nullptr, 0, stream, true);
+}
+
+size_t nvfp4_gemm_sf_workspace_size(int64_t M, int64_t N, int64_t K, int32_t sf_layout) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 256 || K > (int64_t(1) << 22) || sf_layout < 0 || sf_layout > 2) return 0;
+  return gemm_workspace(nvfp4::choose_plan(M, N, K), M, N, K, sf_layout);
+}
+
+nvfp4_status nvfp4_gemm_sf(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                           const float* alpha, uint16_t* d, int64_t M, int64_t N, int64_t K, int32_t sf_layout,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_call(a, a_sf, b, b_sf, alpha, d, M, N, K, workspace, workspace_bytes, stream, false, sf_layout);
 }
 
 size_t nvfp4_mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {

@@ -679,16 +679,50 @@ struct KRegs {
   uint32_t as[C::D][C::TM], bs[C::D][C::TN];        // scale words (4 e4m3)
 };
 
+// Scale layouts the register tiles read in place (nvfp4_gemm_sf): 0 linear
+// [rows][K/16]; 1 the 128 x 4 tiled layout (512-byte tiles of 128 rows x 4
+// scale columns, row-major tile order; row r, column c at byte (r % 32) 16 +
+// ((r % 128) / 32) 4 + c % 4); 2 the 8 x 4 one (32-byte tiles of 8 rows x 4
+// columns; row r, column c at byte (r % 8) 4 + c % 4).  In both tiled
+// layouts the 4 scales of columns 4 j .. 4 j + 3 of a row are one aligned
+// word, the word a lane loads per unit, so only its address changes.
+template <int SFL>
+struct SfLayout {
+  static_assert(SFL >= 0 && SFL <= 2, "scale layout");
+  // bytes between consecutive 256-element units of one row (4 words of 4 scales)
+  static constexpr uint32_t kUnitStep = SFL == 0 ? 16 : (SFL == 1 ? 4 * 512 : 4 * 32);
+  // Scale words of the tile's rows [m0, m0 + rows_valid) of a tensor with lds =
+  // K/16 bytes per row: the descriptor (bounded by the bytes those rows occupy)
+  // and the offset of word g of the tile's row r in unit 0.  m0 is a multiple
+  // of the tile height (16, 32 or 64), so a tile lies in one 128-row group of
+  // the 128 x 4 layout and starts on an 8-row group of the 8 x 4 one.
+  static __device__ __forceinline__ rsrc_t rsrc(const uint8_t* sf, int64_t m0, int rows_valid, int64_t lds) {
+    if constexpr (SFL == 0) return make_rsrc(sf + m0 * lds, (uint32_t)(rows_valid * lds));
+    else if constexpr (SFL == 1) return make_rsrc(sf + (m0 >> 7) * 128 * lds, (uint32_t)(128 * lds));
+    else return make_rsrc(sf + (m0 >> 3) * 8 * lds, (uint32_t)((rows_valid + 7) / 8 * 8 * lds));
+  }
+  static __device__ __forceinline__ uint32_t offset(int64_t m0, int r, int g, int64_t lds) {
+    if constexpr (SFL == 0) return (uint32_t)(r * lds + 4 * g);
+    else if constexpr (SFL == 1) {
+      const int q = (int)(m0 & 127) + r;
+      return (uint32_t)(512 * g + (q & 31) * 16 + ((q >> 5) & 3) * 4);
+    } else {
+      return (uint32_t)((r >> 3) * 8 * lds + 32 * g + (r & 7) * 4);
+    }
+  }
+};
+
 // Loads of unit `unit` into slot u; dead units (past the end of the range)
 // read out of range, which returns zero without a memory access, so every
 // iteration issues the same loads.
-template <class C>
+template <class C, int SFL>
 __device__ __forceinline__ void kreg_load(KRegs<C>& R, int u, int unit, bool live, const rsrc_t& ra,
                                           const rsrc_t& ras, const rsrc_t& rb, const rsrc_t& rbs,
                                           const uint32_t (&va)[C::TM][2], const uint32_t (&vas)[C::TM],
                                           const uint32_t (&vb)[C::TN][2], const uint32_t (&vbs)[C::TN]) {
   constexpr uint32_t kOut = 0x80000000u;
-  const int so = unit * (C::kUnit / 2), sso = unit * (C::kUnit / C::SBLK);
+  const int so = unit * (C::kUnit / 2);
+  const int sso = unit * (SFL == 0 ? C::kUnit / C::SBLK : (int)SfLayout<SFL>::kUnitStep);
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
 #pragma unroll
@@ -711,9 +745,10 @@ __device__ __forceinline__ void kreg_load(KRegs<C>& R, int u, int unit, bool liv
   }
 }
 
-template <class C>
+template <class C, int SFL = 0>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gemm_kreg(
     GemmLaunch p) {
+  static_assert(SFL == 0 || !C::kMx, "the tiled scale layouts are NVFP4 layouts");
   __shared__ __attribute__((aligned(16))) float red[C::KS * C::kTileFloats];
   __shared__ int last_flag;
   const int tiles_n = (int)p.tiles_n, S = p.splits;
@@ -723,9 +758,9 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   const int64_t ld = p.K / 2, lds = p.K / C::SBLK;
   const int rows_a = (int)min<int64_t>(C::BM, p.M - m0), rows_b = (int)min<int64_t>(C::BN, p.N - n0);
   const rsrc_t ra = make_rsrc(p.a + m0 * ld, (uint32_t)(rows_a * ld));
-  const rsrc_t ras = make_rsrc(p.a_sf + m0 * lds, (uint32_t)(rows_a * lds));
+  const rsrc_t ras = SfLayout<SFL>::rsrc(p.a_sf, m0, rows_a, lds);
   const rsrc_t rb = make_rsrc(p.b + n0 * ld, (uint32_t)(rows_b * ld));
-  const rsrc_t rbs = make_rsrc(p.b_sf + n0 * lds, (uint32_t)(rows_b * lds));
+  const rsrc_t rbs = SfLayout<SFL>::rsrc(p.b_sf, n0, rows_b, lds);
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r_in = lane & 15, g = lane >> 4;
   // code offsets: rows lane % 8 and 8 + lane % 8 of each 16-row block, bytes
@@ -740,7 +775,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       va[tm][h] = r < rows_a ? (uint32_t)(r * ld + 16 * (lane >> 3)) : 0x80000000u;
     }
     const int r = tm * 16 + r_in;
-    vas[tm] = r < rows_a ? (uint32_t)(r * lds + sw) : 0x80000000u;
+    if constexpr (SFL == 0) vas[tm] = r < rows_a ? (uint32_t)(r * lds + sw) : 0x80000000u;
+    else vas[tm] = r < rows_a ? SfLayout<SFL>::offset(m0, r, g, lds) : 0x80000000u;
   }
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn) {
@@ -750,7 +786,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       vb[tn][h] = r < rows_b ? (uint32_t)(r * ld + 16 * (lane >> 3)) : 0x80000000u;
     }
     const int r = tn * 16 + r_in;
-    vbs[tn] = r < rows_b ? (uint32_t)(r * lds + sw) : 0x80000000u;
+    if constexpr (SFL == 0) vbs[tn] = r < rows_b ? (uint32_t)(r * lds + sw) : 0x80000000u;
+    else vbs[tn] = r < rows_b ? SfLayout<SFL>::offset(n0, r, g, lds) : 0x80000000u;
   }
   // this work-group's K units [u_lo, u_hi): all of K, or split z of S
   const int nu_all = (int)(p.K / C::kUnit);
@@ -769,7 +806,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 #pragma unroll
   for (int u = 0; u < C::D; ++u) {
     const int unit = wave + u * C::KS;
-    kreg_load<C>(R, u, u_lo + unit, unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+    kreg_load<C, SFL>(R, u, u_lo + unit, unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
     __builtin_amdgcn_sched_barrier(0);
   }
   const bool lo8 = (lane & 8) == 0;
@@ -830,7 +867,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       // share registers; no copies that would wait on the load)
       __builtin_amdgcn_sched_barrier(0);
       const int unit = wave + (i0 + u + C::D) * C::KS;
-      kreg_load<C>(R, u, u_lo + unit, unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
+      kreg_load<C, SFL>(R, u, u_lo + unit, unit < nu, ra, ras, rb, rbs, va, vas, vb, vbs);
     }
   }
   // K-group sum: wave w's partial tile at red[w][.], element (tm, tn, lane, j)
@@ -1116,10 +1153,22 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   return pl;
 }
 
+bool plan_reads_tiled_scales(const GemmPlan& plan) { return plan.kind >= 10 && plan.kind <= 13; }
+
 template <class C>
 static void launch_kreg(const GemmPlan& pl, const GemmLaunch& p, hipStream_t stream) {
   const unsigned grid = (unsigned)(pl.tiles_m * pl.tiles_n * pl.splits);
-  hipLaunchKernelGGL(k_gemm_kreg<C>, dim3(grid), dim3(C::kThreads), 0, stream, p);
+  if constexpr (!C::kMx) {
+    if (p.sf_layout == 1) {
+      hipLaunchKernelGGL((k_gemm_kreg<C, 1>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+      return;
+    }
+    if (p.sf_layout == 2) {
+      hipLaunchKernelGGL((k_gemm_kreg<C, 2>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_gemm_kreg<C, 0>), dim3(grid), dim3(C::kThreads), 0, stream, p);
 }
 
 template <class C, bool SPLITK>

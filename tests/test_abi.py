@@ -325,3 +325,29 @@ def test_8x4_layout_error_paths_and_sizes():
     assert L.nvfp4_scales_from_8x4(FAKE, None, 4, 64, None) == 1
     assert L.nvfp4_scales_from_8x4(FAKE, FAKE, -1, 64, None) == 2
     assert L.nvfp4_scales_to_8x4(None, None, 0, 64, None) == 0
+
+
+def test_tiled_scale_gemm_error_paths_and_workspace():
+    L = nv.lib()
+
+    def call(layout, M=16, N=16, K=256, ws=None, wsb=0, asf=FAKE):
+        return L.nvfp4_gemm_sf(FAKE, asf, FAKE, FAKE, None, FAKE, M, N, K, layout, ws, wsb, None)
+
+    assert call(3) == 2 and "sf_layout" in nv.nvfp4_last_error()
+    assert call(-1) == 2
+    assert call(1, K=40) == 2 and call(2, K=128) == 4
+    assert call(1, asf=None) == 1 and call(2, asf=FAKE + 4) == 3
+    assert call(1, M=0) == 0
+    for layout in (0, 1, 2):
+        assert L.nvfp4_gemm_sf_workspace_size(16, 768, 6144, layout) == L.nvfp4_gemm_workspace_size(16, 768, 6144)
+    assert L.nvfp4_gemm_sf_workspace_size(16, 768, 6144, 3) == 0
+    assert L.nvfp4_gemm_sf_workspace_size(16, 768, 200, 1) == 0
+    # a plan that needs linear scales converts both into the workspace, after
+    # the plan's own split-K scratch (256-byte aligned pieces)
+    base = L.nvfp4_gemm_workspace_size(1024, 256, 6144)
+    rup = lambda x: (x + 255) // 256 * 256
+    for layout in (1, 2):
+        need = L.nvfp4_gemm_sf_workspace_size(1024, 256, 6144, layout)
+        assert need == rup(base) + rup(1024 * 384) + rup(256 * 384)
+        assert call(layout, M=1024, N=256, K=6144, ws=FAKE, wsb=need - 1) == 5
+    assert L.nvfp4_gemm_sf_workspace_size(1024, 256, 6144, 0) == base

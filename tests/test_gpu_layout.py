@@ -51,3 +51,42 @@ def test_gemm_on_imported_scales(layout):
     from_t(dev(o_to(bsf)), bsf_t, N, K)
     d = gpu_gemm(dev(a), asf_t, dev(b), bsf_t, scalar(0.5), M, N, K)
     check_gemm(bits(d), a, asf, b, bsf, np.float32(0.5), "imported scales")
+
+
+# nvfp4_gemm_sf: register-tile plans read the tiled scales in place (M <= 128
+# here), every other plan converts them into the workspace first.
+SF_CASES = [(1, 200, 512), (16, 768, 6144), (33, 130, 1024), (64, 2048, 2304), (128, 320, 768),
+            (16, 16384, 1024), (130, 300, 1280), (1000, 768, 2048), (2048, 6144, 512)]
+
+
+@pytest.mark.parametrize("layout", ["128x4", "8x4"])
+@pytest.mark.parametrize("M,N,K", SF_CASES)
+def test_gemm_on_tiled_scales(layout, M, N, K):
+    _, _, _, _, o_to, _ = LAYOUTS[layout]
+    sfl = nv.SF_128x4 if layout == "128x4" else nv.SF_8x4
+    seed = 17 * M + N + K
+    a, b = synth.random_codes(seed, M, K), synth.random_codes(seed + 1, N, K)
+    asf = synth.random_scale_bytes(seed + 2, M, K, lo=0x28, hi=0x48)
+    bsf = synth.random_scale_bytes(seed + 3, N, K, lo=0x28, hi=0x48)
+    plan = nv.nvfp4_gemm_plan(M, N, K)
+    need = nv.nvfp4_gemm_sf_workspace_size(M, N, K, sfl)
+    say("gemm on tiled scales", layout, M, N, K, plan, need)
+    ws = nv.nvfp4_workspace_init(torch.empty(need, dtype=torch.uint8, device="cuda")) if need else None
+    a_t, b_t = dev(a), dev(b)
+    alpha = scalar(0.75)
+    d = torch.full((M, N), 0x7FC1, dtype=torch.int16, device="cuda")
+    nv.nvfp4_gemm_sf(a_t, dev(o_to(asf)), b_t, dev(o_to(bsf)), alpha, d, M, N, K, sfl, ws)
+    # bit for bit the call on linear scales, and within tolerance of the oracle
+    ref = gpu_gemm(a_t, dev(asf), b_t, dev(bsf), alpha, M, N, K)
+    np.testing.assert_array_equal(bits(d), bits(ref), err_msg=f"{layout} {M}x{N}x{K} ({plan})")
+    check_gemm(bits(d), a, asf, b, bsf, np.float32(0.75), f"tiled scales {layout} {M}x{N}x{K}")
+    if ws is not None:   # the workspace serves a second call (counters left at zero)
+        d2 = torch.zeros_like(d)
+        nv.nvfp4_gemm_sf(a_t, dev(o_to(asf)), b_t, dev(o_to(bsf)), alpha, d2, M, N, K, sfl, ws)
+        np.testing.assert_array_equal(bits(d2), bits(d))
+
+
+def test_tiled_scale_cases_reach_both_paths():
+    # host-side: the cases cover plans that read in place and plans that convert
+    plans = [nv.nvfp4_gemm_plan(M, N, K) for M, N, K in SF_CASES]
+    assert any(p.startswith("kreg") for p in plans) and any(not p.startswith("kreg") for p in plans)
