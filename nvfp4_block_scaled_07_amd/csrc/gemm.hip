@@ -944,8 +944,8 @@ typedef Cfg<64, 64, 2, 2, 32, 256, 3, 0, 1, 2, 32> CfgMx64;         // 4 waves x
 // per SIMD): the other four start their LDS reads and MFMAs at once instead
 // of waiting on the memory pipeline too (8192 x 6144 x 6144: 179.6 -> 172.0
 // us, 4096 x 6144 x 6144 on 256x192 tiles: 105.8 -> 98.9 us; bitwise the
-// same).  With no dequantisation the MX tiles' MFMAs are short enough for
-// that wait to show; on the NVFP4 tiles it made no difference or lost.
+// same).  The NVFP4 256-row tiles do the same (gemm_large.hip); on the
+// NVFP4 K-group tile it made no difference.
 typedef Cfg<256, 256, 2, 4, 32, 256, 2, 0, 1, 2, 32, 4> CfgMx256w8;    // 8 waves x 128x64
 typedef Cfg<256, 256, 2, 4, 32, 128, 4, 0, 1, 2, 32> CfgMx256w8s4;     // all waves load, 4 stages of 128
 typedef Cfg<256, 192, 4, 2, 32, 256, 2, 0, 1, 2, 32, 4> CfgMx256x192;  // 8 waves x 64x96, 119 KB
