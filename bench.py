@@ -610,6 +610,18 @@ def other_workloads(nv, torch, dev, stream, synth, quantise, sweep_inputs, call)
                                                  tflops=round(fl / us / 1e6, 2),
                                                  rows_per_expert_max=gi["rows_per_expert_max"],
                                                  algorithmic_bytes=by)
+    # the plain-weight call with both scale tensors in the 8 x 4 tiled layout,
+    # read in place (nvfp4_grouped_gemm_sf; the weights' scales as one
+    # [E * N][K/16] matrix), converted outside the timed region
+    tsa = torch.empty(nv.nvfp4_scales_8x4_size(rows, K), dtype=torch.uint8, device=dev)
+    tsb = torch.empty(nv.nvfp4_scales_8x4_size(E * N, K), dtype=torch.uint8, device=dev)
+    nv.nvfp4_scales_to_8x4(sfa, tsa, rows, K)
+    nv.nvfp4_scales_to_8x4(bsf.view(E * N, K // 16), tsb, E * N, K)
+    us_t = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_sf(qa, tsa, b, tsb, off_t, alpha, d, rows, N, K, E,
+                                                                   nv.SF_8x4), 10)
+    res["grouped_moe_512tok_256exp_top8"]["tiled_8x4_scales"] = dict(
+        us=round(us_t, 2), gbps=round(by / us_t / 1e3, 1), frac_hbm=round(by / us_t / 1e3 / PEAK_HBM_GBPS, 4))
+    del tsa, tsb
     # the same call on weights packed once into the stage-contiguous layout
     # (packing is a one-time weight transform, outside the timed region)
     pb, psf = nv.grouped_pack(b, bsf, N, K, E)

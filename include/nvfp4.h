@@ -335,6 +335,24 @@ nvfp4_status nvfp4_gemm_sf(const uint8_t* a, const uint8_t* a_sf,
 size_t nvfp4_gemm_sf_workspace_size(int64_t M, int64_t N, int64_t K, int32_t sf_layout);
 
 /*
+ * nvfp4_grouped_gemm with its scales in one of the tiled layouts (sf_layout 1
+ * = 128 x 4, 2 = 8 x 4, 0 = linear, then the call is nvfp4_grouped_gemm
+ * without a workspace): a_sf is the tiled form of the [rows][K/16] activation
+ * scales (nvfp4_scales_<layout>_size(rows, K) bytes), b_sf that of the
+ * experts' scales taken as one [E * N][K/16] matrix (row e * N + n;
+ * nvfp4_scales_<layout>_size(E * N, K) bytes).  The register-streamed kernels
+ * read both in place; K must be a multiple of 512 (NVFP4_ERR_UNSUPPORTED
+ * otherwise).  Everything else (offsets, alpha, status, results bit for bit)
+ * is as for nvfp4_grouped_gemm.  For the weights' scales the 8 x 4 layout
+ * also loads fewer cache lines per instruction than the linear one.
+ */
+nvfp4_status nvfp4_grouped_gemm_sf(const uint8_t* a, const uint8_t* a_sf,
+                                   const uint8_t* b, const uint8_t* b_sf,
+                                   const int32_t* offsets, const float* alpha, uint16_t* d,
+                                   int64_t rows, int64_t N, int64_t K, int32_t E, int32_t sf_layout,
+                                   int32_t* status, void* stream);
+
+/*
  * Quantise fp32 x [R][K] to NVFP4 (q uint8 [R][K/2], sf uint8 [R][K/16]).
  * The pages never quantise (their test used random bytes); this follows the
  * block_size 16 and e4m3fn scale format of the pages above with these steps,

@@ -30,6 +30,8 @@ SIGNATURES = {
     "nvfp4_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nvfp4_gemm_sf": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "nvfp4_gemm_sf_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "nvfp4_grouped_gemm_sf": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp,
+                                             _vp]),
     "nvfp4_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "nvfp4_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
                                           _vp, _vp]),
@@ -277,6 +279,21 @@ def nvfp4_gemm_sf(a, a_sf, b, b_sf, alpha, d, M: int, N: int, K: int, sf_layout:
                              _ptr(b, _n(N, K) // 2, "b", f), _ptr(b_sf, _sf_bytes(N, K, sf_layout), "b_sf", f),
                              _ptr(alpha, 4, "alpha", f), _ptr(d, 2 * _n(M, N), "d", f), M, N, K, sf_layout,
                              _ptr(workspace, 0, "workspace", f), _bytes(workspace), _stream(stream))
+    _check(st, f)
+    return d
+
+
+def nvfp4_grouped_gemm_sf(a, a_sf, b, b_sf, offsets, alpha, d, rows: int, N: int, K: int, E: int, sf_layout: int,
+                          status=None, stream=None):
+    """nvfp4_grouped_gemm with a_sf ([rows][K/16]) and b_sf ([E * N][K/16])
+    in the scale layout sf_layout; see include/nvfp4.h.  d is returned."""
+    f = "nvfp4_grouped_gemm_sf"
+    st = lib().nvfp4_grouped_gemm_sf(_ptr(a, _n(rows, K) // 2, "a", f), _ptr(a_sf, _sf_bytes(rows, K, sf_layout), "a_sf", f),
+                                     _ptr(b, _n(E, N, K) // 2, "b", f),
+                                     _ptr(b_sf, _sf_bytes(_n(E, N), K, sf_layout), "b_sf", f),
+                                     _ptr(offsets, 4 * _n(E + 1), "offsets", f), _ptr(alpha, 4 * _n(E), "alpha", f),
+                                     _ptr(d, 2 * _n(rows, N), "d", f), rows, N, K, E, sf_layout,
+                                     _ptr(status, 4, "status", f), _stream(stream))
     _check(st, f)
     return d
 

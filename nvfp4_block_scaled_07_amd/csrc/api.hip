@@ -239,6 +239,37 @@ nvfp4_status nvfp4_grouped_gemm(const uint8_t* a, const uint8_t* a_sf, const uin
   return hip_status(nvfp4::launch_grouped(p, status, (hipStream_t)stream, true), "nvfp4_grouped_gemm launch");
 }
 
+nvfp4_status nvfp4_grouped_gemm_sf(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                                   const int32_t* offsets, const float* alpha, uint16_t* d, int64_t rows, int64_t N,
+                                   int64_t K, int32_t E, int32_t sf_layout, int32_t* status, void* stream) {
+  if (sf_layout < 0 || sf_layout > 2)
+    return fail(NVFP4_ERR_SHAPE, "sf_layout = %d: 0 (linear), 1 (128 x 4) or 2 (8 x 4)", sf_layout);
+  if (sf_layout == 0)
+    return nvfp4_grouped_gemm(a, a_sf, b, b_sf, offsets, alpha, d, rows, N, K, E, nullptr, 0, status, stream);
+  if (rows < 0 || N < 0 || E < 0)
+    return fail(NVFP4_ERR_SHAPE, "rows = %lld, N = %lld, E = %d must be >= 0", (long long)rows, (long long)N, E);
+  nvfp4_status s = check_k(K);
+  if (s != NVFP4_OK) return s;
+  if (K % 512 != 0) return fail(NVFP4_ERR_UNSUPPORTED, "K = %lld: tiled scales need K %% 512 == 0", (long long)K);
+  if (!offsets && E > 0) return fail(NVFP4_ERR_NULL, "offsets must be non-NULL");
+  if (!aligned(offsets, 4) || !aligned(status, 4))
+    return fail(NVFP4_ERR_ALIGN, "offsets and status must be 4-byte aligned");
+  if (E == 0 || N == 0 || rows == 0) {
+    nvfp4::GroupedLaunch p{a, a_sf, b, b_sf, offsets, alpha, d, rows, N, K, E};
+    return hip_status(nvfp4::launch_grouped(p, status, (hipStream_t)stream, false), "nvfp4_grouped_gemm_sf status");
+  }
+  if (!a || !a_sf || !b || !b_sf || !d)
+    return fail(NVFP4_ERR_NULL, "a, a_sf, b, b_sf and d must be non-NULL (alpha and status may be NULL)");
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_sf, 16) || !aligned(b_sf, 16))
+    return fail(NVFP4_ERR_ALIGN, "a, b, a_sf and b_sf must be 16-byte aligned");
+  if (!aligned(d, 4) || !aligned(alpha, 4)) return fail(NVFP4_ERR_ALIGN, "d and alpha must be 4-byte aligned");
+  if (rows > (1ll << 30) || N > (1ll << 30) || K > (1ll << 30) || E > 65535 || (int64_t)E * N > (1ll << 30))
+    return fail(NVFP4_ERR_UNSUPPORTED, "dimensions above 2^30 (or E > 65535) are not supported");
+  nvfp4::GroupedLaunch p{a, a_sf, b, b_sf, offsets, alpha, d, rows, N, K, E};
+  p.sf_layout = sf_layout;
+  return hip_status(nvfp4::launch_grouped(p, status, (hipStream_t)stream, true), "nvfp4_grouped_gemm_sf launch");
+}
+
 size_t nvfp4_grouped_packed_size(int64_t N, int64_t K, int32_t E, size_t* sf_bytes) {
   if (N <= 0 || K <= 0 || E <= 0 || K % 512 || K > (int64_t(1) << 22) || N > (1ll << 30) || E > 65535) {
     if (sf_bytes) *sf_bytes = 0;

@@ -275,6 +275,41 @@ __device__ __forceinline__ void kreg_exchange(uint32_t (&w)[8], bool lo8) {
   }
 }
 
+// Scale layouts the register-streamed kernels can read in place
+// (nvfp4_gemm_sf, nvfp4_grouped_gemm_sf): 0 linear [rows][K/16]; 1 the 128 x
+// 4 tiled layout (512-byte tiles of 128 rows x 4 scale columns, row-major
+// tile order; row r, column c at byte (r % 32) 16 + ((r % 128) / 32) 4 + c %
+// 4); 2 the 8 x 4 one (32-byte tiles of 8 rows x 4 columns; row r, column c
+// at byte (r % 8) 4 + c % 4).  In both tiled layouts the 4 scales of columns
+// 4 j .. 4 j + 3 of a row are one aligned word, the word a lane loads, so
+// only its address changes.
+template <int SFL>
+struct SfLayout {
+  static_assert(SFL >= 0 && SFL <= 2, "scale layout");
+  // bytes between consecutive 256-element units of one row (4 words)
+  static constexpr uint32_t kUnitStep = SFL == 0 ? 16 : (SFL == 1 ? 4 * 512 : 4 * 32);
+  // Rows [r0, r0 + rows_valid) of a scale matrix with lds = K/16 bytes per
+  // row (r0 counts rows from the matrix start, any alignment): a descriptor
+  // bounded by the bytes of the row groups those rows occupy, and the offset
+  // of word j of local row r in unit 0.
+  static __device__ __forceinline__ rsrc_t rsrc(const uint8_t* sf, int64_t r0, int rows_valid, int64_t lds) {
+    if constexpr (SFL == 0) return make_rsrc(sf + r0 * lds, (uint32_t)(rows_valid * lds));
+    else if constexpr (SFL == 1)
+      return make_rsrc(sf + (r0 >> 7) * 128 * lds, (uint32_t)(((r0 & 127) + rows_valid + 127) / 128 * 128 * lds));
+    else return make_rsrc(sf + (r0 >> 3) * 8 * lds, (uint32_t)(((r0 & 7) + rows_valid + 7) / 8 * 8 * lds));
+  }
+  static __device__ __forceinline__ uint32_t offset(int64_t r0, int r, int j, int64_t lds) {
+    if constexpr (SFL == 0) return (uint32_t)(r * lds + 4 * j);
+    else if constexpr (SFL == 1) {
+      const int q = (int)(r0 & 127) + r;
+      return (uint32_t)((q >> 7) * 128 * lds + 512 * j + (q & 31) * 16 + ((q >> 5) & 3) * 4);
+    } else {
+      const int q = (int)(r0 & 7) + r;
+      return (uint32_t)((q >> 3) * 8 * lds + 32 * j + (q & 7) * 4);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Grouped GEMM streaming B through registers.  Every B element is used by
 // exactly one wave, so B skips LDS: each lane loads its own 16-byte code
@@ -325,7 +360,7 @@ struct PackedStream {
   int64_t stride, sstride;
 };
 
-template <class C, int D, bool PACKED, bool FUSED>
+template <class C, int D, bool PACKED, bool FUSED, int SFL>
 __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const PackedStream& ps,
                                         const rsrc_t& rb, const rsrc_t& rbs,
                                         const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
@@ -369,7 +404,7 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
       R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b64(ra, live ? va : kOut, kt * C::RB, 0));
     else
       R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b32(ra, live ? va : kOut, kt * C::RB, 0));
-    R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * C::SB, 0);
+    R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * (SFL == 0 ? C::SB : (int)SfLayout<SFL>::kUnitStep), 0);
   }
 }
 
@@ -484,10 +519,11 @@ __device__ __forceinline__ void gr_fused_a(const u4_t (&ax)[GRegs<C, D>::kAX], u
   }
 }
 
-template <class C, int D, bool PACKED, bool FUSED = false>
+template <class C, int D, bool PACKED, bool FUSED = false, int SFL = 0>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_grouped_reg(
     GroupedLaunch p) {
   static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
+  static_assert(SFL == 0 || (!PACKED && C::BK == 256), "tiled scales: plain weights, one unit per stage");
   static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
   static_assert(C::BM * C::CH <= C::kThreads, "one A chunk per thread");
   static_assert(PACKED || (C::kSub == 2 && C::KG == 4), "whole-line loads pair the two sub-steps of a 256-K stage");
@@ -525,7 +561,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     bs_ld = C::SB;
   } else {
     b_step = C::RB;
-    bs_step = C::SB;
+    bs_step = SFL == 0 ? C::SB : SfLayout<SFL>::kUnitStep;
     bt = p.b + ((int64_t)e * p.N + n0) * ld;
     bst = p.b_sf + ((int64_t)e * p.N + n0) * lds;
     b_bytes = (uint32_t)(b_rows * ld);
@@ -533,7 +569,9 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     b_ld = (uint32_t)ld;
     bs_ld = (uint32_t)lds;
   }
-  const rsrc_t rb = make_rsrc(bt, b_bytes), rbs = make_rsrc(bst, bs_bytes);
+  const rsrc_t rb = make_rsrc(bt, b_bytes);
+  // SFL > 0: the weights' scales are one tiled matrix of E * N rows
+  const rsrc_t rbs = SFL == 0 ? make_rsrc(bst, bs_bytes) : SfLayout<SFL>::rsrc(p.b_sf, (int64_t)e * p.N + n0, b_rows, lds);
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wn = wave % C::WN, r_in = lane % C::MF, g = lane / C::MF;
   // per-lane B offsets (row part included; rows >= b_rows masked out of range)
@@ -551,7 +589,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       } else {
         const int lrow = wn * C::kWN + tn * C::MF + 8 * s + (lane & 7);
         vb[tn][s] = lrow < b_rows ? (uint32_t)(lrow * b_ld + 16 * (lane >> 3)) : 0x80000000u;
-        vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * g) : 0x80000000u;
+        if constexpr (SFL == 0) vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * g) : 0x80000000u;
+        else vbs[tn][s] = row < b_rows ? SfLayout<SFL>::offset((int64_t)e * p.N + n0, row, g, lds) : 0x80000000u;
       }
     }
   }
@@ -582,9 +621,9 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       va = vas = 0x80000000u;
     } else {
       ra = make_rsrc(p.a + mc * ld, (uint32_t)(rows_c * ld));
-      ras = make_rsrc(p.a_sf + mc * lds, (uint32_t)(rows_c * lds));
+      ras = SfLayout<SFL>::rsrc(p.a_sf, mc, rows_c, lds);
       va = ar < rows_c ? (uint32_t)(ar * ld + ac * 16 + ah * (16 / RT::kAP)) : 0x80000000u;
-      vas = ar < rows_c ? (uint32_t)(ar * lds + 4 * (ac >> 1)) : 0x80000000u;
+      vas = ar < rows_c ? SfLayout<SFL>::offset(mc, ar, ac >> 1, lds) : 0x80000000u;
 #pragma unroll
       for (int i = 0; i < RT::kAX; ++i) vax[i] = 0x80000000u;
     }
@@ -594,7 +633,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     __syncthreads();  // the previous row chunk is done with both A tiles
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      gr_load<C, D, PACKED, FUSED>(R, u, u, true, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
+      gr_load<C, D, PACKED, FUSED, SFL>(R, u, u, true, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
     // fused: the A tile of stage s + 1 is written during stage s, after the
@@ -620,7 +659,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
           __builtin_amdgcn_sched_barrier(0);
-          gr_load<C, D, PACKED, FUSED>(R, u, st + D, st + D < n, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras,
+          gr_load<C, D, PACKED, FUSED, SFL>(R, u, st + D, st + D < n, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras,
                                        va, vas, vax);
         }
       }
@@ -677,39 +716,6 @@ template <class C>
 struct KRegs {
   uint32_t aq[C::D][C::TM][8], bq[C::D][C::TN][8];  // two 16-byte code chunks as words
   uint32_t as[C::D][C::TM], bs[C::D][C::TN];        // scale words (4 e4m3)
-};
-
-// Scale layouts the register tiles read in place (nvfp4_gemm_sf): 0 linear
-// [rows][K/16]; 1 the 128 x 4 tiled layout (512-byte tiles of 128 rows x 4
-// scale columns, row-major tile order; row r, column c at byte (r % 32) 16 +
-// ((r % 128) / 32) 4 + c % 4); 2 the 8 x 4 one (32-byte tiles of 8 rows x 4
-// columns; row r, column c at byte (r % 8) 4 + c % 4).  In both tiled
-// layouts the 4 scales of columns 4 j .. 4 j + 3 of a row are one aligned
-// word, the word a lane loads per unit, so only its address changes.
-template <int SFL>
-struct SfLayout {
-  static_assert(SFL >= 0 && SFL <= 2, "scale layout");
-  // bytes between consecutive 256-element units of one row (4 words of 4 scales)
-  static constexpr uint32_t kUnitStep = SFL == 0 ? 16 : (SFL == 1 ? 4 * 512 : 4 * 32);
-  // Scale words of the tile's rows [m0, m0 + rows_valid) of a tensor with lds =
-  // K/16 bytes per row: the descriptor (bounded by the bytes those rows occupy)
-  // and the offset of word g of the tile's row r in unit 0.  m0 is a multiple
-  // of the tile height (16, 32 or 64), so a tile lies in one 128-row group of
-  // the 128 x 4 layout and starts on an 8-row group of the 8 x 4 one.
-  static __device__ __forceinline__ rsrc_t rsrc(const uint8_t* sf, int64_t m0, int rows_valid, int64_t lds) {
-    if constexpr (SFL == 0) return make_rsrc(sf + m0 * lds, (uint32_t)(rows_valid * lds));
-    else if constexpr (SFL == 1) return make_rsrc(sf + (m0 >> 7) * 128 * lds, (uint32_t)(128 * lds));
-    else return make_rsrc(sf + (m0 >> 3) * 8 * lds, (uint32_t)((rows_valid + 7) / 8 * 8 * lds));
-  }
-  static __device__ __forceinline__ uint32_t offset(int64_t m0, int r, int g, int64_t lds) {
-    if constexpr (SFL == 0) return (uint32_t)(r * lds + 4 * g);
-    else if constexpr (SFL == 1) {
-      const int q = (int)(m0 & 127) + r;
-      return (uint32_t)(512 * g + (q & 31) * 16 + ((q >> 5) & 3) * 4);
-    } else {
-      return (uint32_t)((r >> 3) * 8 * lds + 32 * g + (r & 7) * 4);
-    }
-  }
 };
 
 // Loads of unit `unit` into slot u; dead units (past the end of the range)
@@ -1300,6 +1306,22 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
   int gk = (p.K / 256) % 2 == 0 ? (tall_experts(p) ? 3 : 2) : 1;
   grouped_forced(&gk);
   if (gk >= 2 && (p.K / 256) % 2) gk = 1;
+  if (p.sf_layout != 0) {
+    // tiled scales (K % 512 == 0, checked by the API): the register kernels
+    if (gk < 2) gk = 2;
+    const bool tall = gk == 3;
+    const unsigned bn = tall ? CfgGroupedReg64::BN : CfgGroupedReg::BN;
+    const dim3 grid((unsigned)((p.N + bn - 1) / bn) * (unsigned)p.E);
+    if (tall && p.sf_layout == 1)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false, false, 1>), grid, dim3(CfgGroupedReg64::kThreads), 0, stream, p);
+    else if (tall)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false, false, 2>), grid, dim3(CfgGroupedReg64::kThreads), 0, stream, p);
+    else if (p.sf_layout == 1)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, false, false, 1>), grid, dim3(CfgGroupedReg::kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, false, false, 2>), grid, dim3(CfgGroupedReg::kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   if (gk == 0) {
     const unsigned tiles_n = (unsigned)((p.N + CfgGrouped::BN - 1) / CfgGrouped::BN);
     hipLaunchKernelGGL(k_grouped<CfgGrouped>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGrouped::kThreads), 0, stream,

@@ -41,6 +41,10 @@ struct GroupedLaunch {
   const int32_t* row_token;
   const float* a_gs;
   int64_t T;
+  // Scale layout of a_sf ([rows][K/16]) and b_sf (one [E * N][K/16] matrix):
+  // 0 linear, 1 the 128 x 4 and 2 the 8 x 4 tiled layout (register kernels
+  // only, K % 512 == 0)
+  int sf_layout;
 };
 
 struct GemmPlan {

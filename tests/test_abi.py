@@ -351,3 +351,17 @@ def test_tiled_scale_gemm_error_paths_and_workspace():
         assert need == rup(base) + rup(1024 * 384) + rup(256 * 384)
         assert call(layout, M=1024, N=256, K=6144, ws=FAKE, wsb=need - 1) == 5
     assert L.nvfp4_gemm_sf_workspace_size(1024, 256, 6144, 0) == base
+
+
+def test_tiled_scale_grouped_error_paths():
+    L = nv.lib()
+
+    def call(layout, rows=64, N=64, K=512, E=2, off=FAKE, asf=FAKE):
+        return L.nvfp4_grouped_gemm_sf(FAKE, asf, FAKE, FAKE, off, None, FAKE, rows, N, K, E, layout, None, None)
+
+    assert call(3) == 2 and "sf_layout" in nv.nvfp4_last_error()
+    assert call(1, K=256) == 4 and "512" in nv.nvfp4_last_error()
+    assert call(2, K=40) == 2
+    assert call(1, off=None) == 1
+    assert call(2, asf=None) == 1 and call(2, asf=FAKE + 4) == 3
+    assert call(1, rows=0) == 0

@@ -156,3 +156,34 @@ def test_packed_weights_layout_and_gemm(kind, gplan, force_plan):
     # same bits as the unpacked grouped kernel (same arithmetic, same order)
     d2, _ = _grouped(dev(a), dev(asf), b_t, bsf_t, dev(off), dev(alpha), rows, N, K, E)
     np.testing.assert_array_equal(bits(d2), db)
+
+
+# nvfp4_grouped_gemm_sf: activation and weight scales in a tiled layout (the
+# weights' scales as one [E * N][K/16] matrix), read in place.  N = 300 puts
+# experts at rows that are not multiples of 8 or 128 of that matrix.
+@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("gplan", [-1, 2, 3])
+@pytest.mark.parametrize("kind,N,K", [("alternate", 300, 1024), ([0, 0, 5, 5, 70, 70, 71, 200, 250], 192, 512),
+                                      ([0, 40, 90, 150, 200, 250, 251, 252, 300], 256, 1536),
+                                      ("ones", 130, 512)])
+def test_grouped_gemm_on_tiled_scales(layout, gplan, kind, N, K, force_plan):
+    # gplan: the automatic kernel, or the 32-row (2) or 64-row (3) register kernel forced
+    rows, E = 300, 8
+    force_plan(nv.FAMILY_GROUPED, gplan)
+    off, a, asf, b, bsf, alpha = _small_problem(kind, rows, E, N, K, seed=N + K)
+    to = o.scales_to_128x4 if layout == 1 else o.scales_to_8x4
+    a_t, b_t, off_t, al_t = dev(a), dev(b), dev(off), dev(alpha)
+    say("grouped tiled scales", layout, kind, N, K)
+    d = torch.full((rows, N), SENTINEL, dtype=torch.int16, device="cuda")
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    nv.nvfp4_grouped_gemm_sf(a_t, dev(to(asf)), b_t, dev(to(bsf.reshape(E * N, K // 16))), off_t, al_t, d,
+                             rows, N, K, E, layout, st)
+    assert int(host(st)[0]) == 0
+    ref, _ = _grouped(a_t, dev(asf), b_t, dev(bsf), off_t, al_t, rows, N, K, E)
+    np.testing.assert_array_equal(bits(d), bits(ref))
+    db = bits(d)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            check_gemm(db[lo:hi], a[lo:hi], asf[lo:hi], b[e], bsf[e], alpha[e], f"tiled {layout} expert {e}")
+    assert (db[int(off[-1]):] == SENTINEL).all()
