@@ -309,9 +309,9 @@ nvfp4_status nvfp4_scales_to_8x4(const uint8_t* sf, uint8_t* tiled, int64_t rows
 nvfp4_status nvfp4_scales_from_8x4(const uint8_t* tiled, uint8_t* sf, int64_t rows, int64_t K, void* stream);
 
 /*
- * nvfp4_gemm with both scale tensors in one of the tiled layouts above, the
- * switch that use_8x4_sf_layout is in the mm_fp4 signature ("The Art of
- * Reading the Manual", section "The Message"): sf_layout 1 = the 128 x 4
+ * nvfp4_gemm with both scale tensors in one of the tiled layouts above (the
+ * counterpart of the use_8x4_sf_layout switch of the mm_fp4 signature, "The
+ * Art of Reading the Manual", section "The Message"): sf_layout 1 = the 128 x 4
  * layout of nvfp4_scales_to_128x4, 2 = the 8 x 4 layout of
  * nvfp4_scales_to_8x4, 0 = linear (then the call is nvfp4_gemm).  a_sf holds
  * the tiled bytes of the M x K operand (nvfp4_scales_128x4_size(M, K) or
