@@ -316,10 +316,11 @@ nvfp4_status nvfp4_scales_from_8x4(const uint8_t* tiled, uint8_t* sf, int64_t ro
  * nvfp4_scales_to_8x4, 0 = linear (then the call is nvfp4_gemm).  a_sf holds
  * the tiled bytes of the M x K operand (nvfp4_scales_128x4_size(M, K) or
  * nvfp4_scales_8x4_size(M, K)), b_sf those of the N x K operand; padding
- * bytes are not read.  The plans of small M (the register tiles, M <= 128 at
- * most widths) read the tiled scales in place.  Every other plan first
- * writes linear copies of both into the workspace (two conversion launches
- * on stream, then the GEMM), so the workspace must hold
+ * bytes are not read.  Every automatic plan reads 8 x 4 scales in place, and
+ * the plans of small M (the register tiles, M <= 128 at most widths) read
+ * 128 x 4 scales in place too; the other plans first write linear copies of
+ * 128 x 4 scales into the workspace (two conversion launches on stream, then
+ * the GEMM).  The workspace must hold
  * nvfp4_gemm_sf_workspace_size(M, N, K, sf_layout) bytes, 256-byte aligned,
  * zero-filled once before first use as for nvfp4_gemm.  Everything else
  * (arguments, alignment, results bit for bit, errors) is as for nvfp4_gemm;

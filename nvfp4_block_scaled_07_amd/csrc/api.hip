@@ -52,9 +52,9 @@ nvfp4_status check_k(int64_t K) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Whether nvfp4_gemm_sf converts the tiled scales of this plan into linear
-// copies first (every plan but the register tiles, which read them in place).
+// copies first (the plans that cannot read the layout in place).
 bool converts_scales(const nvfp4::GemmPlan& plan, int32_t sf_layout) {
-  return sf_layout != 0 && !nvfp4::plan_reads_tiled_scales(plan);
+  return sf_layout != 0 && !nvfp4::plan_reads_tiled_scales(plan, sf_layout);
 }
 
 // Workspace of a GEMM call: the plan's own (split-K counters and partial

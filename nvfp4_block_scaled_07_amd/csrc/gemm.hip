@@ -941,6 +941,9 @@ typedef KCfg<64, 32, 4, 2, 2, 1> MxReg64x32;
 // 256 K per stage (each row's codes one 128-byte line), 2 stages; the
 // 256x256 and 256x192 tiles of this kind are in gemm_large.hip
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2> CfgTile128k256;    // 4 waves of 64x64
+// the same tiles on scales in the 8 x 4 tiled layout (nvfp4_gemm_sf)
+typedef Cfg<64, 64, 1, 1, 32, 256, 2, 0, 4, 4, 16, 0, 2> CfgTile64k4Sf8;
+typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 16, 0, 2> CfgTile128k256Sf8;
 // MXFP4 tiles (E8M0 scale per 32 elements, scaled FP4 MFMA)
 typedef Cfg<256, 256, 2, 2, 32, 256, 2, 0, 1, 1, 32> CfgMx256;      // 4 waves x 128x128, 136 KB LDS
 typedef Cfg<128, 128, 2, 2, 32, 256, 2, 0, 1, 2, 32, 2> CfgMx128;   // 4 waves x 64x64, 68 KB (split-K), waves 0-1 load
@@ -1159,7 +1162,10 @@ GemmPlan choose_plan(int64_t M, int64_t N, int64_t K) {
   return pl;
 }
 
-bool plan_reads_tiled_scales(const GemmPlan& plan) { return plan.kind >= 10 && plan.kind <= 13; }
+bool plan_reads_tiled_scales(const GemmPlan& plan, int sf_layout) {
+  if (plan.kind >= 10 && plan.kind <= 13) return true;  // register tiles: both layouts
+  return sf_layout == 2 && (plan.kind == 9 || plan.kind == 14 || plan.kind == 15 || plan.kind == 16);
+}
 
 template <class C>
 static void launch_kreg(const GemmPlan& pl, const GemmLaunch& p, hipStream_t stream) {
@@ -1188,6 +1194,13 @@ hipError_t launch_gemm(const GemmPlan& pl, GemmLaunch p, hipStream_t stream) {
   p.tiles_n = pl.tiles_n;
   p.splits = pl.splits;
   p.group_m = pl.group_m;
+  if (p.sf_layout == 2 && pl.kind != 10 && pl.kind != 11 && pl.kind != 12 && pl.kind != 13) {
+    // 8 x 4 scales read by the LDS tiles (plan_reads_tiled_scales)
+    if (pl.kind == 9) launch_one<CfgTile64k4Sf8, true>(pl, p, stream);
+    else if (pl.kind == 15) launch_one<CfgTile128k256Sf8, true>(pl, p, stream);
+    else launch_large_tile(pl.kind, p, (unsigned)(pl.tiles_m * pl.tiles_n), stream);
+    return hipGetLastError();
+  }
   switch (pl.kind) {
     case 0: launch_one<CfgTile256, false>(pl, p, stream); break;  // plan keeps splits == 1
     case 1: launch_one<CfgTile128, true>(pl, p, stream); break;

@@ -56,8 +56,14 @@ struct Mfma<16> {
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int MF_, int BK_, int STAGES_, int IL_ = 0, int KS_ = 1,
-          int OCC_ = 1, int SBLK_ = 16, int DW_ = 0>
+          int OCC_ = 1, int SBLK_ = 16, int DW_ = 0, int SFL_ = 0>
 struct Cfg {
+  // SFL 2: the scales are in the 8 x 4 tiled layout (32-byte tiles of 8 rows
+  // x 4 scale columns, row r and column c at byte (r % 8) 4 + c % 4, tiles
+  // row-major).  One stage of 8 rows is then one run of 8 SB bytes, word-major
+  // ([column / 4][row % 8][4 bytes]), and the stage is staged in LDS as it is
+  // stored; 0: linear [rows][K/16].
+  static constexpr int SFL = SFL_;
   // SBLK: elements per scale: 16 (NVFP4, e4m3 scales, f16 MFMA after
   // dequantisation) or 32 (MXFP4, E8M0 scales, scaled FP4 MFMA)
   static constexpr int SBLK = SBLK_;
@@ -95,6 +101,8 @@ struct Cfg {
   static_assert(KS == 1 || KS == 2 || KS == 4, "K-groups");
   static_assert(kSub % KS == 0, "sub-steps per K-group");
   static_assert(SBLK == 16 || (SBLK == 32 && MF == 32 && IL == 0), "MX tiles use the 32x32x64 scaled MFMA");
+  static_assert(SFL == 0 || (SFL == 2 && SBLK == 16 && BM % 8 == 0 && BN % 8 == 0 && MF % 8 == 0 && KG * KS % 2 == 0),
+                "8 x 4 scales: NVFP4 tiles of whole 8-row groups");
   typedef typename Mfma<MF>::Acc Acc;
 };
 
@@ -221,8 +229,9 @@ struct StageDma {
   static constexpr int SV = C::SB == 16 ? 16 : 4;
   typedef DmaShape<C::BM, C::RB, 16> A;
   typedef DmaShape<C::BN, C::RB, 16> B;
-  typedef DmaShape<C::BM, C::SB, SV> AS;
-  typedef DmaShape<C::BN, C::SB, SV> BS;
+  // 8 x 4 scales: each 8-row group's stage is one row of 8 SB bytes
+  typedef typename std::conditional<C::SFL == 2, DmaShape<C::BM / 8, 8 * C::SB, 16>, DmaShape<C::BM, C::SB, SV>>::type AS;
+  typedef typename std::conditional<C::SFL == 2, DmaShape<C::BN / 8, 8 * C::SB, 16>, DmaShape<C::BN, C::SB, SV>>::type BS;
   static constexpr int kTotal = A::kInst + B::kInst + AS::kInst + BS::kInst;
   // Every wave that issues loads issues at least this many per stage.  A's
   // code instructions come first and may be skipped (rows an expert does not
@@ -240,10 +249,19 @@ __device__ __forceinline__ void issue_stage(Smem<C>& sm, int buf, const Operand&
   if constexpr (U) wave = wave < W ? wave : -1;
   dma_tile<C::BM, C::RB, 16, C::MF, W, 0, U>(sm.a[buf], A.data, A.ld, A.rows, kt * C::RB, wave, lane, a_rows_dma);
   dma_tile<C::BN, C::RB, 16, C::MF, W, D::A::kInst, U>(sm.b[buf], B.data, B.ld, B.rows, kt * C::RB, wave, lane);
-  dma_tile<C::BM, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst, U>(sm.asf[buf], A.sf, A.lds, A.rows,
-                                                                        kt * C::SB, wave, lane);
-  dma_tile<C::BN, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst, U>(sm.bsf[buf], B.sf, B.lds,
-                                                                                       B.rows, kt * C::SB, wave, lane);
+  if constexpr (C::SFL == 2) {
+    // the operand's scale pointer is its first row's group (rows start on a
+    // group); groups past the last row are padding of the tiled matrix
+    dma_tile<C::BM / 8, 8 * C::SB, 16, 0, W, D::A::kInst + D::B::kInst, U>(sm.asf[buf], A.sf, 8 * A.lds,
+                                                                            (A.rows + 7) / 8, kt * 8 * C::SB, wave, lane);
+    dma_tile<C::BN / 8, 8 * C::SB, 16, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst, U>(
+        sm.bsf[buf], B.sf, 8 * B.lds, (B.rows + 7) / 8, kt * 8 * C::SB, wave, lane);
+  } else {
+    dma_tile<C::BM, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst, U>(sm.asf[buf], A.sf, A.lds, A.rows,
+                                                                          kt * C::SB, wave, lane);
+    dma_tile<C::BN, C::SB, D::SV, 0, W, D::A::kInst + D::B::kInst + D::AS::kInst, U>(sm.bsf[buf], B.sf, B.lds,
+                                                                                         B.rows, kt * C::SB, wave, lane);
+  }
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then a work-group barrier.  The empty asm
@@ -356,8 +374,15 @@ __device__ __forceinline__ ReadAddr<C> read_addr(const Smem<C>& sm) {
   // chunk c's scales: NVFP4 bytes 2c and 2c + 1 (blocks of 16), MXFP4 byte c
   constexpr int kScalePerChunk = 32 / C::SBLK;
   const int c0 = C::KG * kgrp + g;
-  ra.as = lds_addr(sm.asf[0]) + ra_row * C::SB + kScalePerChunk * c0;
-  ra.bs = lds_addr(sm.bsf[0]) + rb_row * C::SB + kScalePerChunk * c0;
+  if constexpr (C::SFL == 2) {
+    // chunk c's two scales: columns 2c, 2c + 1, in word c / 2 of the group's run
+    const int word = (c0 >> 1) * 32 + 2 * (c0 & 1);
+    ra.as = lds_addr(sm.asf[0]) + (ra_row >> 3) * 8 * C::SB + (ra_row & 7) * 4 + word;
+    ra.bs = lds_addr(sm.bsf[0]) + (rb_row >> 3) * 8 * C::SB + (rb_row & 7) * 4 + word;
+  } else {
+    ra.as = lds_addr(sm.asf[0]) + ra_row * C::SB + kScalePerChunk * c0;
+    ra.bs = lds_addr(sm.bsf[0]) + rb_row * C::SB + kScalePerChunk * c0;
+  }
   pin(ra.as);
   pin(ra.bs);
   return ra;
@@ -432,7 +457,8 @@ __device__ __forceinline__ void compute_stage(const Smem<C>& sm, const ReadAddr<
     compute_stage_mx<C, BUF>(ra, acc);
     return;
   }
-  constexpr int kScaleStep = 2 * C::KG * C::KS;  // scale bytes between a K-group's sub-steps
+  // scale bytes between a K-group's sub-steps (KG KS chunks: 2 KG KS columns)
+  constexpr int kScaleStep = C::SFL == 2 ? (C::KG * C::KS / 2) * 32 : 2 * C::KG * C::KS;
 #pragma unroll
   for (int ss = 0; ss < ReadAddr<C>::kS; ++ss) {
     u4_t ac[C::TM], bc[C::TN];

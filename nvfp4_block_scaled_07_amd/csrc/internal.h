@@ -19,7 +19,7 @@ struct GemmLaunch {
   int splits;
   int group_m;
   // Scale layout of a_sf and b_sf: 0 linear [rows][K/16]; 1 and 2 the 128 x 4
-  // and 8 x 4 tiled layouts, read in place by the register-tile plans only
+  // and 8 x 4 tiled layouts, for the plans that read them in place
   // (plan_reads_tiled_scales).
   int sf_layout;
 };
@@ -62,9 +62,10 @@ void set_forced_plan(int family, int kind, int splits);
 
 GemmPlan choose_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmPlan& plan, GemmLaunch p, hipStream_t stream);
-// Whether an NVFP4 plan reads tiled scale layouts in place (its kernels are
-// the register tiles); the others need linear scales.
-bool plan_reads_tiled_scales(const GemmPlan& plan);
+// Whether an NVFP4 plan reads scales in tiled layout sf_layout in place: the
+// register tiles read both layouts, the automatic LDS tiles the 8 x 4 one;
+// the others need linear scales.
+bool plan_reads_tiled_scales(const GemmPlan& plan, int sf_layout);
 // The unsplit 256x256 (plan kind 14) and 256x192 (kind 16) NVFP4 tiles, built
 // in their own source with another instruction schedule; p carries the plan's
 // tile counts, grid = their product.

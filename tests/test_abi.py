@@ -342,14 +342,14 @@ def test_tiled_scale_gemm_error_paths_and_workspace():
         assert L.nvfp4_gemm_sf_workspace_size(16, 768, 6144, layout) == L.nvfp4_gemm_workspace_size(16, 768, 6144)
     assert L.nvfp4_gemm_sf_workspace_size(16, 768, 6144, 3) == 0
     assert L.nvfp4_gemm_sf_workspace_size(16, 768, 200, 1) == 0
-    # a plan that needs linear scales converts both into the workspace, after
-    # the plan's own split-K scratch (256-byte aligned pieces)
+    # an LDS plan reads 8 x 4 scales in place but converts 128 x 4 ones into
+    # the workspace, after the plan's own split-K scratch (256-byte aligned)
     base = L.nvfp4_gemm_workspace_size(1024, 256, 6144)
     rup = lambda x: (x + 255) // 256 * 256
-    for layout in (1, 2):
-        need = L.nvfp4_gemm_sf_workspace_size(1024, 256, 6144, layout)
-        assert need == rup(base) + rup(1024 * 384) + rup(256 * 384)
-        assert call(layout, M=1024, N=256, K=6144, ws=FAKE, wsb=need - 1) == 5
+    need = L.nvfp4_gemm_sf_workspace_size(1024, 256, 6144, 1)
+    assert need == rup(base) + rup(1024 * 384) + rup(256 * 384)
+    assert call(1, M=1024, N=256, K=6144, ws=FAKE, wsb=need - 1) == 5
+    assert L.nvfp4_gemm_sf_workspace_size(1024, 256, 6144, 2) == base
     assert L.nvfp4_gemm_sf_workspace_size(1024, 256, 6144, 0) == base
 
 
