@@ -348,8 +348,12 @@ struct GRegs {
 // the compiler can count outstanding loads exactly); a dead stage (live ==
 // false, past the end of K) uses out-of-range offsets, which return zero
 // without a memory access.  Unpacked weights (whole-line loads) need one
-// scale word per 16-row block; packed weights hold a lane's four scale words
-// (both row blocks, both sub-steps) in one 16-byte chunk.
+// scale word per 16-row block and stage: with linear scales the even slots
+// load the words of two stages at once (8 bytes per lane, 32 of each row), so
+// a 16-row block's scale load touches its 16 rows' lines once per two stages
+// instead of once per stage; tiled scales take one word per stage (two lines
+// per block in the 8 x 4 layout).  Packed weights hold a lane's four scale
+// words (both row blocks, both sub-steps) in one 16-byte chunk.
 // Packed weights: stage kt of a slab is the block at base + kt * stride
 // (codes) and sbase + kt * sstride (scales); the buffer resource of each
 // stage is formed from the 64-bit address, so no 32-bit offset limits the
@@ -388,8 +392,20 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
     for (int s = 0; s < C::kSub; ++s) {
       R.bq[u][tn][s] = __builtin_bit_cast(
           u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbk, live ? vb[tn][s] : kOut, bo, 0));
-      if (!PACKED && s == 0)
-        R.bs[u][tn][0] = __builtin_amdgcn_raw_buffer_load_b32(rbsk, live ? vbs[tn][0] : kOut, bso, 0);
+      if (!PACKED && s == 0) {
+        if constexpr (SFL == 0) {
+          // linear scales: an even slot loads the words of two stages (u odd
+          // loads none), spread over the lane rows as gr_compute expects
+          if (u % 2 == 0) {
+            const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rbsk, live ? vbs[tn][0] : kOut,
+                                                                                         bso, 0));
+            R.bs[u][tn][0] = w[0];
+            R.bs[u][tn][1] = w[1];
+          }
+        } else {
+          R.bs[u][tn][0] = __builtin_amdgcn_raw_buffer_load_b32(rbsk, live ? vbs[tn][0] : kOut, bso, 0);
+        }
+      }
     }
   if constexpr (PACKED) {
     const u4_t w = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbsk, live ? vbs[0][0] : kOut,
@@ -447,9 +463,25 @@ __device__ __forceinline__ void gr_dequant_a(const GRegs<C, D>& R, int u, uint16
 // the B fragments of register slot u (whole-line loads are first put into
 // MFMA layout by the DPP exchange) dequantised and multiplied with the f16 A
 // tile af.
-template <class C, int D, bool PACKED>
+template <class C, int D, bool PACKED, int SFL>
 __device__ __forceinline__ void gr_compute(GRegs<C, D>& R, int u, const uint16_t* af,
                                            typename C::Acc (&acc)[C::TM][C::TN], int r_in, int g, bool lo8) {
+  if constexpr (!PACKED && SFL == 0) {
+    // linear scales of stages kt (this slot) and kt + 1 (the next): lane row
+    // g (lanes 16 g .. 16 g + 15) loaded the 8 bytes at 8 ((g & 1) 2 + g / 2)
+    // of the two stages' 32, so rows 0 and 2 hold words 0, 1 and 2, 3 of
+    // stage kt and rows 1 and 3 those of stage kt + 1.  Swapping the odd rows
+    // of the first word with the even rows of the second leaves word g of
+    // stage kt in the first and word g of stage kt + 1 in the second.
+    if (u % 2 == 0) {
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const auto w = __builtin_amdgcn_permlane16_swap(R.bs[u][tn][0], R.bs[u][tn][1], false, false);
+        R.bs[u][tn][0] = w[0];
+        R.bs[u + 1][tn][0] = w[1];
+      }
+    }
+  }
   if constexpr (!PACKED) {
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
@@ -589,7 +621,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       } else {
         const int lrow = wn * C::kWN + tn * C::MF + 8 * s + (lane & 7);
         vb[tn][s] = lrow < b_rows ? (uint32_t)(lrow * b_ld + 16 * (lane >> 3)) : 0x80000000u;
-        if constexpr (SFL == 0) vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 4 * g) : 0x80000000u;
+        // linear: the 8 bytes this lane row loads of each pair of stages
+        if constexpr (SFL == 0) vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 8 * (((g & 1) << 1) | (g >> 1))) : 0x80000000u;
         else vbs[tn][s] = row < b_rows ? SfLayout<SFL>::offset((int64_t)e * p.N + n0, row, g, lds) : 0x80000000u;
       }
     }
@@ -651,7 +684,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // LDS-only barrier: a __syncthreads() fence would also wait for the
           // prefetched loads (loads and stores share one counter)
           lds_barrier();
-          gr_compute<C, D, PACKED>(R, u, af, acc, r_in, g, lo8);
+          gr_compute<C, D, PACKED, SFL>(R, u, af, acc, r_in, g, lo8);
           if constexpr (FUSED) {
             __builtin_amdgcn_sched_barrier(0);
             if (st + 1 < n) gr_fused_a<C, D>(R.ax[(u + 1) % D], sm.af[(u + 1) & 1], gs_a, wave, lane);
@@ -961,7 +994,7 @@ typedef Cfg<256, 192, 4, 2, 32, 256, 2, 0, 1, 2, 32, 4> CfgMx256x192;  // 8 wave
 typedef Cfg<64, 256, 1, 8, 16, 256, 3> CfgGrouped;      // MoE experts: <= 64 rows per pass
 static_assert(CfgGrouped::WM == 1, "grouped row-block count assumes one wave row");
 typedef Cfg<32, 256, 1, 8, 16, 256, 3> CfgGroupedA16;   // MoE experts, shared f16 A: <= 32 rows per pass
-typedef Cfg<32, 256, 1, 8, 16, 256, 2> CfgGroupedReg;    // MoE experts, B streamed through registers
+typedef Cfg<32, 256, 1, 8, 16, 256, 2, 0, 1, 4> CfgGroupedReg;  // MoE experts, B streamed through registers: 2 WGs per CU
 typedef Cfg<64, 256, 1, 8, 16, 256, 2, 0, 1, 2> CfgGroupedReg64;  // the same with 64-row passes over each expert
 typedef Cfg<32, 256, 1, 8, 16, 256, 2, 0, 1, 4> CfgGroupedRegF;  // 32-row passes quantising A on load: 2 WGs per CU
 
