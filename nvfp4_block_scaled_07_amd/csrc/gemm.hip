@@ -336,6 +336,8 @@ struct GRegs {
   typedef typename std::conditional<kAP == 1, u4_t, typename std::conditional<kAP == 2, u2_t, u1_t>::type>::type AQ;
   u4_t bq[D][C::TN][C::kSub];
   uint32_t bs[D][C::TN][C::kSub];
+  // linear scales four stages at a time: the words of stages 4 k .. 4 k + 3
+  uint32_t bsq[C::TN][4];
   AQ aq[D];
   uint32_t as[D];
   // fused quantisation: kAX 16-byte chunks of bf16 activations per lane and
@@ -348,11 +350,12 @@ struct GRegs {
 // the compiler can count outstanding loads exactly); a dead stage (live ==
 // false, past the end of K) uses out-of-range offsets, which return zero
 // without a memory access.  Unpacked weights (whole-line loads) need one
-// scale word per 16-row block and stage: with linear scales the even slots
-// load the words of two stages at once (8 bytes per lane, 32 of each row), so
-// a 16-row block's scale load touches its 16 rows' lines once per two stages
-// instead of once per stage; tiled scales take one word per stage (two lines
-// per block in the 8 x 4 layout).  Packed weights hold a lane's four scale
+// scale word per 16-row block and stage: with linear scales the kernel loads
+// the words of four stages at once (gr_load_sq, when 4 divides the stage
+// count) or the even slots those of two (8 bytes per lane, 32 of each row),
+// so a 16-row block's scale load touches its 16 rows' lines once per four or
+// two stages instead of once per stage; tiled scales take one word per stage
+// (two lines per block in the 8 x 4 layout).  Packed weights hold a lane's four scale
 // words (both row blocks, both sub-steps) in one 16-byte chunk.
 // Packed weights: stage kt of a slab is the block at base + kt * stride
 // (codes) and sbase + kt * sstride (scales); the buffer resource of each
@@ -364,7 +367,7 @@ struct PackedStream {
   int64_t stride, sstride;
 };
 
-template <class C, int D, bool PACKED, bool FUSED, int SFL>
+template <class C, int D, bool PACKED, bool FUSED, int SFL, int SG>
 __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live, const PackedStream& ps,
                                         const rsrc_t& rb, const rsrc_t& rbs,
                                         const uint32_t (&vb)[C::TN][C::kSub], const uint32_t (&vbs)[C::TN][C::kSub],
@@ -396,7 +399,7 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
         if constexpr (SFL == 0) {
           // linear scales: an even slot loads the words of two stages (u odd
           // loads none), spread over the lane rows as gr_compute expects
-          if (u % 2 == 0) {
+          if (SG == 2 && u % 2 == 0) {
             const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rbsk, live ? vbs[tn][0] : kOut,
                                                                                          bso, 0));
             R.bs[u][tn][0] = w[0];
@@ -421,6 +424,44 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
     else
       R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b32(ra, live ? va : kOut, kt * C::RB, 0));
     R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * (SFL == 0 ? C::SB : (int)SfLayout<SFL>::kUnitStep), 0);
+  }
+}
+
+// Linear B scales four stages at a time (stages kt .. kt + 3, kt % 4 == 0):
+// lane row g (lanes 16 g .. 16 g + 15) loads the 16 bytes of stage kt + g of
+// its row, so the instruction touches each of a 16-row block's lines once per
+// four stages.  gr_split_sq then leaves word g of stage kt + s in bsq[tn][s]
+// (a 4 x 4 transpose over lane rows and registers: lane-row halves swapped
+// with permlane32, then single lane rows with permlane16).
+template <class C, int D>
+__device__ __forceinline__ void gr_load_sq(GRegs<C, D>& R, int kt, bool live, const rsrc_t& rbs,
+                                           const uint32_t (&vbs)[C::TN][C::kSub], uint32_t bs_step) {
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const u4_t w = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbs, live ? vbs[tn][0] : 0x80000000u,
+                                                                                  kt * bs_step, 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R.bsq[tn][j] = w[j];
+  }
+}
+
+template <class C, int D>
+__device__ __forceinline__ void gr_split_sq(GRegs<C, D>& R) {
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    uint32_t* q = R.bsq[tn];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto w = __builtin_amdgcn_permlane32_swap(q[j], q[j + 2], false, false);
+      q[j] = w[0];
+      q[j + 2] = w[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const auto w = __builtin_amdgcn_permlane16_swap(q[j], q[j + 1], false, false);
+      q[j] = w[0];
+      q[j + 1] = w[1];
+    }
   }
 }
 
@@ -463,7 +504,7 @@ __device__ __forceinline__ void gr_dequant_a(const GRegs<C, D>& R, int u, uint16
 // the B fragments of register slot u (whole-line loads are first put into
 // MFMA layout by the DPP exchange) dequantised and multiplied with the f16 A
 // tile af.
-template <class C, int D, bool PACKED, int SFL>
+template <class C, int D, bool PACKED, int SFL, int SG>
 __device__ __forceinline__ void gr_compute(GRegs<C, D>& R, int u, const uint16_t* af,
                                            typename C::Acc (&acc)[C::TM][C::TN], int r_in, int g, bool lo8) {
   if constexpr (!PACKED && SFL == 0) {
@@ -473,7 +514,7 @@ __device__ __forceinline__ void gr_compute(GRegs<C, D>& R, int u, const uint16_t
     // stage kt and rows 1 and 3 those of stage kt + 1.  Swapping the odd rows
     // of the first word with the even rows of the second leaves word g of
     // stage kt in the first and word g of stage kt + 1 in the second.
-    if (u % 2 == 0) {
+    if (SG == 2 && u % 2 == 0) {
 #pragma unroll
       for (int tn = 0; tn < C::TN; ++tn) {
         const auto w = __builtin_amdgcn_permlane16_swap(R.bs[u][tn][0], R.bs[u][tn][1], false, false);
@@ -551,11 +592,16 @@ __device__ __forceinline__ void gr_fused_a(const u4_t (&ax)[GRegs<C, D>::kAX], u
   }
 }
 
-template <class C, int D, bool PACKED, bool FUSED = false, int SFL = 0>
+template <class C, int D, bool PACKED, bool FUSED = false, int SFL = 0, int SG = 2>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_grouped_reg(
     GroupedLaunch p) {
   static_assert(C::MF == 16 && C::WM == 1 && C::KS == 1, "grouped layout");
   static_assert(SFL == 0 || (!PACKED && C::BK == 256), "tiled scales: plain weights, one unit per stage");
+  // SG: stages per linear B scale load (plain weights): 2, or 4 when 4
+  // divides the stage count (the launcher's choice)
+  constexpr bool kQuad = SG == 4 && SFL == 0 && !PACKED;
+  static_assert(SG == 2 || (kQuad && D == 2), "scale groups of four: plain weights, linear scales, two slots");
+  constexpr int G = kQuad ? 4 : D;  // stages per loop iteration
   static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
   static_assert(C::BM * C::CH <= C::kThreads, "one A chunk per thread");
   static_assert(PACKED || (C::kSub == 2 && C::KG == 4), "whole-line loads pair the two sub-steps of a 256-K stage");
@@ -621,8 +667,9 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       } else {
         const int lrow = wn * C::kWN + tn * C::MF + 8 * s + (lane & 7);
         vb[tn][s] = lrow < b_rows ? (uint32_t)(lrow * b_ld + 16 * (lane >> 3)) : 0x80000000u;
-        // linear: the 8 bytes this lane row loads of each pair of stages
-        if constexpr (SFL == 0) vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 8 * (((g & 1) << 1) | (g >> 1))) : 0x80000000u;
+        // linear: the bytes this lane row loads of each pair (quad) of stages
+        if constexpr (SFL == 0 && kQuad) vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 16 * g) : 0x80000000u;
+        else if constexpr (SFL == 0) vbs[tn][s] = row < b_rows ? (uint32_t)(row * bs_ld + 8 * (((g & 1) << 1) | (g >> 1))) : 0x80000000u;
         else vbs[tn][s] = row < b_rows ? SfLayout<SFL>::offset((int64_t)e * p.N + n0, row, g, lds) : 0x80000000u;
       }
     }
@@ -664,9 +711,10 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     zero_acc<C>(acc);
     GRegs<C, D> R;
     __syncthreads();  // the previous row chunk is done with both A tiles
+    if constexpr (kQuad) gr_load_sq<C, D>(R, 0, true, rbs, vbs, bs_step);
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      gr_load<C, D, PACKED, FUSED, SFL>(R, u, u, true, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
+      gr_load<C, D, PACKED, FUSED, SFL, SG>(R, u, u, true, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
       __builtin_amdgcn_sched_barrier(0);  // slots are issued in order 0, 1, ...
     }
     // fused: the A tile of stage s + 1 is written during stage s, after the
@@ -674,17 +722,23 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     // quantisation overlaps the other waves' MFMAs instead of holding every
     // wave at the barrier; stage 0's is written here
     if constexpr (FUSED) gr_fused_a<C, D>(R.ax[0], sm.af[0], gs_a, wave, lane);
-    for (int i0 = 0; i0 < n; i0 += D) {
+    for (int i0 = 0; i0 < n; i0 += G) {
 #pragma unroll
-      for (int u = 0; u < D; ++u) {
-        const int st = i0 + u;  // < n: the launcher picks this kernel only when D divides n
+      for (int v = 0; v < G; ++v) {
+        const int u = v % D;
+        const int st = i0 + v;  // < n: the launcher picks this kernel only when G divides n
         {
+          if constexpr (kQuad) {
+            if (v == 0) gr_split_sq<C, D>(R);
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn) R.bs[u][tn][0] = R.bsq[tn][v];
+          }
           uint16_t* af = sm.af[u & 1];
           if constexpr (!FUSED) gr_dequant_a<C, D>(R, u, af, ar, ac, ah);
           // LDS-only barrier: a __syncthreads() fence would also wait for the
           // prefetched loads (loads and stores share one counter)
           lds_barrier();
-          gr_compute<C, D, PACKED, SFL>(R, u, af, acc, r_in, g, lo8);
+          gr_compute<C, D, PACKED, SFL, SG>(R, u, af, acc, r_in, g, lo8);
           if constexpr (FUSED) {
             __builtin_amdgcn_sched_barrier(0);
             if (st + 1 < n) gr_fused_a<C, D>(R.ax[(u + 1) % D], sm.af[(u + 1) & 1], gs_a, wave, lane);
@@ -692,7 +746,11 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // keep the reload of slot u after its last reads, so old and new
           // contents share registers (no copies that would wait on the load)
           __builtin_amdgcn_sched_barrier(0);
-          gr_load<C, D, PACKED, FUSED, SFL>(R, u, st + D, st + D < n, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras,
+          // the next four stages' scales, issued before the codes of stage
+          // st + D so that waiting for them leaves those codes in flight
+          if constexpr (kQuad)
+            if (v == G - 1) gr_load_sq<C, D>(R, i0 + G, i0 + G < n, rbs, vbs, bs_step);
+          gr_load<C, D, PACKED, FUSED, SFL, SG>(R, u, st + D, st + D < n, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras,
                                        va, vas, vax);
         }
       }
@@ -1373,13 +1431,22 @@ hipError_t launch_grouped(GroupedLaunch p, int32_t* status, hipStream_t stream, 
     hipLaunchKernelGGL(k_grouped<CfgGrouped>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGrouped::kThreads), 0, stream,
                        p);
   } else if (gk == 2) {
+    // linear scales four stages per load when 4 divides K / 256, else two
     const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg::BN - 1) / CfgGroupedReg::BN);
-    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, false>), dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedReg::kThreads),
-                       0, stream, p);
+    if ((p.K / CfgGroupedReg::BK) % 4 == 0)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, false, false, 0, 4>), dim3(tiles_n * (unsigned)p.E),
+                         dim3(CfgGroupedReg::kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg, 2, false>), dim3(tiles_n * (unsigned)p.E),
+                         dim3(CfgGroupedReg::kThreads), 0, stream, p);
   } else if (gk == 3) {
     const unsigned tiles_n = (unsigned)((p.N + CfgGroupedReg64::BN - 1) / CfgGroupedReg64::BN);
-    hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false>), dim3(tiles_n * (unsigned)p.E),
-                       dim3(CfgGroupedReg64::kThreads), 0, stream, p);
+    if ((p.K / CfgGroupedReg64::BK) % 4 == 0)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false, false, 0, 4>), dim3(tiles_n * (unsigned)p.E),
+                         dim3(CfgGroupedReg64::kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false>), dim3(tiles_n * (unsigned)p.E),
+                         dim3(CfgGroupedReg64::kThreads), 0, stream, p);
   } else {
     const unsigned tiles_n = (unsigned)((p.N + CfgGroupedA16::BN - 1) / CfgGroupedA16::BN);
     hipLaunchKernelGGL(k_grouped_a16<CfgGroupedA16>, dim3(tiles_n * (unsigned)p.E), dim3(CfgGroupedA16::kThreads),
@@ -1530,6 +1597,14 @@ hipError_t launch_grouped_fused(GroupedLaunch p, bool packed, int32_t* status, h
                          stream, p);
     else
       hipLaunchKernelGGL((k_grouped_reg<CfgGroupedRegF, 2, true, true>), grid, dim3(CfgGroupedRegF::kThreads), 0,
+                         stream, p);
+  } else if ((p.K / CfgGroupedRegF::BK) % 4 == 0) {
+    // linear weight scales four stages per load
+    if (gk == 3)
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedReg64, 2, false, true, 0, 4>), grid, dim3(CfgGroupedReg64::kThreads),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((k_grouped_reg<CfgGroupedRegF, 2, false, true, 0, 4>), grid, dim3(CfgGroupedRegF::kThreads), 0,
                          stream, p);
   } else {
     if (gk == 3)
