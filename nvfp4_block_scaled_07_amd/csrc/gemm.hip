@@ -340,6 +340,9 @@ struct GRegs {
   uint32_t bsq[C::TN][4];
   AQ aq[D];
   uint32_t as[D];
+  // A scales four stages at a time: lane l of each DPP quad holds its word of
+  // stage 4 k + l % 4 (the quad's four lanes share one word of every stage)
+  uint32_t asq;
   // fused quantisation: kAX 16-byte chunks of bf16 activations per lane and
   // stage, one per 8-element half block (whole-line loads: 32 lanes per row)
   static constexpr int kAX = C::BM * C::BK * 2 / 16 / C::kThreads;
@@ -355,7 +358,10 @@ struct GRegs {
 // count) or the even slots those of two (8 bytes per lane, 32 of each row),
 // so a 16-row block's scale load touches its 16 rows' lines once per four or
 // two stages instead of once per stage; tiled scales take one word per stage
-// (two lines per block in the 8 x 4 layout).  Packed weights hold a lane's four scale
+// (two lines per block in the 8 x 4 layout).  With four-stage B loads the
+// A scale words come four stages at a time too where each DPP quad shares
+// one word (GrQuad::kA): lane l % 4 of the quad loads stage 4 k + l % 4 and
+// each stage broadcasts its lane to the quad.  Packed weights hold a lane's four scale
 // words (both row blocks, both sub-steps) in one 16-byte chunk.
 // Packed weights: stage kt of a slab is the block at base + kt * stride
 // (codes) and sbase + kt * sstride (scales); the buffer resource of each
@@ -365,6 +371,26 @@ struct PackedStream {
   const uint8_t* base;
   const uint8_t* sbase;
   int64_t stride, sstride;
+};
+
+// Lane v (0..3, a constant after unrolling) of each DPP quad, broadcast to
+// the quad (quad_perm v, v, v, v).
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x, int v) {
+  switch (v) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x00, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x55, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xAA, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xFF, 0xF, 0xF, false);
+  }
+}
+
+// Which scale loads take four stages at a time: B's on plain weights with
+// linear scales, and A's where each DPP quad of lanes shares one A scale word
+// (two threads per A code chunk).
+template <class C, int D, bool PACKED, bool FUSED, int SFL, int SG>
+struct GrQuad {
+  static constexpr bool kB = SG == 4 && SFL == 0 && !PACKED;
+  static constexpr bool kA = kB && !FUSED && GRegs<C, D>::kAP == 2;
 };
 
 template <class C, int D, bool PACKED, bool FUSED, int SFL, int SG>
@@ -423,7 +449,9 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
       R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b64(ra, live ? va : kOut, kt * C::RB, 0));
     else
       R.aq[u] = __builtin_bit_cast(AQ, __builtin_amdgcn_raw_buffer_load_b32(ra, live ? va : kOut, kt * C::RB, 0));
-    R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut, kt * (SFL == 0 ? C::SB : (int)SfLayout<SFL>::kUnitStep), 0);
+    if constexpr (!GrQuad<C, D, PACKED, FUSED, SFL, SG>::kA)
+      R.as[u] = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : kOut,
+                                                     kt * (SFL == 0 ? C::SB : (int)SfLayout<SFL>::kUnitStep), 0);
   }
 }
 
@@ -433,9 +461,11 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 // four stages.  gr_split_sq then leaves word g of stage kt + s in bsq[tn][s]
 // (a 4 x 4 transpose over lane rows and registers: lane-row halves swapped
 // with permlane32, then single lane rows with permlane16).
-template <class C, int D>
+template <class C, int D, bool AQ>
 __device__ __forceinline__ void gr_load_sq(GRegs<C, D>& R, int kt, bool live, const rsrc_t& rbs,
-                                           const uint32_t (&vbs)[C::TN][C::kSub], uint32_t bs_step) {
+                                           const uint32_t (&vbs)[C::TN][C::kSub], uint32_t bs_step, const rsrc_t& ras,
+                                           uint32_t vas) {
+  if constexpr (AQ) R.asq = __builtin_amdgcn_raw_buffer_load_b32(ras, live ? vas : 0x80000000u, kt * C::SB, 0);
 #pragma unroll
   for (int tn = 0; tn < C::TN; ++tn) {
     const u4_t w = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbs, live ? vbs[tn][0] : 0x80000000u,
@@ -599,7 +629,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
   static_assert(SFL == 0 || (!PACKED && C::BK == 256), "tiled scales: plain weights, one unit per stage");
   // SG: stages per linear B scale load (plain weights): 2, or 4 when 4
   // divides the stage count (the launcher's choice)
-  constexpr bool kQuad = SG == 4 && SFL == 0 && !PACKED;
+  constexpr bool kQuad = GrQuad<C, D, PACKED, FUSED, SFL, SG>::kB;
+  constexpr bool kAQ = GrQuad<C, D, PACKED, FUSED, SFL, SG>::kA;
   static_assert(SG == 2 || (kQuad && D == 2), "scale groups of four: plain weights, linear scales, two slots");
   constexpr int G = kQuad ? 4 : D;  // stages per loop iteration
   static_assert(D % 2 == 0, "A tile double buffer alternates with the stage");
@@ -704,6 +735,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
       ras = SfLayout<SFL>::rsrc(p.a_sf, mc, rows_c, lds);
       va = ar < rows_c ? (uint32_t)(ar * ld + ac * 16 + ah * (16 / RT::kAP)) : 0x80000000u;
       vas = ar < rows_c ? SfLayout<SFL>::offset(mc, ar, ac >> 1, lds) : 0x80000000u;
+      // four stages per load: lane l % 4 of the quad takes stage 4 k + l % 4
+      if (kAQ && ar < rows_c) vas += 16 * (threadIdx.x & 3);
 #pragma unroll
       for (int i = 0; i < RT::kAX; ++i) vax[i] = 0x80000000u;
     }
@@ -711,7 +744,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
     zero_acc<C>(acc);
     GRegs<C, D> R;
     __syncthreads();  // the previous row chunk is done with both A tiles
-    if constexpr (kQuad) gr_load_sq<C, D>(R, 0, true, rbs, vbs, bs_step);
+    if constexpr (kQuad) gr_load_sq<C, D, kAQ>(R, 0, true, rbs, vbs, bs_step, ras, vas);
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       gr_load<C, D, PACKED, FUSED, SFL, SG>(R, u, u, true, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras, va, vas, vax);
@@ -733,6 +766,8 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 #pragma unroll
             for (int tn = 0; tn < C::TN; ++tn) R.bs[u][tn][0] = R.bsq[tn][v];
           }
+          // this stage's A scale word from lane v of the quad
+          if constexpr (kAQ) R.as[u] = quad_bcast(R.asq, v);
           uint16_t* af = sm.af[u & 1];
           if constexpr (!FUSED) gr_dequant_a<C, D>(R, u, af, ar, ac, ah);
           // LDS-only barrier: a __syncthreads() fence would also wait for the
@@ -749,7 +784,7 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
           // the next four stages' scales, issued before the codes of stage
           // st + D so that waiting for them leaves those codes in flight
           if constexpr (kQuad)
-            if (v == G - 1) gr_load_sq<C, D>(R, i0 + G, i0 + G < n, rbs, vbs, bs_step);
+            if (v == G - 1) gr_load_sq<C, D, kAQ>(R, i0 + G, i0 + G < n, rbs, vbs, bs_step, ras, vas);
           gr_load<C, D, PACKED, FUSED, SFL, SG>(R, u, st + D, st + D < n, ps, rb, rbs, vb, vbs, b_step, bs_step, ra, ras,
                                        va, vas, vax);
         }
