@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--profile-grouped", action="store_true",
                     help="for profiler runs: one 256 MiB device copy (counter calibration), then the grouped "
                          "MoE GEMM on packed weights (graph of 10 calls, replayed 4 times); prints its time")
+    ap.add_argument("--profile-grouped-plain", action="store_true",
+                    help="for profiler runs: the grouped MoE GEMM on plain [E][N][K/2] weights with linear scales "
+                         "(nvfp4_grouped_gemm; graph of 10 calls, replayed 6 times); prints its time")
     ap.add_argument("--profile-mx", type=int, default=0, metavar="M",
                     help="for profiler runs: the MXFP4 GEMM M x 6144 x 6144 (graph of 10 calls, replayed 6 times); "
                          "prints its time")
@@ -159,8 +162,8 @@ def main():
     if args.profile_call:
         profile_call(torch, nv, sweep_inputs, call, args.workload, args.profile_call, args.graph)
         return
-    if args.profile_grouped:
-        profile_grouped(torch, nv, synth, quantise, stream)
+    if args.profile_grouped or args.profile_grouped_plain:
+        profile_grouped(torch, nv, synth, quantise, stream, packed=args.profile_grouped)
         return
     if args.profile_mx:
         profile_mx(torch, nv, synth, stream, args.profile_mx)
@@ -433,18 +436,26 @@ def grouped_call_name(rows, N, K, E):
     return f"nvfp4_grouped_gemm_packed rows={rows} N={N} K={K} E={E}"
 
 
-def profile_grouped(torch, nv, synth, quantise, stream):
+def profile_grouped(torch, nv, synth, quantise, stream, packed=True):
     """Workload of the grouped profiler runs: the 256 MiB calibration copy,
-    then the grouped MoE GEMM on packed expert weights, timed as the bench
-    times it (a graph of 10 calls); prints the call and its time."""
+    then the grouped MoE GEMM on packed expert weights (packed) or on the
+    plain [E][N][K/2] weights with linear scales (nvfp4_grouped_gemm), timed
+    as the bench times it (a graph of 10 calls); prints the call and its time."""
     calibration_copy(torch)
     gi = grouped_inputs(torch, nv, synth, quantise, torch.device("cuda"))
     rows, N, K, E = gi["rows"], gi["N"], gi["K"], gi["E"]
-    pb, psf = nv.grouped_pack(gi["b"], gi["bsf"], N, K, E)
-    del gi["b"], gi["bsf"]
-    us = timed(torch, stream, lambda i: nv.nvfp4_grouped_gemm_packed(gi["qa"], gi["sfa"], pb, psf, gi["off"],
-                                                                      gi["alpha"], gi["d"], rows, N, K, E), 10)
-    print(json.dumps({"call": grouped_call_name(rows, N, K, E), "us_per_call": round(us, 2),
+    if packed:
+        pb, psf = nv.grouped_pack(gi["b"], gi["bsf"], N, K, E)
+        del gi["b"], gi["bsf"]
+        fn = lambda i: nv.nvfp4_grouped_gemm_packed(gi["qa"], gi["sfa"], pb, psf, gi["off"], gi["alpha"], gi["d"],
+                                                     rows, N, K, E)
+        name = grouped_call_name(rows, N, K, E)
+    else:
+        fn = lambda i: nv.nvfp4_grouped_gemm(gi["qa"], gi["sfa"], gi["b"], gi["bsf"], gi["off"], gi["alpha"], gi["d"],
+                                              rows, N, K, E)
+        name = f"nvfp4_grouped_gemm rows={rows} N={N} K={K} E={E}"
+    us = timed(torch, stream, fn, 10)
+    print(json.dumps({"call": name, "us_per_call": round(us, 2),
                       "algorithmic_bytes": gi["bytes"], "gbps": round(gi["bytes"] / us / 1e3, 1)}))
 
 
