@@ -104,10 +104,12 @@ def main():
                          "TCC_EA0_RDREQ_64B_sum, TCC_EA0_RDREQ_128B_sum, as a cross-check of the copy scaling")
     args = ap.parse_args()
     if args.traffic:
-        if not args.profile_call and not args.profile_grouped:
-            raise SystemExit("--traffic needs the --profile-call M or --profile-grouped the counters were taken with")
+        if not args.profile_call and not args.profile_grouped and not args.profile_grouped_plain:
+            raise SystemExit("--traffic needs the --profile-call M, --profile-grouped or --profile-grouped-plain the "
+                             "counters were taken with")
         write_traffic_record(*args.traffic, args.requests,
-                             "grouped" if args.profile_grouped else (args.workload, args.profile_call))
+                             "grouped" if args.profile_grouped else
+                             "grouped_plain" if args.profile_grouped_plain else (args.workload, args.profile_call))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only; multi-GPU sharding is a design note, "
@@ -482,11 +484,16 @@ def write_traffic_record(fetch_csv, write_csv, requests_csv, target):
     the copy scaling (which assumes the kernel's request sizes match the copy's)."""
     import nvfp4_block_scaled_07_amd as nv
     import synth
-    if target == "grouped":
+    if target in ("grouped", "grouped_plain"):
         g = synth.GROUPED
         _, off = synth.routing(g["seed_router"], g["tokens"], g["experts"], g["top_k"])
-        call = grouped_call_name(int(off[-1]), g["n"], g["k"], g["experts"])
-        match, path_out = "k_grouped", GROUPED_TRAFFIC_RECORD
+        if target == "grouped":
+            call = grouped_call_name(int(off[-1]), g["n"], g["k"], g["experts"])
+            path_out = GROUPED_TRAFFIC_RECORD
+        else:
+            call = f"nvfp4_grouped_gemm rows={int(off[-1])} N={g['n']} K={g['k']} E={g['experts']}"
+            path_out = os.path.join(os.path.dirname(GROUPED_TRAFFIC_RECORD), "traffic_grouped_moe_plain.json")
+        match = "k_grouped"
     else:
         name, m = target
         w = synth.WORKLOADS[name]
