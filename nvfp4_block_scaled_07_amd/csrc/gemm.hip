@@ -361,7 +361,10 @@ struct GRegs {
 // (two lines per block in the 8 x 4 layout).  With four-stage B loads the
 // A scale words come four stages at a time too where each DPP quad shares
 // one word (GrQuad::kA): lane l % 4 of the quad loads stage 4 k + l % 4 and
-// each stage broadcasts its lane to the quad.  Packed weights hold a lane's four scale
+// each stage broadcasts its lane to the quad.  With four-stage scale loads
+// the weight codes are loaded non-temporal (read once), which keeps the
+// scale lines, each loaded in two halves four stages apart, and the A rows
+// in L2.  Packed weights hold a lane's four scale
 // words (both row blocks, both sub-steps) in one 16-byte chunk.
 // Packed weights: stage kt of a slab is the block at base + kt * stride
 // (codes) and sbase + kt * sstride (scales); the buffer resource of each
@@ -420,7 +423,8 @@ __device__ __forceinline__ void gr_load(GRegs<C, D>& R, int u, int kt, bool live
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
       R.bq[u][tn][s] = __builtin_bit_cast(
-          u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbk, live ? vb[tn][s] : kOut, bo, 0));
+          u4_t, __builtin_amdgcn_raw_buffer_load_b128(rbk, live ? vb[tn][s] : kOut, bo,
+                                                      GrQuad<C, D, PACKED, FUSED, SFL, SG>::kB ? 2 : 0));
       if (!PACKED && s == 0) {
         if constexpr (SFL == 0) {
           // linear scales: an even slot loads the words of two stages (u odd
